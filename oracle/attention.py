@@ -1,0 +1,102 @@
+"""Masked softmax attention in float64 over the kept keys (oracle).
+
+For batch b, head h and query row q (definitions from [FSA-190] Design: bool
+mask True = keep, floating bias additive; GQA with the KV head of head h being
+h // G, G = H / KVH; aux tensors broadcast over singleton batch / head / query
+dims by the ({B|1}, {H|KVH|1}, {Sq|1}, K) contract):
+
+  kept  = { key j < Sk : mask[b', h', q', j] }          (all keys if no mask)
+  s_j   = scale * <Q[b, q, h, :], K[b, j, h // G, :]> + bias[b', h', q', j]
+  m     = max_{j in kept} s_j
+  O     = sum_{j in kept} exp(s_j - m) V[b, j, h // G, :] / sum_{j in kept} exp(s_j - m)
+  LSE   = m + log sum_{j in kept} exp(s_j - m)
+
+with b' = b or 0, q' = q or 0 for singleton dims, and h' = h (head dim H),
+h // G (head dim KVH) or 0 (head dim 1). A row with no kept key returns O = 0
+(the fully-masked-row invariant) and LSE = -inf (log of an empty sum). Masked
+positions are left out of the sums, which is the same as giving them score
+-inf. The default scale is 1 / sqrt(D).
+
+The mask may also be a DFlashGeom: its rows then come from
+oracle.dflash.dflash_dense_mask, shared by every batch and head ([SF-452]
+Problem / Expected Behavior).
+"""
+
+import math
+
+import numpy as np
+
+from .dflash import DFlashGeom, dflash_dense_mask
+
+
+def _aux_rows(t, b, h, rows, H, KVH):
+    """Rows of a broadcastable 4D aux tensor for (b, h, rows)."""
+    Bt, Ht, Qt, _ = t.shape
+    G = H // KVH
+    bi = b if Bt > 1 else 0
+    if Ht == H:
+        hi = h
+    elif Ht == KVH:
+        hi = h // G
+    elif Ht == 1:
+        hi = 0
+    else:
+        raise ValueError(f"aux head dim {Ht} not in (1, {KVH}, {H})")
+    if Qt > 1:
+        return t[bi, hi, rows, :]
+    return np.broadcast_to(t[bi, hi, 0, :], (len(rows), t.shape[3]))
+
+
+def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
+    """O (len(rows), D) and LSE (len(rows),) for batch b, head h, query rows.
+
+    q: (B, Sq, H, D), k/v: (B, Sk, KVH, D) float arrays holding the exact
+    stored values; mask: None, a DFlashGeom, or a bool (Bm, Hm, Qm, K>=Sk)
+    array; bias: None or a float (Bb, Hb, Qb, K>=Sk) array.
+    """
+    q = np.asarray(q, np.float64)
+    B, Sq, H, D = q.shape
+    Sk, KVH = k.shape[1], k.shape[2]
+    G = H // KVH
+    rows = np.asarray(rows, np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Kh = np.asarray(k[b, :, h // G, :], np.float64)
+    Vh = np.asarray(v[b, :, h // G, :], np.float64)
+    Q = q[b, rows, h, :]
+    s = scale * (Q @ Kh.T)
+    if bias is not None:
+        s = s + _aux_rows(np.asarray(bias, np.float64), b, h, rows, H, KVH)[:, :Sk]
+    if mask is None:
+        kept = np.ones(s.shape, bool)
+    elif isinstance(mask, DFlashGeom):
+        kept = dflash_dense_mask(mask, rows)[:, :Sk]
+    else:
+        kept = np.asarray(_aux_rows(np.asarray(mask, bool), b, h, rows, H, KVH)[:, :Sk])
+    O = np.zeros((len(rows), D))
+    lse = np.full(len(rows), -np.inf)
+    for r in range(len(rows)):
+        sel = kept[r]
+        if not sel.any():
+            continue
+        sr = s[r, sel]
+        m = sr.max()
+        p = np.exp(sr - m)
+        l = p.sum()
+        O[r] = (p @ Vh[sel]) / l
+        lse[r] = m + math.log(l)
+    return O, lse
+
+
+def attention_full(q, k, v, scale=None, mask=None, bias=None):
+    """O (B, Sq, H, D) and LSE (B, H, Sq) for every row (small sizes only)."""
+    q = np.asarray(q, np.float64)
+    B, Sq, H, D = q.shape
+    O = np.zeros((B, Sq, H, D))
+    lse = np.zeros((B, H, Sq))
+    rows = np.arange(Sq)
+    for b in range(B):
+        for h in range(H):
+            O[b, :, h, :], lse[b, h, :] = attention_rows(
+                q, k, v, b, h, rows, scale=scale, mask=mask, bias=bias)
+    return O, lse
