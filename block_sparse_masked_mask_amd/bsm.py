@@ -1,0 +1,315 @@
+"""Thin Python binding of libbsm.so (include/bsm.h), argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; torch supplies device
+memory, shapes/strides and the current stream. There is no fallback: if the
+library is not built, or a call fails, this module raises.
+
+Names follow the C ABI: resolve_dflash_is_causal, block_mask_shape,
+build_block_mask, dynamic_topk_mask, dflash_dense_mask, masked_attn_fwd, plus
+create_mask, the 2D/4D pre-mask normalisation of flash-sparse-attention PR #197
+(Implementation Notes) done as zero-copy views before dynamic_topk_mask.
+"""
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_void_p
+from dataclasses import dataclass
+from typing import NamedTuple, Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsm.so")
+
+BSM_OK, BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE, BSM_E_UNSUPPORTED, BSM_E_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
+
+EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
+           "dynamic_topk_mask", "dflash_dense_mask", "masked_attn_fwd", "bsm_last_error")
+
+
+class Tensor4(ctypes.Structure):
+    _fields_ = [("data", c_void_p), ("dtype", c_int32), ("reserved", c_int32),
+                ("size", c_int64 * 4), ("stride", c_int64 * 4)]
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("B", "H", "KVH", "Sq", "Sk", "D")]
+
+
+class DFlashC(ctypes.Structure):
+    _fields_ = [("ctx_len", c_int64), ("num_blocks", c_int64), ("block_size", c_int64),
+                ("ctx_per_block", c_int64), ("ctx_end_offset", c_int64),
+                ("is_causal", c_int32), ("layer_type", c_int32), ("sliding_window", c_int64)]
+
+
+class BlockMaskC(ctypes.Structure):
+    _fields_ = [("kv_num_blocks", c_void_p), ("kv_indices", c_void_p),
+                ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p),
+                ("Bm", c_int64), ("Hm", c_int64), ("nQm", c_int64), ("nK", c_int64)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("o", c_void_p),
+                ("o_stride", c_int64 * 4), ("lse", c_void_p), ("softmax_scale", c_float),
+                ("reserved", c_int32), ("pred", POINTER(DFlashC)), ("mask", POINTER(Tensor4)),
+                ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC))]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbsm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m block_sparse_masked_mask_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bsm_last_error.restype = c_char_p
+        L.bsm_last_error.argtypes = []
+        L.resolve_dflash_is_causal.argtypes = [c_int32, c_int32]
+        L.block_mask_shape.argtypes = [POINTER(Geom), POINTER(DFlashC), POINTER(Tensor4),
+                                       POINTER(c_int64)]
+        L.build_block_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), POINTER(Tensor4),
+                                       POINTER(BlockMaskC), c_void_p]
+        L.dynamic_topk_mask.argtypes = [POINTER(Tensor4), POINTER(Tensor4), c_int64, c_int64,
+                                        c_void_p, c_void_p]
+        L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
+        L.masked_attn_fwd.argtypes = [POINTER(Geom), POINTER(AttnArgs), c_void_p]
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = c_int32
+        _lib = L
+    return _lib
+
+
+class BsmError(Exception):
+    pass
+
+
+def _check(status):
+    if status >= 0:
+        return status
+    msg = lib().bsm_last_error().decode()
+    if status in (BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE):
+        raise ValueError(f"bsm status {status}: {msg}")
+    raise RuntimeError(f"bsm status {status}: {msg}")
+
+
+_DT = {torch.bool: BSM_BOOL, torch.uint8: BSM_BOOL, torch.bfloat16: BSM_BF16,
+       torch.float32: BSM_F32}
+
+
+def tensor4(t, dims=4):
+    """Tensor4 view of a 4D torch tensor (sizes and element strides as they are)."""
+    if t.dim() != dims:
+        raise ValueError(f"expected a {dims}D tensor, got {tuple(t.shape)}")
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    x = Tensor4()
+    x.data = t.data_ptr() if t.numel() > 0 else None
+    x.dtype = _DT[t.dtype]
+    x.reserved = 0
+    for i in range(4):
+        x.size[i] = t.shape[i]
+        x.stride[i] = t.stride(i)
+    return x
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+class Geometry(NamedTuple):
+    B: int
+    H: int
+    KVH: int
+    Sq: int
+    Sk: int
+    D: int
+
+    def c(self):
+        return Geom(*[int(x) for x in self])
+
+
+def geometry_of(q, k):
+    """Geometry from Q (B, Sq, H, D) and K (B, Sk, KVH, D)."""
+    B, Sq, H, D = q.shape
+    return Geometry(B, H, k.shape[2], Sq, k.shape[1], D)
+
+
+@dataclass(frozen=True)
+class DFlash:
+    """DFlash draft-block mask parameters (see include/bsm.h, bsm_dflash).
+
+    is_causal: None (absent), False or True; layer_type: 'full' or 'sliding'.
+    """
+
+    ctx_len: int
+    num_blocks: int
+    block_size: int
+    ctx_per_block: int = 0
+    ctx_end_offset: int = 0
+    is_causal: Optional[bool] = None
+    layer_type: str = "full"
+    sliding_window: int = 0
+
+    def c(self):
+        ic = -1 if self.is_causal is None else int(bool(self.is_causal))
+        lt = {"full": 0, "sliding": 1}.get(self.layer_type, self.layer_type)
+        return DFlashC(self.ctx_len, self.num_blocks, self.block_size, self.ctx_per_block,
+                       self.ctx_end_offset, ic, lt, self.sliding_window)
+
+    @property
+    def Sq(self):
+        return self.num_blocks * self.block_size
+
+    @property
+    def Sk(self):
+        return self.ctx_len + self.num_blocks * self.block_size
+
+
+class BlockMask(NamedTuple):
+    kv_num_blocks: torch.Tensor
+    kv_indices: torch.Tensor
+    full_kv_num_blocks: torch.Tensor
+    full_kv_indices: torch.Tensor
+
+    def c(self):
+        Bm, Hm, nQm, nK = self.kv_indices.shape
+        return BlockMaskC(self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
+                          self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr(),
+                          Bm, Hm, nQm, nK)
+
+
+def round_multiple(x, m=128):
+    return (int(x) + m - 1) // m * m
+
+
+def resolve_dflash_is_causal(is_causal, layer_type):
+    ic = -1 if is_causal is None else int(bool(is_causal))
+    lt = {"full": 0, "sliding": 1}.get(layer_type, layer_type)
+    return bool(_check(lib().resolve_dflash_is_causal(ic, lt)))
+
+
+def block_mask_shape(geom, pred=None, mask=None):
+    out = (c_int64 * 4)()
+    g = Geometry(*geom).c()
+    pc = pred.c() if pred is not None else None
+    mc = tensor4(mask) if mask is not None else None
+    _check(lib().block_mask_shape(ctypes.byref(g), ctypes.byref(pc) if pc else None,
+                                  ctypes.byref(mc) if mc else None, out))
+    return tuple(int(x) for x in out)
+
+
+def build_block_mask(geom, pred=None, mask=None, device=None, stream=None):
+    """Block mask of a DFlash predicate or a dense bool mask (four int32 tensors)."""
+    shp = block_mask_shape(geom, pred, mask)
+    if device is None:
+        device = mask.device if mask is not None else torch.device("cuda")
+    Bm, Hm, nQm, nK = shp
+    bm = BlockMask(torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=device),
+                   torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=device),
+                   torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=device),
+                   torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=device))
+    g = Geometry(*geom).c()
+    pc = pred.c() if pred is not None else None
+    mc = tensor4(mask) if mask is not None else None
+    bc = bm.c()
+    _check(lib().build_block_mask(ctypes.byref(g), ctypes.byref(pc) if pc else None,
+                                  ctypes.byref(mc) if mc else None, ctypes.byref(bc),
+                                  _stream(stream)))
+    return bm
+
+
+def dynamic_topk_mask(bias, premask, seqlen_k, k, out=None, stream=None):
+    """Top-k keep mask (bool, bias's shape) over a 4D bias."""
+    if out is None:
+        out = torch.empty(bias.shape, dtype=torch.bool, device=bias.device)
+    bc = tensor4(bias)
+    pc = tensor4(premask) if premask is not None else None
+    _check(lib().dynamic_topk_mask(ctypes.byref(bc), ctypes.byref(pc) if pc else None,
+                                   int(seqlen_k), int(k),
+                                   out.data_ptr() if out.numel() else None, _stream(stream)))
+    return out
+
+
+def create_mask(attention_bias, attention_mask, batch_size, query_len, key_len, window_size,
+                stream=None):
+    """Normalise a 2D or 4D pre-mask to the bias's 4D contract, then top-k.
+
+    2D (batch, key_len) -> (batch, 1, 1, key_len) view; 4D must already
+    broadcast to the bias (dims 1 or equal, last dim key_len or K_round).
+    A 2D mask of length query_len != key_len is not supported (the pages
+    disagree on whether to pad it with ones or zeros).
+    """
+    pm = attention_mask
+    if pm is not None:
+        if pm.dim() == 2:
+            if tuple(pm.shape) == (batch_size, key_len):
+                pm = pm.as_strided((batch_size, 1, 1, key_len), (pm.stride(0), 0, 0, pm.stride(1)))
+            elif pm.shape[1] == query_len:
+                raise NotImplementedError("2D mask over query_len != key_len is not supported")
+            else:
+                raise ValueError(f"2D mask must be (batch, key_len), got {tuple(pm.shape)}")
+        elif pm.dim() != 4:
+            raise ValueError("mask must be 2D or 4D")
+        if pm.dtype != torch.bool:
+            raise ValueError("mask must be bool")
+    return dynamic_topk_mask(attention_bias, pm, key_len, window_size, stream=stream)
+
+
+def dflash_dense_mask(geom, pred, out=None, stream=None):
+    """Dense (Sq, K_round) bool DFlash mask, written by the library's kernel."""
+    g = Geometry(*geom)
+    if out is None:
+        out = torch.empty((g.Sq, round_multiple(g.Sk)), dtype=torch.bool, device="cuda")
+    pc = pred.c()
+    _check(lib().dflash_dense_mask(ctypes.byref(g.c()), ctypes.byref(pc),
+                                   out.data_ptr() if out.numel() else None, _stream(stream)))
+    return out
+
+
+def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
+                    softmax_scale=None, return_lse=False, out=None, lse=None, stream=None):
+    """Masked attention forward; returns O (and LSE if return_lse)."""
+    geom = geometry_of(q, k)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((geom.B, geom.H, geom.Sq), dtype=torch.float32, device=q.device)
+    a = AttnArgs()
+    a.q, a.k, a.v = tensor4(q), tensor4(k), tensor4(v)
+    a.o = out.data_ptr() if out.numel() else None
+    for i in range(4):
+        a.o_stride[i] = out.stride(i)
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.reserved = 0
+    keep = []
+    if pred is not None:
+        pc = pred.c()
+        keep.append(pc)
+        a.pred = ctypes.pointer(pc)
+    if mask is not None:
+        mc = tensor4(mask)
+        keep.append(mc)
+        a.mask = ctypes.pointer(mc)
+    if bias is not None:
+        bc = tensor4(bias)
+        keep.append(bc)
+        a.bias = ctypes.pointer(bc)
+    if block_mask is not None:
+        bmc = block_mask.c()
+        keep.append(bmc)
+        a.bm = ctypes.pointer(bmc)
+    _check(lib().masked_attn_fwd(ctypes.byref(geom.c()), ctypes.byref(a), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,66 @@
+// Shared pieces of the masked attention kernels: which key tiles a query tile
+// visits, and where its mask / bias rows live.
+//
+// Broadcast rules (flash-sparse-attention PR #190, Design and Changes): an aux
+// tensor's batch / query dims broadcast by stride 0 when of size 1, and its head
+// dim is H (index h), KVH (index h / G) or 1 (index 0). The block mask follows
+// the same head rule and is shared by every query tile when it has one query
+// tile row (nQm == 1).
+#pragma once
+
+#include "bsm_internal.h"
+#include "dflash_rows.h"
+
+namespace bsm {
+
+__device__ inline int64_t head_index(int mode, int h, int G) {
+  return mode == 0 ? 0 : (mode == 1 ? h : h / G);
+}
+
+__device__ inline const uint8_t* aux_row(const AuxView& a, int64_t elem, int b, int h,
+                                         int G, int q) {
+  const int64_t off = (int64_t)b * a.sb + head_index(a.h_mode, h, G) * a.sh +
+                      (a.q_bcast ? 0 : (int64_t)q) * a.sq;
+  return reinterpret_cast<const uint8_t*>(a.data) + off * elem;
+}
+
+// Key tiles visited by query tile qt of (b, h): first the full tiles, then the
+// partial ones. Without a block mask every key tile is visited, as partial when
+// a mask is present and as full otherwise.
+struct TileList {
+  const int32_t* full;
+  const int32_t* part;
+  int nfull, npart;
+
+  __device__ inline void init(const AttnParams& p, int b, int h, int qt) {
+    if (p.has_bm) {
+      const BlockMaskView& m = p.bm;
+      const int64_t mb = m.Bm == 1 ? 0 : b;
+      const int64_t mh = head_index(m.h_mode, h, p.G);
+      const int64_t mq = m.nQm == 1 ? 0 : qt;
+      const int64_t r = (mb * m.Hm + mh) * m.nQm + mq;
+      nfull = m.full_num[r];
+      npart = m.kv_num[r];
+      full = m.full_idx + r * m.nK;
+      part = m.kv_idx + r * m.nK;
+    } else {
+      full = part = nullptr;
+      if (p.mask_kind == 0) {
+        nfull = p.nK;
+        npart = 0;
+      } else {
+        nfull = 0;
+        npart = p.nK;
+      }
+    }
+  }
+  __device__ inline int count() const { return nfull + npart; }
+  // key tile of visit i, and whether it is full (no mask test needed)
+  __device__ inline int tile(int i, bool& is_full) const {
+    is_full = i < nfull;
+    if (is_full) return full ? full[i] : i;
+    return part ? part[i - nfull] : i - nfull;
+  }
+};
+
+}  // namespace bsm

@@ -1,0 +1,505 @@
+// Host side of the C ABI declared in include/bsm.h: argument validation, the
+// broadcast / head-group-swap view rewrites, and kernel launches on the caller's
+// stream. No device memory is allocated here and nothing synchronises the host.
+//
+// Shape contract (flash-sparse-attention PR #190, Design and Changes): aux
+// tensors are 4D ({B|1}, {H|KVH|1}, {Sq|1}, round_multiple(Sk, 128)) with a
+// contiguous last dim; size-1 dims broadcast by stride 0; nothing is implicitly
+// unsqueezed or expanded. Swapped path (PR #190, Design / Implementation Notes):
+// with Sq == 1 and H > KVH the G heads of a KV group become G query rows of that
+// KV head, by rewriting strides only, and the LSE write-back follows the same
+// view.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bsm.h"
+#include "bsm_internal.h"
+
+using namespace bsm;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int64_t round_multiple(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int elem_size(int32_t dt) { return dt == BSM_BOOL ? 1 : (dt == BSM_BF16 ? 2 : 4); }
+
+struct Geo {
+  int64_t B, H, KVH, Sq, Sk, D, G, Kr, nQ, nK;
+  bool swap;
+};
+
+int check_geom(const bsm_geom* g, Geo& o) {
+  if (!g) return fail(BSM_E_ARG, "geom is NULL");
+  if (g->B < 0 || g->H < 1 || g->KVH < 1 || g->Sq < 0 || g->Sk < 0 || g->D < 1)
+    return fail(BSM_E_SHAPE, "bad geometry B=%lld H=%lld KVH=%lld Sq=%lld Sk=%lld D=%lld",
+                (long long)g->B, (long long)g->H, (long long)g->KVH, (long long)g->Sq,
+                (long long)g->Sk, (long long)g->D);
+  if (g->H % g->KVH)
+    return fail(BSM_E_SHAPE, "H=%lld is not a multiple of KVH=%lld", (long long)g->H,
+                (long long)g->KVH);
+  if (g->Sq > INT32_MAX / 2 || g->Sk > INT32_MAX / 2 || g->B > 65535 || g->H > 65535)
+    return fail(BSM_E_UNSUPPORTED, "geometry beyond this build's limits");
+  o.B = g->B;
+  o.H = g->H;
+  o.KVH = g->KVH;
+  o.Sq = g->Sq;
+  o.Sk = g->Sk;
+  o.D = g->D;
+  o.G = g->H / g->KVH;
+  o.Kr = round_multiple(g->Sk, kTile);
+  o.nK = o.Kr / kTile;
+  o.nQ = (g->Sq + kTile - 1) / kTile;
+  o.swap = g->Sq == 1 && g->H > g->KVH;
+  return BSM_OK;
+}
+
+int resolve_causal(int32_t is_causal, int32_t layer_type) {
+  if (layer_type != 0 && layer_type != 1) return -1;
+  if (is_causal == -1) return layer_type == 1;
+  if (is_causal == 0 || is_causal == 1) return is_causal;
+  return -1;
+}
+
+int check_dflash(const bsm_dflash* d, const Geo& g, DFlashRule& r) {
+  if (d->ctx_len < 0 || d->num_blocks < 0 || d->block_size < 1 || d->ctx_per_block < 0)
+    return fail(BSM_E_ARG, "bad DFlash sizes ctx_len=%lld num_blocks=%lld block_size=%lld",
+                (long long)d->ctx_len, (long long)d->num_blocks, (long long)d->block_size);
+  const int c = resolve_causal(d->is_causal, d->layer_type);
+  if (c < 0)
+    return fail(BSM_E_ARG, "bad is_causal=%d / layer_type=%d", d->is_causal, d->layer_type);
+  int64_t S = d->ctx_per_block;
+  if (S == 0 && d->num_blocks > 0) {
+    if (d->ctx_len % d->num_blocks)
+      return fail(BSM_E_ARG, "ctx_per_block=0 needs ctx_len %% num_blocks == 0");
+    S = d->ctx_len / d->num_blocks;
+  }
+  if (g.Sq != d->num_blocks * d->block_size)
+    return fail(BSM_E_SHAPE, "DFlash needs Sq == num_blocks*block_size (%lld != %lld)",
+                (long long)g.Sq, (long long)(d->num_blocks * d->block_size));
+  if (g.Sk != d->ctx_len + d->num_blocks * d->block_size)
+    return fail(BSM_E_SHAPE, "DFlash needs Sk == ctx_len + num_blocks*block_size");
+  if (d->layer_type == 1 && d->sliding_window < 1)
+    return fail(BSM_E_ARG, "sliding layer needs sliding_window >= 1");
+  r.C = d->ctx_len;
+  r.bs = d->block_size;
+  r.S = S;
+  r.e0 = d->ctx_end_offset;
+  r.W = d->layer_type == 1 ? d->sliding_window : 0;
+  r.causal = c;
+  r.pad = 0;
+  return BSM_OK;
+}
+
+// Stride rules common to every 4D view: last dim contiguous, no negative
+// stride, no 0 stride on a dim of size > 1, 16-byte aligned rows.
+int check_strides(const bsm_tensor4* t, const char* name, int esz) {
+  if (t->reserved != 0) return fail(BSM_E_ARG, "%s.reserved must be 0", name);
+  if (t->size[3] > 1 && t->stride[3] != 1)
+    return fail(BSM_E_STRIDE, "%s: last dim must be contiguous", name);
+  for (int i = 0; i < 3; ++i) {
+    if (t->stride[i] < 0) return fail(BSM_E_STRIDE, "%s: negative stride", name);
+    if (t->size[i] > 1 && t->stride[i] == 0)
+      return fail(BSM_E_STRIDE, "%s: stride 0 on dim %d of size %lld (no implicit expand)",
+                  name, i, (long long)t->size[i]);
+    if (t->size[i] > 1 && (t->stride[i] * esz) % 16)
+      return fail(BSM_E_STRIDE, "%s: dim %d stride is not a multiple of 16 bytes", name, i);
+  }
+  if ((uintptr_t)t->data % 16) return fail(BSM_E_STRIDE, "%s: data not 16-byte aligned", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->size[i] < 0) return fail(BSM_E_SHAPE, "%s: negative size", name);
+  return BSM_OK;
+}
+
+int64_t numel(const bsm_tensor4* t) {
+  return t->size[0] * t->size[1] * t->size[2] * t->size[3];
+}
+
+// Aux tensor (mask / bias) in the attention's iteration space.
+struct Aux {
+  AuxView view;
+  int64_t Bm, Hm, Qm;  // sizes in that space
+};
+
+int check_aux(const bsm_tensor4* t, const char* name, const Geo& g, int32_t dtype, Aux& a) {
+  if (t->dtype != dtype)
+    return fail(BSM_E_DTYPE, "%s: dtype %d, expected %d", name, t->dtype, dtype);
+  const int esz = elem_size(dtype);
+  int e = check_strides(t, name, esz);
+  if (e) return e;
+  if (t->size[3] != g.Kr)
+    return fail(BSM_E_SHAPE, "%s: last dim %lld must be round_multiple(Sk,128)=%lld", name,
+                (long long)t->size[3], (long long)g.Kr);
+  if (t->size[0] != g.B && t->size[0] != 1)
+    return fail(BSM_E_SHAPE, "%s: dim 0 must be B or 1", name);
+  if (t->size[1] != g.H && t->size[1] != g.KVH && t->size[1] != 1)
+    return fail(BSM_E_SHAPE, "%s: dim 1 must be H, KVH or 1", name);
+  if (t->size[2] != g.Sq && t->size[2] != 1)
+    return fail(BSM_E_SHAPE, "%s: dim 2 must be Sq or 1", name);
+  if (!t->data && numel(t) > 0) return fail(BSM_E_ARG, "%s: data is NULL", name);
+  const int64_t sb = t->size[0] == 1 ? 0 : t->stride[0];
+  const int64_t sh = t->size[1] == 1 ? 0 : t->stride[1];
+  const int64_t sq = t->size[2] == 1 ? 0 : t->stride[2];
+  a.view.data = t->data;
+  a.view.sb = sb;
+  a.Bm = t->size[0];
+  if (!g.swap) {
+    a.view.h_mode = t->size[1] == g.H ? 1 : (t->size[1] == g.KVH ? 2 : 0);
+    a.view.sh = sh;
+    a.view.sq = sq;
+    a.view.q_bcast = t->size[2] == 1;
+    a.Hm = t->size[1];
+    a.Qm = t->size[2];
+  } else if (t->size[1] == g.H) {
+    // (Bm, H, 1, K) viewed as (Bm, KVH, G, K): head kvh*G + g -> row g of kvh
+    a.view.h_mode = 1;
+    a.view.sh = g.G * t->stride[1];
+    a.view.sq = t->stride[1];
+    a.view.q_bcast = 0;
+    a.Hm = g.KVH;
+    a.Qm = g.G;
+  } else if (t->size[1] == g.KVH) {
+    a.view.h_mode = 1;
+    a.view.sh = sh;
+    a.view.sq = 0;
+    a.view.q_bcast = 1;
+    a.Hm = g.KVH;
+    a.Qm = 1;
+  } else {
+    a.view.h_mode = 0;
+    a.view.sh = 0;
+    a.view.sq = 0;
+    a.view.q_bcast = 1;
+    a.Hm = 1;
+    a.Qm = 1;
+  }
+  return BSM_OK;
+}
+
+// Heads and query rows of the attention's iteration space.
+int64_t iter_heads(const Geo& g) { return g.swap ? g.KVH : g.H; }
+int64_t iter_rows(const Geo& g) { return g.swap ? g.G : g.Sq; }
+
+int expected_bm(const Geo& g, const bsm_dflash* pred, const Aux* mask, int64_t out[4]) {
+  if (pred) {
+    out[0] = 1;
+    out[1] = 1;
+    out[2] = g.nQ;  // the predicate's rows (Sq == 1 under the swap: one tile)
+    out[3] = g.nK;
+  } else {
+    out[0] = mask->Bm;
+    out[1] = mask->Hm;
+    out[2] = (mask->Qm + kTile - 1) / kTile;
+    out[3] = g.nK;
+  }
+  return BSM_OK;
+}
+
+int bm_head_mode(const Geo& g, int64_t Hm) {
+  const int64_t Hi = iter_heads(g);
+  const int64_t KVHi = g.KVH;
+  return Hm == Hi ? 1 : (Hm == KVHi ? 2 : 0);
+}
+
+int check_tensor_qkv(const bsm_tensor4* t, const char* name, int64_t d0, int64_t d1,
+                     int64_t d2, int64_t d3, int32_t dtype) {
+  if (t->dtype != dtype) return fail(BSM_E_DTYPE, "%s: dtype mismatch", name);
+  if (t->size[0] != d0 || t->size[1] != d1 || t->size[2] != d2 || t->size[3] != d3)
+    return fail(BSM_E_SHAPE, "%s: sizes (%lld,%lld,%lld,%lld) expected (%lld,%lld,%lld,%lld)",
+                name, (long long)t->size[0], (long long)t->size[1], (long long)t->size[2],
+                (long long)t->size[3], (long long)d0, (long long)d1, (long long)d2,
+                (long long)d3);
+  int e = check_strides(t, name, elem_size(dtype));
+  if (e) return e;
+  if (!t->data && numel(t) > 0) return fail(BSM_E_ARG, "%s: data is NULL", name);
+  return BSM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return BSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsm_last_error(void) { return g_err.c_str(); }
+
+int resolve_dflash_is_causal(int32_t is_causal, int32_t layer_type) {
+  const int c = resolve_causal(is_causal, layer_type);
+  if (c < 0)
+    return fail(BSM_E_ARG, "bad is_causal=%d / layer_type=%d", is_causal, layer_type);
+  return c;
+}
+
+int block_mask_shape(const bsm_geom* geom, const bsm_dflash* pred, const bsm_tensor4* mask,
+                     int64_t out_shape[4]) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!out_shape) return fail(BSM_E_ARG, "out_shape is NULL");
+  if ((pred == nullptr) == (mask == nullptr))
+    return fail(BSM_E_ARG, "exactly one of pred and mask must be given");
+  if (pred) {
+    DFlashRule r;
+    e = check_dflash(pred, g, r);
+    if (e) return e;
+    return expected_bm(g, pred, nullptr, out_shape);
+  }
+  if (mask->dtype != BSM_BOOL) return fail(BSM_E_DTYPE, "mask must be BSM_BOOL");
+  Aux a;
+  e = check_aux(mask, "mask", g, BSM_BOOL, a);
+  if (e) return e;
+  return expected_bm(g, nullptr, &a, out_shape);
+}
+
+int build_block_mask(const bsm_geom* geom, const bsm_dflash* pred, const bsm_tensor4* mask,
+                     const bsm_block_mask* out, hipStream_t stream) {
+  int64_t shp[4];
+  int e = block_mask_shape(geom, pred, mask, shp);
+  if (e) return e;
+  if (!out) return fail(BSM_E_ARG, "out is NULL");
+  if (out->Bm != shp[0] || out->Hm != shp[1] || out->nQm != shp[2] || out->nK != shp[3])
+    return fail(BSM_E_SHAPE, "block mask dims (%lld,%lld,%lld,%lld) expected (%lld,%lld,%lld,%lld)",
+                (long long)out->Bm, (long long)out->Hm, (long long)out->nQm, (long long)out->nK,
+                (long long)shp[0], (long long)shp[1], (long long)shp[2], (long long)shp[3]);
+  const int64_t rows = shp[0] * shp[1] * shp[2];
+  if (rows > 0 && (!out->kv_num_blocks || !out->full_kv_num_blocks ||
+                   (shp[3] > 0 && (!out->kv_indices || !out->full_kv_indices))))
+    return fail(BSM_E_ARG, "block mask buffer is NULL");
+  if (shp[3] > 65536) return fail(BSM_E_UNSUPPORTED, "more than 65536 key tiles");
+  Geo g;
+  check_geom(geom, g);
+  if (pred) {
+    DFlashRule r;
+    check_dflash(pred, g, r);
+    return hip_status(launch_block_mask_pred(r, g.Sq, g.Sk, shp[2], shp[3], out->kv_num_blocks,
+                                             out->kv_indices, out->full_kv_num_blocks,
+                                             out->full_kv_indices, stream),
+                      "block_mask_pred");
+  }
+  Aux a;
+  check_aux(mask, "mask", g, BSM_BOOL, a);
+  DenseMaskView v;
+  v.data = reinterpret_cast<const uint8_t*>(a.view.data);
+  v.sb = a.view.sb;
+  v.sh = a.view.sh;
+  v.sq = a.view.sq;
+  v.Bm = a.Bm;
+  v.Hm = a.Hm;
+  v.Qm = a.Qm;
+  v.K = g.Kr;
+  v.Sk = g.Sk;
+  return hip_status(launch_block_mask_dense(v, out->kv_num_blocks, out->kv_indices,
+                                            out->full_kv_num_blocks, out->full_kv_indices,
+                                            stream),
+                    "block_mask_dense");
+}
+
+int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64_t seqlen_k,
+                      int64_t k, uint8_t* out_mask, hipStream_t stream) {
+  if (!bias) return fail(BSM_E_ARG, "bias is NULL");
+  if (k < 0) return fail(BSM_E_ARG, "k must be >= 0 (got %lld)", (long long)k);
+  if (seqlen_k < 0) return fail(BSM_E_ARG, "seqlen_k must be >= 0");
+  if (bias->dtype != BSM_BF16 && bias->dtype != BSM_F32)
+    return fail(BSM_E_DTYPE, "bias must be bf16 or f32");
+  int e = check_strides(bias, "bias", elem_size(bias->dtype));
+  if (e) return e;
+  const int64_t Kr = round_multiple(seqlen_k, kTile);
+  if (bias->size[3] != Kr)
+    return fail(BSM_E_SHAPE, "bias last dim %lld must be round_multiple(seqlen_k,128)=%lld",
+                (long long)bias->size[3], (long long)Kr);
+  const int64_t n = numel(bias);
+  if (n > 0 && (!bias->data || !out_mask)) return fail(BSM_E_ARG, "bias or out_mask is NULL");
+  if (bias->size[0] * bias->size[1] * bias->size[2] > INT32_MAX)
+    return fail(BSM_E_UNSUPPORTED, "too many rows");
+  TopkParams p{};
+  p.bias = bias->data;
+  p.b_sb = bias->size[0] == 1 ? 0 : bias->stride[0];
+  p.b_sh = bias->size[1] == 1 ? 0 : bias->stride[1];
+  p.b_sq = bias->size[2] == 1 ? 0 : bias->stride[2];
+  p.Bb = bias->size[0];
+  p.Hb = bias->size[1];
+  p.Qb = bias->size[2];
+  p.K = Kr;
+  p.Sk = seqlen_k;
+  p.k = k;
+  p.out = out_mask;
+  p.is_bf16 = bias->dtype == BSM_BF16;
+  p.pm = nullptr;
+  if (premask) {
+    if (premask->dtype != BSM_BOOL) return fail(BSM_E_DTYPE, "premask must be BSM_BOOL");
+    if (premask->reserved != 0) return fail(BSM_E_ARG, "premask.reserved must be 0");
+    for (int i = 0; i < 3; ++i)
+      if (premask->size[i] != 1 && premask->size[i] != bias->size[i])
+        return fail(BSM_E_SHAPE, "premask dim %d must be 1 or %lld", i, (long long)bias->size[i]);
+    if (premask->size[3] != seqlen_k && premask->size[3] != Kr)
+      return fail(BSM_E_SHAPE, "premask last dim must be seqlen_k or round_multiple(seqlen_k,128)");
+    if (premask->size[3] > 1 && premask->stride[3] != 1)
+      return fail(BSM_E_STRIDE, "premask: last dim must be contiguous");
+    for (int i = 0; i < 3; ++i) {
+      if (premask->stride[i] < 0) return fail(BSM_E_STRIDE, "premask: negative stride");
+      if (premask->size[i] > 1 && premask->stride[i] == 0)
+        return fail(BSM_E_STRIDE, "premask: stride 0 on dim %d of size > 1", i);
+    }
+    if (!premask->data && numel(premask) > 0) return fail(BSM_E_ARG, "premask data is NULL");
+    p.pm = reinterpret_cast<const uint8_t*>(premask->data);
+    p.p_sb = premask->size[0] == 1 ? 0 : premask->stride[0];
+    p.p_sh = premask->size[1] == 1 ? 0 : premask->stride[1];
+    p.p_sq = premask->size[2] == 1 ? 0 : premask->stride[2];
+    p.pK = premask->size[3];
+  }
+  if (n == 0) return BSM_OK;
+  return hip_status(launch_topk(p, stream), "dynamic_topk_mask");
+}
+
+int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred, uint8_t* out_mask,
+                      hipStream_t stream) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!pred) return fail(BSM_E_ARG, "pred is NULL");
+  DFlashRule r;
+  e = check_dflash(pred, g, r);
+  if (e) return e;
+  if (g.Sq * g.Kr > 0 && !out_mask) return fail(BSM_E_ARG, "out_mask is NULL");
+  if ((uintptr_t)out_mask % 16) return fail(BSM_E_STRIDE, "out_mask not 16-byte aligned");
+  return hip_status(launch_dflash_dense(r, g.Sq, g.Sk, g.Kr, out_mask, stream), "dflash_dense");
+}
+
+int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t stream) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!a) return fail(BSM_E_ARG, "args is NULL");
+  if (a->reserved != 0) return fail(BSM_E_ARG, "args.reserved must be 0");
+  if (g.D != 64 && g.D != 128)
+    return fail(BSM_E_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)g.D);
+  const int32_t dt = a->q.dtype;
+  if (dt != BSM_BF16 && dt != BSM_F32) return fail(BSM_E_DTYPE, "q must be bf16 or f32");
+  if ((e = check_tensor_qkv(&a->q, "q", g.B, g.Sq, g.H, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->k, "k", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->v, "v", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  {
+    bsm_tensor4 o{};
+    o.data = a->o;
+    o.dtype = dt;
+    o.size[0] = g.B;
+    o.size[1] = g.Sq;
+    o.size[2] = g.H;
+    o.size[3] = g.D;
+    for (int i = 0; i < 4; ++i) o.stride[i] = a->o_stride[i];
+    if ((e = check_tensor_qkv(&o, "o", g.B, g.Sq, g.H, g.D, dt))) return e;
+  }
+  if (a->pred && a->mask) return fail(BSM_E_ARG, "give at most one of pred and mask");
+  if (std::isnan(a->softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
+  DFlashRule rule{};
+  if (a->pred && (e = check_dflash(a->pred, g, rule))) return e;
+  Aux mk{}, bs{};
+  if (a->mask && (e = check_aux(a->mask, "mask", g, BSM_BOOL, mk))) return e;
+  if (a->bias && (e = check_aux(a->bias, "bias", g, dt, bs))) return e;
+  BlockMaskView bmv{};
+  if (a->bm) {
+    if (!a->pred && !a->mask) return fail(BSM_E_ARG, "a block mask needs pred or mask");
+    int64_t shp[4];
+    expected_bm(g, a->pred, &mk, shp);
+    const bsm_block_mask* m = a->bm;
+    if (m->Bm != shp[0] || m->Hm != shp[1] || m->nQm != shp[2] || m->nK != shp[3])
+      return fail(BSM_E_SHAPE, "block mask dims (%lld,%lld,%lld,%lld) do not match this call "
+                  "(%lld,%lld,%lld,%lld)", (long long)m->Bm, (long long)m->Hm,
+                  (long long)m->nQm, (long long)m->nK, (long long)shp[0], (long long)shp[1],
+                  (long long)shp[2], (long long)shp[3]);
+    if (shp[0] * shp[1] * shp[2] > 0 &&
+        (!m->kv_num_blocks || !m->full_kv_num_blocks ||
+         (shp[3] > 0 && (!m->kv_indices || !m->full_kv_indices))))
+      return fail(BSM_E_ARG, "block mask buffer is NULL");
+    bmv.kv_num = m->kv_num_blocks;
+    bmv.kv_idx = m->kv_indices;
+    bmv.full_num = m->full_kv_num_blocks;
+    bmv.full_idx = m->full_kv_indices;
+    bmv.Bm = m->Bm;
+    bmv.Hm = m->Hm;
+    bmv.nQm = m->nQm;
+    bmv.nK = m->nK;
+    bmv.h_mode = bm_head_mode(g, m->Hm);
+  }
+  if (g.B == 0 || g.Sq == 0) return BSM_OK;
+
+  AttnParams p{};
+  p.q = a->q.data;
+  p.k = a->k.data;
+  p.v = a->v.data;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.k_sb = a->k.stride[0];
+  p.k_sk = a->k.stride[1];
+  p.k_sh = a->k.stride[2];
+  p.v_sb = a->v.stride[0];
+  p.v_sk = a->v.stride[1];
+  p.v_sh = a->v.stride[2];
+  p.B = (int32_t)g.B;
+  p.Sk = (int32_t)g.Sk;
+  p.nK = (int32_t)g.nK;
+  if (!g.swap) {
+    p.q_sb = a->q.stride[0];
+    p.q_sq = a->q.stride[1];
+    p.q_sh = a->q.stride[2];
+    p.o_sb = a->o_stride[0];
+    p.o_sq = a->o_stride[1];
+    p.o_sh = a->o_stride[2];
+    p.lse_sb = g.H * g.Sq;
+    p.lse_sh = g.Sq;
+    p.lse_sq = 1;
+    p.H = (int32_t)g.H;
+    p.KVH = (int32_t)g.KVH;
+    p.G = (int32_t)g.G;
+    p.Sq = (int32_t)g.Sq;
+  } else {
+    // heads kvh*G + i of one KV group -> rows i of KV head kvh
+    p.q_sb = a->q.stride[0];
+    p.q_sq = a->q.stride[2];
+    p.q_sh = g.G * a->q.stride[2];
+    p.o_sb = a->o_stride[0];
+    p.o_sq = a->o_stride[2];
+    p.o_sh = g.G * a->o_stride[2];
+    p.lse_sb = g.H;
+    p.lse_sh = g.G;
+    p.lse_sq = 1;
+    p.H = (int32_t)g.KVH;
+    p.KVH = (int32_t)g.KVH;
+    p.G = 1;
+    p.Sq = (int32_t)g.G;
+  }
+  p.nQ = (p.Sq + kTile - 1) / kTile;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)g.D);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mask_kind = a->pred ? 1 : (a->mask ? 2 : 0);
+  p.pred_row0 = g.swap && a->pred;
+  p.rule = rule;
+  p.mask = mk.view;
+  p.bias = bs.view;
+  p.has_bias = a->bias != nullptr;
+  p.has_bm = a->bm != nullptr;
+  p.bm = bmv;
+  const hipError_t he = dt == BSM_BF16 ? launch_attn_bf16(p, (int)g.D, stream)
+                                       : launch_attn_f32(p, (int)g.D, stream);
+  return hip_status(he, "masked_attn_fwd");
+}
+
+}  // extern "C"

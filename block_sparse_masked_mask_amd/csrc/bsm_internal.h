@@ -1,0 +1,101 @@
+// Internal interfaces between the host API (bsm_api.cpp) and the HIP kernels.
+// All sizes are validated by the host API before a launcher is called; the
+// launchers only map work onto grids and return hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsm {
+
+constexpr int kTile = 128;  // query and key tile edge
+
+// DFlash predicate, resolved on the host: per-row kept keys are two
+// half-open intervals, [lo1, hi1) in the context and [lo2, hi2) in the row's
+// own draft block (see dflash_row in dflash_rows.h).
+struct DFlashRule {
+  int64_t C;      // context tokens
+  int64_t bs;     // draft block size
+  int64_t S;      // context tokens per block
+  int64_t e0;     // context end offset
+  int64_t W;      // left-bound window, 0 = none
+  int32_t causal; // in-block causality
+  int32_t pad;
+};
+
+// Device-side block mask view in the attention's iteration space.
+struct BlockMaskView {
+  const int32_t* kv_num;
+  const int32_t* kv_idx;
+  const int32_t* full_num;
+  const int32_t* full_idx;
+  int64_t Bm, Hm, nQm, nK;
+  int32_t h_mode;  // 0: head index 0, 1: h, 2: h / G
+  int32_t pad;
+};
+
+// Aux tensor (mask or bias) addressed as base + b*sb + hidx*sh + q*sq + k,
+// with stride 0 on broadcast dims and hidx chosen by h_mode.
+struct AuxView {
+  const void* data;
+  int64_t sb, sh, sq;
+  int32_t h_mode;  // 0: 0, 1: h, 2: h / G
+  int32_t q_bcast; // 1 if the query dim broadcasts
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sq, q_sh;
+  int64_t k_sb, k_sk, k_sh;
+  int64_t v_sb, v_sk, v_sh;
+  int64_t o_sb, o_sq, o_sh;
+  int64_t lse_sb, lse_sh, lse_sq;
+  int32_t B, H, KVH, G, Sq, Sk, nQ, nK;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t mask_kind; // 0 none, 1 DFlash predicate, 2 dense mask
+  int32_t pred_row0; // predicate evaluated at query 0 for every row (swap)
+  DFlashRule rule;
+  AuxView mask;
+  AuxView bias;
+  int32_t has_bias;
+  int32_t has_bm;
+  BlockMaskView bm;
+};
+
+struct DenseMaskView {
+  const uint8_t* data;
+  int64_t sb, sh, sq;
+  int64_t Bm, Hm, Qm, K;  // K = K_round
+  int64_t Sk;
+};
+
+struct TopkParams {
+  const void* bias;
+  int64_t b_sb, b_sh, b_sq;
+  int64_t Bb, Hb, Qb, K;  // K = K_round
+  int64_t Sk;
+  const uint8_t* pm;      // nullable
+  int64_t p_sb, p_sh, p_sq, pK;
+  int64_t k;
+  uint8_t* out;
+  int32_t is_bf16;
+};
+
+hipError_t launch_block_mask_pred(const DFlashRule& r, int64_t Sq, int64_t Sk,
+                                  int64_t nQ, int64_t nK, int32_t* kv_num,
+                                  int32_t* kv_idx, int32_t* full_num,
+                                  int32_t* full_idx, hipStream_t s);
+hipError_t launch_dflash_dense(const DFlashRule& r, int64_t Sq, int64_t Sk,
+                               int64_t K, uint8_t* out, hipStream_t s);
+hipError_t launch_block_mask_dense(const DenseMaskView& m, int32_t* kv_num,
+                                   int32_t* kv_idx, int32_t* full_num,
+                                   int32_t* full_idx, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnParams& p, int D, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
+
+}  // namespace bsm

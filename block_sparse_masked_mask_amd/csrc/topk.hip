@@ -1,0 +1,272 @@
+// Dynamic top-k keep mask for gfx950: one workgroup per bias row, radix select.
+//
+// What it computes (flash-sparse-attention PR #197, Design / Implementation
+// Notes and the review suggestion on dynamic_mask): positions the pre-mask marks
+// invalid take the bias dtype's minimum finite value, the k largest entries of
+// the row are selected, and out = selected AND valid. Keys >= Sk are invalid
+// (PR #190, Implementation Notes). Ties at the cut go to the lower key index;
+// -0 and +0 compare equal.
+//
+// How: every value is mapped to an unsigned key whose integer order is the
+// value order (sign bit set -> bitwise NOT, else set the sign bit; -0 folded to
+// +0 first). The k-th largest key T is found one 8-bit digit at a time, most
+// significant first (2 passes for bf16, 4 for f32): an LDS histogram of the
+// digit among the keys that share the prefix found so far, then one wave walks
+// the 256 bins from the top to find the digit where the running count reaches
+// the remaining k. Keys > T are selected, and of the keys == T the `need`
+// lowest-indexed ones, found with a workgroup prefix count taken in index order
+// during the single write pass (16 keys per thread, one 16-byte store). When the
+// row fits, its keys stay in LDS between passes so the bias is read from HBM
+// once; otherwise each pass re-reads the row (L2-resident at these sizes).
+#include "bsm_internal.h"
+
+namespace bsm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPer = 16;  // keys per thread per chunk
+constexpr int kChunk = kThreads * kPer;
+
+template <typename KeyT>
+struct KeyTraits;
+
+template <>
+struct KeyTraits<uint16_t> {
+  static constexpr int kBits = 16;
+  // order-preserving key of a bf16 bit pattern
+  __device__ static uint16_t key(uint16_t b) {
+    if ((b & 0x7FFFu) == 0) b = 0;
+    return (b & 0x8000u) ? (uint16_t)~b : (uint16_t)(b | 0x8000u);
+  }
+  // key of the sentinel finfo(bfloat16).min = -(2 - 2^-7) * 2^127 (bits 0xFF7F)
+  __device__ static uint16_t sentinel() { return (uint16_t)~(uint16_t)0xFF7Fu; }
+};
+
+template <>
+struct KeyTraits<uint32_t> {
+  static constexpr int kBits = 32;
+  __device__ static uint32_t key(uint32_t b) {
+    if ((b & 0x7FFFFFFFu) == 0) b = 0;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  // finfo(float32).min = -(2 - 2^-23) * 2^127 (bits 0xFF7FFFFF)
+  __device__ static uint32_t sentinel() { return ~0xFF7FFFFFu; }
+};
+
+// Exclusive prefix sum of v over the workgroup in thread order.
+__device__ inline int block_excl_sum(int v, int* s_wave, int& tot) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[w] = x;
+  __syncthreads();
+  int off = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int t = s_wave[i];
+    off += i < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  return off + x - v;
+}
+
+template <typename KeyT, bool kCache>
+__global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
+  using Tr = KeyTraits<KeyT>;
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_wave[kWaves];
+  __shared__ uint32_t s_sel[2];  // chosen digit, count of keys above it
+
+  KeyT* s_keys = reinterpret_cast<KeyT*>(s_dyn);
+  const int64_t row = blockIdx.x;
+  const int64_t qb = row % p.Qb;
+  const int64_t hb = (row / p.Qb) % p.Hb;
+  const int64_t bb = row / (p.Qb * p.Hb);
+  const KeyT* brow = reinterpret_cast<const KeyT*>(p.bias) + bb * p.b_sb + hb * p.b_sh + qb * p.b_sq;
+  const uint8_t* prow = p.pm ? p.pm + bb * p.p_sb + hb * p.p_sh + qb * p.p_sq : nullptr;
+  uint8_t* orow = p.out + row * p.K;
+  const int64_t K = p.K;
+  const KeyT sent = Tr::sentinel();
+
+  auto valid = [&](int64_t k) -> bool {
+    return k < p.Sk && (prow == nullptr || (k < p.pK && prow[k] != 0));
+  };
+  // keys of 16 consecutive positions starting at k0 (k0 % 16 == 0, k0 < K)
+  auto load16 = [&](int64_t k0, KeyT* out) {
+    if (kCache) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) out[i] = s_keys[k0 + i];
+    } else {
+      constexpr int kVecs = kPer * sizeof(KeyT) / 16;
+      const uint4* src = reinterpret_cast<const uint4*>(brow + k0);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v) {
+        const uint4 x = src[v];
+        const KeyT* e = reinterpret_cast<const KeyT*>(&x);
+#pragma unroll
+        for (int i = 0; i < 16 / (int)sizeof(KeyT); ++i) {
+          const int64_t kk = k0 + v * (16 / sizeof(KeyT)) + i;
+          out[v * (16 / sizeof(KeyT)) + i] = valid(kk) ? Tr::key(e[i]) : sent;
+        }
+      }
+    }
+  };
+
+  const int64_t keff = p.k < K ? p.k : K;
+  if (keff == 0 || keff == K) {
+    // nothing or everything selected: out = valid (or nothing)
+    for (int64_t k0 = (int64_t)threadIdx.x * kPer; k0 < K; k0 += kChunk) {
+      uint32_t w[4] = {0, 0, 0, 0};
+      if (keff == K) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) w[i / 4] |= (uint32_t)valid(k0 + i) << (8 * (i % 4));
+      }
+      *reinterpret_cast<uint4*>(orow + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+
+  if (kCache) {
+    constexpr int kVecs = kPer * sizeof(KeyT) / 16;
+    for (int64_t k0 = (int64_t)threadIdx.x * kPer; k0 < K; k0 += kChunk) {
+      const uint4* src = reinterpret_cast<const uint4*>(brow + k0);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v) {
+        const uint4 x = src[v];
+        const KeyT* e = reinterpret_cast<const KeyT*>(&x);
+        KeyT kk[16 / sizeof(KeyT)];
+#pragma unroll
+        for (int i = 0; i < 16 / (int)sizeof(KeyT); ++i) {
+          const int64_t pos = k0 + v * (16 / sizeof(KeyT)) + i;
+          kk[i] = valid(pos) ? Tr::key(e[i]) : sent;
+        }
+        *reinterpret_cast<uint4*>(s_keys + k0 + v * (16 / sizeof(KeyT))) =
+            *reinterpret_cast<const uint4*>(kk);
+      }
+    }
+  }
+
+  // ---- radix select of the keff-th largest key ----
+  uint32_t prefix = 0;      // digits found so far, in place
+  uint32_t rem = (uint32_t)keff;
+  for (int shift = Tr::kBits - 8; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
+    __syncthreads();  // also orders the LDS key fill before the first pass
+    const int hs = shift + 8;  // bits above this digit must equal the prefix
+    for (int64_t k0 = (int64_t)threadIdx.x * kPer; k0 < K; k0 += kChunk) {
+      KeyT kk[kPer];
+      load16(k0, kk);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t key = (uint32_t)kk[i];
+        const bool match = hs >= Tr::kBits || ((key ^ prefix) >> hs) == 0;
+        if (match) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l covers digits 255-4l .. 252-4l (descending)
+      const int lane = threadIdx.x;
+      uint32_t c[4];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s_hist[255 - 4 * lane - j];
+        sum += c[j];
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const uint32_t excl = incl - sum;
+      if (excl < rem && rem <= incl) {
+        uint32_t above = excl;
+        int d = 255 - 4 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (above + c[j] >= rem) {
+            d = 255 - 4 * lane - j;
+            break;
+          }
+          above += c[j];
+        }
+        s_sel[0] = (uint32_t)d;
+        s_sel[1] = above;
+      }
+    }
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    rem -= s_sel[1];
+    __syncthreads();  // s_sel / s_hist reuse
+  }
+  const uint32_t T = prefix;
+  const int need = (int)rem;  // keys equal to T to take, lowest index first
+
+  // ---- write pass, index order ----
+  int taken = 0;
+  for (int64_t base = 0; base < K; base += kChunk) {
+    const int64_t k0 = base + (int64_t)threadIdx.x * kPer;
+    KeyT kk[kPer];
+    int neq = 0;
+    if (k0 < K) {
+      load16(k0, kk);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) neq += (uint32_t)kk[i] == T;
+    }
+    int tot;
+    int r = taken + block_excl_sum(neq, s_wave, tot);
+    if (k0 < K) {
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t key = (uint32_t)kk[i];
+        bool sel = key > T;
+        if (key == T) {
+          sel = r < need;
+          ++r;
+        }
+        w[i / 4] |= (uint32_t)(sel && valid(k0 + i)) << (8 * (i % 4));
+      }
+      *reinterpret_cast<uint4*>(orow + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    taken += tot;
+  }
+}
+
+constexpr size_t kCacheMax = 64 * 1024;
+
+}  // namespace
+
+hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
+  const int64_t rows = p.Bb * p.Hb * p.Qb;
+  if (rows == 0 || p.K == 0) return hipSuccess;
+  const size_t ksz = p.is_bf16 ? 2 : 4;
+  const size_t bytes = (size_t)p.K * ksz;
+  const bool cache = bytes <= kCacheMax;
+  const dim3 grid((unsigned)rows), block(kThreads);
+  if (p.is_bf16) {
+    if (cache)
+      hipLaunchKernelGGL((k_topk<uint16_t, true>), grid, block, bytes, s, p);
+    else
+      hipLaunchKernelGGL((k_topk<uint16_t, false>), grid, block, 0, s, p);
+  } else {
+    if (cache)
+      hipLaunchKernelGGL((k_topk<uint32_t, true>), grid, block, bytes, s, p);
+    else
+      hipLaunchKernelGGL((k_topk<uint32_t, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsm

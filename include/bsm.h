@@ -1,0 +1,203 @@
+/*
+ * bsm.h -- C ABI of the block-sparse masked attention library for MI355X
+ * (gfx950). One shared library, libbsm.so; every entry point below is
+ * extern "C", takes plain pointers and sizes, and enqueues its work on the
+ * caller's HIP stream.
+ *
+ * Sources (cited by title and section):
+ *   [SF-452]  SpecForge issue #452, "flex_attention BlockMask incorrectly created
+ *             with H=num_heads" -- traceback (create_block_mask returns a partial
+ *             and a full block part), Problem, Expected Behavior (one head-shared
+ *             block mask).
+ *   [SF-905]  SpecForge PR #905, "Fix DFlash attention masking" -- Motivation
+ *             (is_causal x layer-type rule), maintainer reply item #934
+ *             (resolve_dflash_is_causal, left-bound-only in-block window).
+ *   [SF-474]  SpecForge issue #474, "DFlash block mask currently relies on Flex
+ *             Attention only" -- Suggestion 2 (dense [B,1,Q_LEN,KV_LEN] bool mask).
+ *   [FSA-190] flash-sparse-attention PR #190, "Broadcastable 4D mask/bias,
+ *             128-rounded key length, stride-0 broadcasting, and dbias
+ *             reductions" -- Design, Changes (mha_fwd validation), Implementation
+ *             Notes (swapped path, stability fix).
+ *   [FSA-197] flash-sparse-attention PR #197, "Centralize dynamic mask creation
+ *             for FDMA" -- Design, Changes, Implementation Notes, review
+ *             suggestion on dynamic_mask.
+ *
+ * Conventions shared by all entry points
+ *   Layout. Q is (B, Sq, H, D); K and V are (B, Sk, KVH, D); O is (B, Sq, H, D);
+ *     all with element strides and the last dimension contiguous. LSE is float
+ *     (B, H, Sq), contiguous. G = H / KVH; the KV head of head h is h / G.
+ *   Aux tensors (mask, bias) are 4D: ({B|1}, {H|KVH|1}, {Sq|1}, K_round) with
+ *     K_round = round_multiple(Sk, 128) = (Sk + 127) / 128 * 128, last dim
+ *     contiguous ([FSA-190] Design). A size-1 dim broadcasts and its stride is
+ *     ignored (read as 0); a stride of 0 on a dim of size > 1 is rejected (no
+ *     implicit expand, [FSA-190] Changes). Keys >= Sk are never kept, whatever
+ *     the tail of a mask or bias holds ([FSA-190] Implementation Notes).
+ *     Mask: 1 byte per element, nonzero = keep. Bias: additive, unscaled, same
+ *     dtype as Q. Mask and bias rows must start 16-byte aligned.
+ *   Tiles. 128 queries x 128 keys. nQ = ceil(Sq / 128), nK = K_round / 128.
+ *   Swap. When Sq == 1 and H > KVH, the library runs the head-group swap of
+ *     [FSA-190] Design / Implementation Notes: the H heads of one KV group are
+ *     treated as G query rows of KV head kvh, by views only. build_block_mask
+ *     and masked_attn_fwd both apply it, so a block mask always lives in the
+ *     iteration space of the attention kernel; block_mask_shape reports it.
+ *   Ownership. The caller allocates every device buffer; the library allocates
+ *     no device memory and keeps no state except a thread-local error string.
+ *     Work is enqueued on `stream` with no host synchronisation, so inputs and
+ *     outputs must stay alive until that stream's work completes.
+ *   Errors. Every entry point returns 0 (BSM_OK) or a negative bsm_status. On a
+ *     validation error nothing is enqueued and no output is touched;
+ *     bsm_last_error() then describes the failure. BSM_E_HIP reports a failed
+ *     kernel launch on the caller's stream.
+ */
+#ifndef BSM_H
+#define BSM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSM_OK = 0,
+  BSM_E_ARG = -1,         /* bad scalar argument or NULL pointer */
+  BSM_E_SHAPE = -2,       /* sizes violate the 4D / GQA / DFlash contract */
+  BSM_E_STRIDE = -3,      /* non-contiguous last dim, illegal 0 stride, misalignment */
+  BSM_E_DTYPE = -4,       /* dtype not allowed for this argument */
+  BSM_E_UNSUPPORTED = -5, /* valid request outside what this build implements */
+  BSM_E_HIP = -6          /* HIP launch error */
+} bsm_status;
+
+typedef enum {
+  BSM_BOOL = 0, /* 1 byte per element, nonzero = keep */
+  BSM_BF16 = 1,
+  BSM_F32 = 2
+} bsm_dtype;
+
+/* A 4D device tensor view: element sizes and element strides. */
+typedef struct {
+  const void* data;
+  int32_t dtype;     /* bsm_dtype */
+  int32_t reserved;  /* must be 0 */
+  int64_t size[4];
+  int64_t stride[4];
+} bsm_tensor4;
+
+typedef struct {
+  int64_t B, H, KVH, Sq, Sk, D;
+} bsm_geom;
+
+/* DFlash draft-block predicate ([SF-452] Problem; [SF-905] Motivation, #934).
+ * Keys: ctx_len C context tokens, then num_blocks NB draft blocks of
+ * block_size bs tokens (Sk = C + NB*bs). Queries: the NB*bs draft tokens.
+ * Draft block j sees context keys k < E_j = clamp((j+1)*S + ctx_end_offset, 0, C)
+ * with S = ctx_per_block (0 -> C / NB, which requires C % NB == 0), and the
+ * draft tokens of its own block (token i sees i' <= i if in-block attention is
+ * causal). is_causal: -1 absent, 0, 1; layer_type: 0 full-attention,
+ * 1 sliding-attention. Causality = resolve_dflash_is_causal(is_causal,
+ * layer_type). On sliding layers a key is visible only if
+ * pos_q - pos_k < sliding_window (left bound only), with pos(context c) = c and
+ * pos(draft token i of block j) = E_j + i. The mask is the same for every batch
+ * entry and head. */
+typedef struct {
+  int64_t ctx_len, num_blocks, block_size, ctx_per_block, ctx_end_offset;
+  int32_t is_causal;
+  int32_t layer_type;
+  int64_t sliding_window;
+} bsm_dflash;
+
+/* Block mask ([SF-452] traceback: partial and full block parts). Four int32
+ * device arrays: kv_num_blocks / full_kv_num_blocks of shape (Bm, Hm, nQm),
+ * kv_indices / full_kv_indices of shape (Bm, Hm, nQm, nK), contiguous.
+ * For query tile qt, kv_indices lists the partial key tiles (some but not all
+ * pairs kept) and full_kv_indices the full ones (all pairs kept), ascending,
+ * padded with -1. Tiles in neither list are empty and never visited. */
+typedef struct {
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+  int64_t Bm, Hm, nQm, nK;
+} bsm_block_mask;
+
+typedef struct {
+  bsm_tensor4 q, k, v;       /* bf16 or f32, all the same dtype */
+  void* o;                   /* output, q's dtype, sizes (B, Sq, H, D) */
+  int64_t o_stride[4];
+  float* lse;                /* nullable; float (B, H, Sq) contiguous, natural log */
+  float softmax_scale;       /* <= 0 selects 1 / sqrt(D) */
+  int32_t reserved;          /* must be 0 */
+  const bsm_dflash* pred;    /* nullable; DFlash predicate as the mask */
+  const bsm_tensor4* mask;   /* nullable; bool aux tensor (not with pred) */
+  const bsm_tensor4* bias;   /* nullable; additive aux tensor */
+  const bsm_block_mask* bm;  /* nullable; NULL visits every key tile */
+} bsm_attn_args;
+
+/* In-block causality of a DFlash layer ([SF-905] Motivation; #934):
+ * is_causal absent (-1) -> 0 on full-attention layers, 1 on sliding ones;
+ * 0 -> 0; 1 -> 1. Returns 0 or 1, or BSM_E_ARG for any other input.
+ * Host only; enqueues nothing. */
+int resolve_dflash_is_causal(int32_t is_causal, int32_t layer_type);
+
+/* Shape (Bm, Hm, nQm, nK) of the block mask build_block_mask produces for this
+ * geometry and mask source (exactly one of pred / mask non-NULL), so the caller
+ * can allocate the four arrays. DFlash: (1, 1, nQ, nK), shared by every batch
+ * entry and head ([SF-452] Expected Behavior). Dense mask: (mask B, mask H,
+ * ceil(mask Sq / 128), nK), after the swap when it applies. Host only. */
+int block_mask_shape(const bsm_geom* geom, const bsm_dflash* pred,
+                     const bsm_tensor4* mask, int64_t out_shape[4]);
+
+/* Build the block mask of a DFlash predicate (pred) or of a dense bool mask
+ * (mask, after the swap when it applies), exactly one non-NULL. out's
+ * dimensions must equal block_mask_shape's and its four arrays must be device
+ * buffers of those sizes. The DFlash path never materialises the dense mask;
+ * the dense path reads the mask once. Replaces flex_attention's dense
+ * create_block_mask reduction ([SF-452] traceback). */
+int build_block_mask(const bsm_geom* geom, const bsm_dflash* pred,
+                     const bsm_tensor4* mask, const bsm_block_mask* out,
+                     hipStream_t stream);
+
+/* Dynamic top-k keep mask over an additive bias ([FSA-197] Design,
+ * Implementation Notes, review suggestion on dynamic_mask).
+ * bias: bf16 or f32, 4D (Bb, Hb, Qb, round_multiple(seqlen_k, 128)), last dim
+ * contiguous. premask: NULL or bool 4D with dims 1 or equal to the bias's and
+ * last dim seqlen_k or the bias's (zero-copy view of a 2D (B, seqlen_k) mask as
+ * (B, 1, 1, seqlen_k) is allowed); keys at or beyond its last dim count as
+ * masked. Per row: invalid keys (pre-masked, or >= seqlen_k) take the bias
+ * dtype's minimum finite value, the k largest values are selected (ties go to
+ * the lower key index; -0 == +0), and out = selected AND valid, so a row keeps
+ * exactly min(k, #valid) keys. out_mask: device, contiguous bool with the
+ * bias's sizes. k < 0 is BSM_E_ARG. */
+int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask,
+                      int64_t seqlen_k, int64_t k, uint8_t* out_mask,
+                      hipStream_t stream);
+
+/* Dense DFlash mask, materialised: out_mask is a device, contiguous bool array
+ * (Sq, K_round) (the [B,1,Q_LEN,KV_LEN] mask of [SF-474] Suggestion 2 with the
+ * batch dim dropped, keys rounded to 128, tail False). For consumers that need
+ * a dense mask; the block-sparse path never calls it. */
+int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred,
+                      uint8_t* out_mask, hipStream_t stream);
+
+/* Masked scaled-dot-product attention forward ([FSA-190] Design, Changes;
+ * [SF-452]). For each (b, h, query q) with kept keys j < Sk:
+ *   s_j = scale * <q, k_j> + bias[b', h', q', j],  O = softmax(s) V,
+ *   LSE = log sum_j exp(s_j);
+ * a row with no kept key gets O = 0 and LSE = -inf. With a block mask only its
+ * listed tiles are visited (full tiles skip the mask test); it must have been
+ * built by build_block_mask for the same geometry and mask source. bf16 runs on
+ * bf16 MFMA with float accumulation and a float online softmax, O rounded to
+ * nearest even; f32 computes in float. D must be 64 or 128. */
+int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* args,
+                    hipStream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). The pointer
+ * stays valid until the next call into the library on this thread. */
+const char* bsm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSM_H */

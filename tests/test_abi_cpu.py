@@ -1,0 +1,197 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/bsm.h declares, and its host-only logic (is_causal resolution, block mask
+shapes, argument validation) answers without touching a device. Validation
+cases use fake, never-dereferenced device addresses and must fail before any
+launch."""
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import GOLDEN, ROOT
+
+from block_sparse_masked_mask_amd import bsm
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsm.LIB_PATH):
+        from block_sparse_masked_mask_amd.build import build
+        build()
+    return bsm.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "bsm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(L):
+    decl = _declared_functions()
+    assert set(decl) == set(bsm.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", bsm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in decl:
+        assert name in syms, name
+        assert hasattr(L, name)
+
+
+def test_struct_sizes_match_header():
+    # C layout: pointer 8, two int32, 2 x int64[4]
+    assert ctypes.sizeof(bsm.Tensor4) == 80
+    assert ctypes.sizeof(bsm.DFlashC) == 56
+    assert ctypes.sizeof(bsm.BlockMaskC) == 64
+    assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 4 * 8
+
+
+def test_resolve_is_causal_table(L):
+    tab = json.load(open(os.path.join(GOLDEN, "dflash_is_causal.json")))["table"]
+    for e in tab:
+        ic = -1 if e["is_causal"] is None else int(e["is_causal"])
+        lt = 0 if e["layer_type"] == "full" else 1
+        assert L.resolve_dflash_is_causal(ic, lt) == int(e["causal"])
+    assert L.resolve_dflash_is_causal(2, 0) == bsm.BSM_E_ARG
+    assert L.resolve_dflash_is_causal(-1, 2) == bsm.BSM_E_ARG
+    assert b"layer_type" in L.bsm_last_error()
+
+
+def _t4(shape, dtype=bsm.BSM_BOOL, strides=None, data=1 << 20):
+    t = bsm.Tensor4()
+    t.data = data
+    t.dtype = dtype
+    t.reserved = 0
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i in range(4):
+        t.size[i] = shape[i]
+        t.stride[i] = strides[i]
+    return t
+
+
+def _shape(L, geom, pred=None, mask=None):
+    out = (ctypes.c_int64 * 4)()
+    g = bsm.Geom(*geom)
+    st = L.block_mask_shape(ctypes.byref(g), ctypes.byref(pred) if pred else None,
+                            ctypes.byref(mask) if mask else None, out)
+    return st, tuple(out)
+
+
+def test_block_mask_shapes(L):
+    # DFlash: one (1, 1, nQ, nK) block mask for every batch entry and head
+    tiny = bsm.DFlash(256, 4, 16).c()
+    assert _shape(L, (1, 2, 2, 64, 320, 64), pred=tiny) == (0, (1, 1, 1, 3))
+    train = bsm.DFlash(4096, 256, 16).c()
+    assert _shape(L, (2, 32, 8, 4096, 8192, 128), pred=train) == (0, (1, 1, 32, 64))
+    long = bsm.DFlash(32768, 2048, 16, is_causal=True, layer_type="sliding",
+                      sliding_window=4096).c()
+    assert _shape(L, (1, 32, 8, 32768, 65536, 128), pred=long) == (0, (1, 1, 256, 512))
+    # dense top-k mask (B, KVH, 1, 8064) broadcast over queries
+    m = _t4((2, 4, 1, 8064))
+    assert _shape(L, (2, 16, 4, 8000, 8000, 128), mask=m) == (0, (2, 4, 1, 63))
+    # decode: (B, H, 1, K) under the head-group swap -> (B, KVH, 1 tile of G rows, nK)
+    m = _t4((64, 32, 1, 16384))
+    assert _shape(L, (64, 32, 8, 1, 16384, 128), mask=m) == (0, (64, 8, 1, 128))
+    # no swap when H == KVH
+    m = _t4((3, 8, 1, 256))
+    assert _shape(L, (3, 8, 8, 1, 200, 64), mask=m) == (0, (3, 8, 1, 2))
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(mask_shape=(2, 4, 1, 8000)), bsm.BSM_E_SHAPE),      # K not rounded to 128
+    (dict(mask_shape=(3, 4, 1, 8064)), bsm.BSM_E_SHAPE),      # batch not B or 1
+    (dict(mask_shape=(2, 5, 1, 8064)), bsm.BSM_E_SHAPE),      # head not H, KVH or 1
+    (dict(mask_shape=(2, 4, 7, 8064)), bsm.BSM_E_SHAPE),      # query not Sq or 1
+    (dict(mask_shape=(2, 4, 1, 8064), dtype=bsm.BSM_BF16), bsm.BSM_E_DTYPE),
+    (dict(mask_shape=(2, 4, 1, 8064), strides=(0, 8064, 8064, 1)), bsm.BSM_E_STRIDE),  # expand
+    (dict(mask_shape=(2, 4, 1, 8064), strides=(8064 * 4, 8064, 8064, 2)), bsm.BSM_E_STRIDE),
+    (dict(mask_shape=(2, 4, 1, 8064), strides=(8064 * 4 + 3, 8064, 8064, 1)), bsm.BSM_E_STRIDE),
+    (dict(mask_shape=(2, 4, 1, 8064), data=(1 << 20) + 8), bsm.BSM_E_STRIDE),  # misaligned
+])
+def test_mask_validation(L, case, code):
+    m = _t4(case["mask_shape"], case.get("dtype", bsm.BSM_BOOL), case.get("strides"),
+            case.get("data", 1 << 20))
+    st, _ = _shape(L, (2, 16, 4, 8000, 8000, 128), mask=m)
+    assert st == code, L.bsm_last_error()
+
+
+def test_geometry_and_source_validation(L):
+    d = bsm.DFlash(256, 4, 16).c()
+    assert _shape(L, (1, 6, 4, 64, 320, 64), pred=d)[0] == bsm.BSM_E_SHAPE  # H % KVH
+    assert _shape(L, (1, 2, 2, 63, 320, 64), pred=d)[0] == bsm.BSM_E_SHAPE  # Sq != NB*bs
+    assert _shape(L, (1, 2, 2, 64, 300, 64), pred=d)[0] == bsm.BSM_E_SHAPE  # Sk != C + NB*bs
+    assert _shape(L, (1, 2, 2, 64, 320, 64))[0] == bsm.BSM_E_ARG            # no source
+    m = _t4((1, 1, 64, 384))
+    assert _shape(L, (1, 2, 2, 64, 320, 64), pred=d, mask=m)[0] == bsm.BSM_E_ARG
+    bad = bsm.DFlash(250, 4, 16).c()  # C % NB != 0 with derived ctx_per_block
+    assert _shape(L, (1, 2, 2, 64, 314, 64), pred=bad)[0] == bsm.BSM_E_ARG
+    nowin = bsm.DFlash(256, 4, 16, layer_type="sliding", sliding_window=0).c()
+    assert _shape(L, (1, 2, 2, 64, 320, 64), pred=nowin)[0] == bsm.BSM_E_ARG
+
+
+def _attn_args(geom, dtype=bsm.BSM_BF16, **kw):
+    B, H, KVH, Sq, Sk, D = geom
+    a = bsm.AttnArgs()
+    a.q = _t4((B, Sq, H, D), dtype)
+    a.k = _t4((B, Sk, KVH, D), dtype)
+    a.v = _t4((B, Sk, KVH, D), dtype)
+    a.o = 1 << 21
+    for i, s in enumerate(_t4((B, Sq, H, D)).stride):
+        a.o_stride[i] = s
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _attn(L, geom, a):
+    g = bsm.Geom(*geom)
+    return L.masked_attn_fwd(ctypes.byref(g), ctypes.byref(a), None)
+
+
+def test_attention_validation(L):
+    geom = (2, 16, 4, 64, 300, 128)
+    a = _attn_args(geom)
+    a.k = _t4((2, 300, 4, 128), bsm.BSM_F32)
+    assert _attn(L, geom, a) == bsm.BSM_E_DTYPE
+    a = _attn_args(geom)
+    a.q = _t4((2, 64, 16, 128), bsm.BSM_BF16, strides=(64 * 16 * 128, 16 * 128, 128, 2))
+    assert _attn(L, geom, a) == bsm.BSM_E_STRIDE
+    geom96 = (2, 16, 4, 64, 300, 96)
+    assert _attn(L, geom96, _attn_args(geom96)) == bsm.BSM_E_UNSUPPORTED
+    a = _attn_args(geom)
+    bias = _t4((2, 4, 1, 384), bsm.BSM_F32)
+    a.bias = ctypes.pointer(bias)
+    assert _attn(L, geom, a) == bsm.BSM_E_DTYPE       # bias dtype != q dtype
+    a = _attn_args(geom)
+    bm = bsm.BlockMaskC(1 << 22, 1 << 22, 1 << 22, 1 << 22, 1, 1, 1, 3)
+    a.bm = ctypes.pointer(bm)
+    assert _attn(L, geom, a) == bsm.BSM_E_ARG         # block mask without a source
+    a = _attn_args(geom)
+    m = _t4((2, 4, 1, 384))
+    a.mask = ctypes.pointer(m)
+    bm = bsm.BlockMaskC(1 << 22, 1 << 22, 1 << 22, 1 << 22, 2, 4, 1, 2)
+    a.bm = ctypes.pointer(bm)
+    assert _attn(L, geom, a) == bsm.BSM_E_SHAPE       # block mask for another geometry
+    assert b"block mask" in L.bsm_last_error()
+
+
+def test_topk_validation(L):
+    bias = _t4((2, 4, 1, 8064), bsm.BSM_BF16)
+    st = L.dynamic_topk_mask(ctypes.byref(bias), None, 8000, -1, 1 << 21, None)
+    assert st == bsm.BSM_E_ARG
+    st = L.dynamic_topk_mask(ctypes.byref(bias), None, 8100, 10, 1 << 21, None)
+    assert st == bsm.BSM_E_SHAPE
+    pm = _t4((2, 2, 1, 8000))
+    st = L.dynamic_topk_mask(ctypes.byref(bias), ctypes.byref(pm), 8000, 10, 1 << 21, None)
+    assert st == bsm.BSM_E_SHAPE
+    bad = _t4((2, 4, 1, 8064), bsm.BSM_BOOL)
+    st = L.dynamic_topk_mask(ctypes.byref(bad), None, 8000, 10, 1 << 21, None)
+    assert st == bsm.BSM_E_DTYPE

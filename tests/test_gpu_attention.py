@@ -1,0 +1,200 @@
+"""GPU parity: masked attention forward against the fp64 CPU oracle.
+
+Bars: bf16 inputs max|err| <= 2e-2 and mean|err| <= 2e-3, f32 inputs
+max|err| <= 1e-4, on O and on LSE; -inf LSE (fully masked rows) exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows,
+                         sample_rows, say, synth)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(q, k, v, dt, mask=None, pred=None, bias=None, bm=None, scale=None,
+                   rows=None, heads=None, what=""):
+    """Run the GPU path, compare the given rows of every (b, h) with the oracle."""
+    say("attention", what, tuple(q.shape), tuple(k.shape), dt)
+    o, lse = bsm.masked_attn_fwd(q, k, v, pred=pred, mask=mask, bias=bias, block_mask=bm,
+                                 softmax_scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    B, Sq, H, D = q.shape
+    omask = oracle_geom(pred) if pred is not None else mask
+    rows = np.arange(Sq) if rows is None else rows
+    heads = range(H) if heads is None else heads
+    o_np = o[:, rows].float().cpu().numpy()
+    lse_np = lse[:, :, rows].cpu().numpy()
+    for b in range(B):
+        for h in heads:
+            want_o, want_l = oracle_rows(q, k, v, b, h, rows, scale=scale, mask=omask, bias=bias)
+            assert_close(o_np[b, :, h, :], want_o, dt, f"{what} O b={b} h={h}")
+            assert_close(lse_np[b, h], want_l, dt, f"{what} LSE b={b} h={h}")
+    return o, lse
+
+
+def test_tiny_dflash_fp32():
+    """Tiny DFlash case in f32: 256 context + 4 blocks of 16, full layer."""
+    cfg = synth.CONFIGS["tiny_dflash_fp32"]
+    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"])
+    q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 2, 2, 64, "f32", seed=0))
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, pred=d)
+    assert int(bm.kv_num_blocks.sum()) == 3 and int(bm.full_kv_num_blocks.sum()) == 0
+    _run_and_check(q, k, v, "f32", pred=d, bm=bm, what="tiny+bm")
+    _run_and_check(q, k, v, "f32", pred=d, what="tiny")
+
+
+SMALL_DFLASH = [
+    dict(ctx_len=260, num_blocks=13, block_size=16),
+    dict(ctx_len=260, num_blocks=13, block_size=16, layer_type="sliding", sliding_window=100),
+    dict(ctx_len=260, num_blocks=13, block_size=16, is_causal=False, layer_type="sliding",
+         sliding_window=37),
+    dict(ctx_len=999, num_blocks=3, block_size=200, is_causal=True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_DFLASH)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_small_dflash(case, D, dt):
+    d = bsm.DFlash(**case)
+    q, k, v = cuda(*synth.qkv(2, d.Sq, d.Sk, 4, 2, D, dt, seed=1))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    _run_and_check(q, k, v, dt, pred=d, bm=bm, what=f"dflash {case} D={D}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("mshape,bshape", [
+    ((2, 4, 300, 640), None),
+    ((1, 1, 1, 640), (2, 2, 1, 640)),
+    ((2, 2, 1, 640), (1, 4, 300, 640)),
+    ((1, 4, 300, 640), (2, 1, 1, 640)),
+    (None, (2, 2, 300, 640)),
+    (None, None),
+])
+def test_dense_mask_and_bias(dt, mshape, bshape):
+    B, Sq, Sk, H, KVH, D = 2, 300, 600, 4, 2, 128
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, dt, seed=2))
+    mask = bias = None
+    if mshape is not None:
+        m = synth.random_bool(mshape, 0.3, 2, synth.TID_MASK)
+        m[..., 5] = True
+        mask = torch.from_numpy(m).cuda()
+    if bshape is not None:
+        bias = synth.normal_tensor(bshape, 2, synth.TID_BIAS, dt).cuda()
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask) if mask is not None else None
+    _run_and_check(q, k, v, dt, mask=mask, bias=bias, bm=bm, scale=0.07,
+                   what=f"dense m={mshape} b={bshape}")
+    if mask is not None:
+        _run_and_check(q, k, v, dt, mask=mask, bias=bias, scale=0.07, what="dense, no bm")
+
+
+def test_fully_masked_rows_and_single_keys():
+    B, Sq, Sk, H, KVH, D = 1, 200, 300, 2, 1, 64
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=3))
+    m = np.zeros((1, 1, Sq, 384), bool)
+    m[0, 0, ::3, 7] = True          # single kept key
+    m[0, 0, 1::3, :] = True         # everything kept (and the tail, ignored)
+    # rows 2::3 keep nothing
+    mask = torch.from_numpy(m).cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    o, lse = _run_and_check(q, k, v, "bf16", mask=mask, bm=bm, what="masked rows")
+    assert (o[0, 2::3].float() == 0).all()
+    assert torch.isneginf(lse[0, :, 2::3]).all()
+    # a single kept key returns that value row, rounded to bf16
+    torch.testing.assert_close(o[0, ::3, 0].float(), v[0, 7:8, 0].float().expand(67, 64),
+                               rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("with_mask", [True, False])
+def test_decode_swap_small(with_mask):
+    """seqlen_q == 1 with H > KVH runs the head-group swap; compare with the
+    unswapped definition."""
+    B, Sk, H, KVH, D = 3, 1000, 8, 2, 128
+    q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=4))
+    bias = synth.normal_tensor((B, H, 1, 1024), 4, synth.TID_BIAS, "bf16").cuda()
+    mask = bm = None
+    if with_mask:
+        mask = bsm.dynamic_topk_mask(bias, None, Sk, 100)
+        bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+        assert bm.kv_indices.shape == (B, KVH, 1, 8)
+    _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, what="swap")
+
+
+def test_decode_swap_pred():
+    d = bsm.DFlash(200, 1, 1)
+    q, k, v = cuda(*synth.qkv(2, 1, d.Sk, 8, 2, 64, "bf16", seed=5))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what="swap pred")
+
+
+def test_deterministic():
+    d = bsm.DFlash(260, 13, 16, layer_type="sliding", sliding_window=100)
+    q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 4, 2, 128, "bf16", seed=6))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    o1 = bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm)
+    o2 = bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm)
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+
+
+def _dflash_full(name, layer, rows_per_head=24, heads=(0, 5, 31)):
+    cfg = synth.CONFIGS[name]
+    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
+                   is_causal=layer["is_causal"], layer_type=layer["layer_type"],
+                   sliding_window=layer["window"])
+    q, k, v = cuda(*synth.qkv(cfg["B"], d.Sq, d.Sk, cfg["H"], cfg["KVH"], cfg["D"], cfg["dtype"],
+                              seed=0, scale=cfg["qkv_scale"]))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    rows = sample_rows(d.Sq, rows_per_head, seed=1)
+    _run_and_check(q, k, v, cfg["dtype"], pred=d, bm=bm, rows=rows, heads=heads,
+                   what=f"{name}/{layer['name']}")
+
+
+@pytest.mark.parametrize("layer", synth.CONFIGS["dflash_train_bf16"]["layers"],
+                         ids=lambda l: l["name"])
+def test_dflash_train_full_size(layer):
+    _dflash_full("dflash_train_bf16", layer)
+
+
+def test_long_dflash_full_size():
+    _dflash_full("long_dflash_bf16", synth.CONFIGS["long_dflash_bf16"]["layers"][0],
+                 rows_per_head=12, heads=(0, 31))
+
+
+def test_dynamic_topk_attention_full_size():
+    cfg = synth.CONFIGS["dynamic_topk_bf16"]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0))
+    bias, pad2d = synth.topk_inputs(cfg, seed=0)
+    bias, pad2d = bias.cuda(), pad2d.cuda()
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    rows = sample_rows(Sq, 16, seed=2)
+    _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, rows=rows, heads=(0, 7, 15),
+                   what="dynamic top-k")
+
+
+def test_decode_full_size():
+    cfg = synth.CONFIGS["decode_swap_bf16"]
+    B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
+    q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0))
+    bias, _ = synth.topk_inputs(cfg, seed=0)
+    bias = bias.cuda()
+    mask = bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"])
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm, return_lse=True)
+    torch.cuda.synchronize()
+    say("decode full size: comparing sampled (b, h)")
+    for b in (0, 17, 63):
+        for h in (0, 13, 31):
+            want_o, want_l = oracle_rows(q, k, v, b, h, [0], mask=mask, bias=bias)
+            assert_close(o[b, 0, h].float().cpu().numpy()[None], want_o, "bf16", f"O b={b} h={h}")
+            assert_close(lse[b, h].cpu().numpy(), want_l, "bf16", f"LSE b={b} h={h}")
