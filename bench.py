@@ -1,0 +1,232 @@
+"""Benchmark of the block-sparse masked attention hot path on one MI355X.
+
+One step = one pass of the DFlash training-shape workload through the library:
+resolve the layer's in-block causality, build the head-shared block mask from the
+DFlash predicate, and run the masked attention forward -- for a full-attention
+layer (bidirectional in-block) and a sliding-window layer (causal in-block,
+left-bound window 2048). B=2, H=32, KVH=8, D=128, 4096 context tokens + 256 draft
+blocks of 16 (Sq=4096 queries, Sk=8192 keys), bf16, Q/K/V ~ 0.5 N(0,1).
+
+value = counted flops of the step / step time, where counted flops are
+4 * D * (rows x keys) summed over the non-empty 128x128 tiles of every (b, h)
+(QK^T plus PV; exp not counted). The JSON line also carries:
+  roofline     -- the attention kernel alone: algorithmic flops per launch over
+                  its HIP-event-timed average launch duration, against the bf16
+                  dense MFMA peak;
+  mask_build   -- the dense-mask block-mask builder on the long-context DFlash
+                  mask materialised densely (1 x 1 x 32768 x 65536 bytes), GB/s
+                  against HBM peak;
+  cpu_baseline -- the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_masked_mask_amd import bsm, synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+WORKLOAD = "dflash_train_bf16"
+METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build GB/s"
+
+
+def counted_flops(bm, geom):
+    """4*D*rows*keys over non-empty tiles of every (b, h), from a block mask."""
+    B, H, KVH, Sq, Sk, D = geom
+    kvn, kvi, fn, fi = [t.cpu().numpy() for t in bm]
+    Bm, Hm, nQm, nK = kvi.shape
+    total = 0
+    for b in range(B):
+        for h in range(H):
+            mb = 0 if Bm == 1 else b
+            mh = 0 if Hm == 1 else (h if Hm == H else h // (H // KVH))
+            for qt in range((Sq + 127) // 128):
+                mq = 0 if nQm == 1 else qt
+                rows = min(128, Sq - 128 * qt)
+                tiles = list(kvi[mb, mh, mq, :kvn[mb, mh, mq]]) + \
+                    list(fi[mb, mh, mq, :fn[mb, mh, mq]])
+                for kt in tiles:
+                    total += rows * min(128, Sk - 128 * int(kt))
+    return 4 * D * total
+
+
+class Step:
+    """The DFlash training-shape step: both layers, block mask + attention."""
+
+    def __init__(self, seed=0):
+        cfg = synth.CONFIGS[WORKLOAD]
+        self.cfg = cfg
+        self.layers = []
+        for lay in cfg["layers"]:
+            d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
+                           is_causal=lay["is_causal"], layer_type=lay["layer_type"],
+                           sliding_window=lay["window"])
+            self.layers.append((lay["name"], d))
+        d0 = self.layers[0][1]
+        self.q, self.k, self.v = [t.cuda() for t in synth.qkv(
+            cfg["B"], d0.Sq, d0.Sk, cfg["H"], cfg["KVH"], cfg["D"], "bf16", seed=seed,
+            scale=cfg["qkv_scale"])]
+        self.geom = bsm.geometry_of(self.q, self.k)
+        self.out = [torch.empty_like(self.q) for _ in self.layers]
+        self.bms = [bsm.build_block_mask(self.geom, pred=d) for _, d in self.layers]
+        self.flops = [counted_flops(bm, self.geom) for bm in self.bms]
+        self.attn_events = []
+
+    def run(self, record=False):
+        stream = torch.cuda.current_stream()
+        for i, (name, d) in enumerate(self.layers):
+            bsm.resolve_dflash_is_causal(d.is_causal, d.layer_type)
+            bm = bsm.build_block_mask(self.geom, pred=d)
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            bsm.masked_attn_fwd(self.q, self.k, self.v, pred=d, block_mask=bm, out=self.out[i])
+            if record:
+                e1.record(stream)
+                self.attn_events.append((i, e0, e1))
+
+
+def measure_mask_build(reps=5):
+    """Dense builder on the long-context DFlash mask written out densely."""
+    d = bsm.DFlash(32768, 2048, 16, is_causal=True, layer_type="sliding", sliding_window=4096)
+    geom = bsm.Geometry(1, 32, 8, d.Sq, d.Sk, 128)
+    dense = bsm.dflash_dense_mask(geom, d)[None, None]
+    bm = bsm.build_block_mask(geom, mask=dense)  # warm
+    ref = bsm.build_block_mask(geom, pred=d)
+    for a, b in zip(bm, ref):
+        if not torch.equal(a, b):
+            raise RuntimeError("dense and predicate block masks differ")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bsm.build_block_mask(geom, mask=dense)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    nbytes = dense.numel() + 4 * sum(t.numel() for t in bm)
+    ms = float(np.mean(times))
+    del dense
+    return {"workload": "long_dflash_dense_mask", "shape": [1, 1, d.Sq, 65536],
+            "bytes": int(nbytes), "ms": ms, "GB/s": nbytes / ms / 1e6,
+            "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def cpu_baseline(step, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of the step's work, in the metric's unit."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg = step.cfg
+    q, k, v = step.q.cpu(), step.k.cpu(), step.v.cpu()
+    rng = np.random.default_rng(0)
+    done_flops = 0
+    units = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        li = units % len(step.layers)
+        _, d = step.layers[li]
+        b = int(rng.integers(cfg["B"]))
+        h = int(rng.integers(cfg["H"]))
+        qt = int(rng.integers(d.Sq // 128))
+        og = oracle.DFlashGeom(d.ctx_len, d.num_blocks, d.block_size, d.ctx_per_block,
+                               d.ctx_end_offset, d.is_causal, d.layer_type, d.sliding_window)
+        rows = np.arange(128 * qt, 128 * qt + 128)
+        qb = synth.as_f64(q[b:b + 1])
+        kb = synth.as_f64(k[b:b + 1])
+        vb = synth.as_f64(v[b:b + 1])
+        oracle.attention_rows(qb, kb, vb, 0, h, rows, mask=og)
+        band = oracle.dflash_dense_mask(og, rows)
+        part, full = oracle.blockmask.classify_tile_band(band, og.Sk)
+        done_flops += 4 * cfg["D"] * 128 * 128 * (len(part) + len(full))
+        units += 1
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{units} random (layer, b, h, 128-row query tile) units of the "
+                      f"{WORKLOAD} step, float64, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mask-build", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
+              "is measured on a single MI355X; sharding is described, not run.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    step = Step()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(record=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el * 1e3 / args.steps
+    flops_step = sum(step.flops)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    attn_ms = [e0.elapsed_time(e1) for _, e0, e1 in step.attn_events]
+    attn_flops = [step.flops[i] for i, _, _ in step.attn_events]
+    achieved = sum(attn_flops) / (sum(attn_ms) * 1e-3) / 1e12
+    per_layer = {}
+    for li, (name, _) in enumerate(step.layers):
+        ms = [e0.elapsed_time(e1) for i, e0, e1 in step.attn_events if i == li]
+        per_layer[name] = {"attn_ms": float(np.mean(ms)), "flops": int(step.flops[li]),
+                           "TFLOP/s": step.flops[li] / (np.mean(ms) * 1e-3) / 1e12}
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": 2, "H": 32, "KVH": 8, "D": 128,
+                   "ctx_len": 4096, "draft_blocks": 256, "block_size": 16,
+                   "Sq": 4096, "Sk": 8192, "layers": [n for n, _ in step.layers],
+                   "flops_per_step": int(flops_step)},
+        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": float(np.mean(attn_ms)),
+                     "flops_per_launch": float(np.mean(attn_flops))},
+        "per_layer": per_layer,
+    }
+    if not args.no_mask_build:
+        line["mask_build"] = measure_mask_build()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(step)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
