@@ -214,7 +214,7 @@ def main():
                    "ctx_len": 4096, "draft_blocks": 256, "block_size": 16,
                    "Sq": 4096, "Sk": 8192, "layers": [n for n, _ in step.layers],
                    "flops_per_step": int(flops_step)},
-        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16_v2<128>", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                      "avg_launch_ms": float(np.mean(attn_ms)),

@@ -58,8 +58,12 @@ struct TileList {
   // key tile of visit i, and whether it is full (no mask test needed)
   __device__ inline int tile(int i, bool& is_full) const {
     is_full = i < nfull;
-    if (is_full) return full ? full[i] : i;
-    return part ? part[i - nfull] : i - nfull;
+    int kt;
+    if (is_full)
+      kt = full ? full[i] : i;
+    else
+      kt = part ? part[i - nfull] : i - nfull;
+    return __builtin_amdgcn_readfirstlane(kt);  // uniform across the workgroup
   }
 };
 

@@ -1,0 +1,423 @@
+// Masked attention forward, bf16, pipelined variant for gfx950.
+//
+// Same arithmetic as k_attn_bf16 (attn.hip): S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_32x32x16_bf16 with a float online softmax, full tiles without a
+// mask test, partial tiles testing the DFlash row intervals or the mask bytes,
+// additive bias, keys >= Sk never kept (flash-sparse-attention PR #190, Design;
+// SpecForge issue #452). What changes is how K and V reach the matrix cores:
+//
+//  * 512 threads = 8 waves: waves 0-3 take 128 query rows of head h, waves 4-7
+//    the same rows of head h+1 of the same KV group, so one K/V tile in LDS
+//    feeds two heads. Used when both heads share the block mask row (a block
+//    mask broadcast over heads, or over the heads of a KV group).
+//  * K and V tiles go from HBM/L2 straight into LDS with 16-byte LDS-DMA loads
+//    (global_load_lds_dwordx4: each wave instruction fills 1 KiB of LDS), double
+//    buffered: the loads of tile i+1 are in flight while tile i is computed.
+//  * Both tiles stay row-major ([key][d]). Rows are XOR-swizzled in 16-byte
+//    chunks (the swizzle is applied to the global addresses, since an LDS-DMA
+//    instruction writes 64 consecutive 16-byte slots): K with
+//    (r & 3) | ((r >> 1) & 4), which spreads the 8 rows one 16-byte read group
+//    touches over 8 distinct bank groups; V with 2 (r & 3), which spreads the
+//    4 rows of one transposed read.
+//  * V^T operands come from ds_read_b64_tr_b16: in each 16-lane group, lane
+//    4e + g points at 4 d-values of key row e; the hardware hands lane 4g + s
+//    the 4 keys of d-value s. Two such reads give a lane the 8 consecutive keys
+//    of one d column that the MFMA A operand needs, with no transpose pass.
+//  * Work items (b, KV group pair, query tile) are laid out so that each XCD
+//    gets a contiguous range (so the query tiles of one (b, kvh) share an L2)
+//    and, inside a head pair, the heaviest query tiles first.
+#include <math.h>
+
+#include "attn_common.h"
+#include "bsm_internal.h"
+#include "dflash_rows.h"
+
+namespace bsm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kThreads = 512;
+constexpr int kXcds = 8;
+
+__device__ inline int perm_row(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
+__device__ inline int swz_k(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ inline int swz_v(int r) { return (r & 3) << 1; }
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// vmcnt <= n, other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D>
+struct Tiles {
+  __bf16 k[kTile * D];
+  __bf16 v[kTile * D];
+};
+
+template <int D>
+struct V2Ctx {
+  static constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  static constexpr int LOADS = kTile * D * 2 / (kThreads * 16);  // per tensor per thread
+  static constexpr int NS = D / 16;
+  static constexpr int NDC = D / 32;
+};
+
+// Byte offsets (within one (b, kv head)) of this thread's LDS-DMA chunks of
+// key tile 0; tile kt adds kt * 128 rows. Rows >= Sk fall outside the buffer
+// resource's range and load as zeros.
+template <int D>
+struct Loader {
+  uint32_t koff[V2Ctx<D>::LOADS];
+  uint32_t voff[V2Ctx<D>::LOADS];
+  uint32_t ktile_bytes, vtile_bytes;  // bytes per 128 rows
+  __amdgpu_buffer_rsrc_t kr, vr;
+
+  __device__ inline void init(const void* kbase, const void* vbase, int64_t k_sk, int64_t v_sk,
+                              int Sk, int w, int lane) {
+    constexpr int CPR = V2Ctx<D>::CPR;
+    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), 0,
+                                           (int)((int64_t)Sk * k_sk * 2), 0x00020000);
+    vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), 0,
+                                           (int)((int64_t)Sk * v_sk * 2), 0x00020000);
+    ktile_bytes = (uint32_t)(kTile * k_sk * 2);
+    vtile_bytes = (uint32_t)(kTile * v_sk * 2);
+#pragma unroll
+    for (int j = 0; j < V2Ctx<D>::LOADS; ++j) {
+      const int f = (j * (kThreads / 64) + w) * 64 + lane;
+      const int r = f / CPR;
+      const int c = f % CPR;
+      koff[j] = (uint32_t)(r * k_sk * 2 + ((c ^ swz_k(r)) * 16));
+      voff[j] = (uint32_t)(r * v_sk * 2 + ((c ^ swz_v(r)) * 16));
+    }
+  }
+
+  // The loads are written as inline asm so that the compiler does not treat
+  // them as LDS stores it must wait for before every LDS read (it cannot tell
+  // the two buffers apart); completion is awaited explicitly with wait_vmcnt
+  // before the barrier that publishes a buffer. The instruction has no
+  // destination register: data goes to LDS at m0 + 16 * lane.
+  __device__ inline void issue(Tiles<D>& t, int kt, int w) const {
+#pragma unroll
+    for (int j = 0; j < V2Ctx<D>::LOADS; ++j) {
+      const int slot = (j * (kThreads / 64) + w) * 64;  // first 16-byte slot of the wave
+      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
+      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
+      const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
+      const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+          "s_mov_b32 m0, %3\n\t"
+          "buffer_load_dwordx4 %4, %5, 0 offen lds"
+          :
+          : "s"(__builtin_amdgcn_readfirstlane(lk)), "v"(ok), "s"(kr),
+            "s"(__builtin_amdgcn_readfirstlane(lv)), "v"(ov), "s"(vr)
+          : "memory");
+    }
+  }
+};
+
+// Workgroup barrier without a memory fence: LDS-DMA completion is awaited
+// explicitly with wait_vmcnt, and a fence would wait for the prefetch as well.
+__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Row intervals in 32 bits (keys < 2^31 here).
+struct RowIv32 {
+  int lo1, hi1, lo2, hi2;
+};
+
+struct WaveState {
+  float m_run, l_run;
+};
+
+template <int D>
+__device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
+                                    bool is_full, const bf16x8* qf, f32x16* oacc,
+                                    WaveState& st, const RowIv32& iv, const uint8_t* mrow,
+                                    const uint16_t* brow, bool qvalid, int lane) {
+  constexpr int NS = V2Ctx<D>::NS;
+  constexpr int NDC = V2Ctx<D>::NDC;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t k0 = (int64_t)kt * kTile;
+  const bool check_k = k0 + kTile > p.Sk;
+  const bool check_mask = !is_full && p.mask_kind != 0;
+  const bool plain = !check_k && !check_mask && brow == nullptr && qvalid;
+  // transposed-read lane roles
+  const int blk = lane >> 4;
+  const int e4 = (lane >> 2) & 3;
+  const int g4 = lane & 3;
+
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    f32x16 sacc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = (2 * half + c) * 32 + perm_row(n);
+      const __bf16* krow = t.k + row * D;
+      const int sw = swz_k(row);
+      sacc[c] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * s + hh) ^ sw) * 8));
+        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[c], 0, 0, 0);
+      }
+    }
+
+    float mloc = -INFINITY;
+    if (plain) {
+      // scores stay unscaled here: the scale is folded into the exponent below
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) mloc = fmaxf(mloc, sacc[c][u]);
+      mloc *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int kc = 2 * half + c;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int64_t kb = k0 + kc * 32 + 16 * sb + 8 * hh;
+          float bv[8];
+          if (brow) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(brow + kb);
+            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+          }
+          uint32_t mbits = 0xFFu;
+          if (check_mask) {
+            if (p.mask_kind == 2) {
+              uint2 mb = make_uint2(0, 0);
+              if (mrow) mb = *reinterpret_cast<const uint2*>(mrow + kb);
+              mbits = 0;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+                mbits |= (byte != 0u ? 1u : 0u) << e;
+              }
+            } else {
+              mbits = 0;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int key = (int)kb + e;
+                const bool keep =
+                    (key >= iv.lo1 && key < iv.hi1) || (key >= iv.lo2 && key < iv.hi2);
+                mbits |= (keep ? 1u : 0u) << e;
+              }
+            }
+          }
+          if (!qvalid) mbits = 0;
+          if (check_k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (kb + e >= p.Sk) mbits &= ~(1u << e);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 8 * sb + e;
+            float sv = sacc[c][u] * p.scale_log2 + bv[e];
+            sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+            sacc[c][u] = sv;
+            mloc = fmaxf(mloc, sv);
+          }
+        }
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(st.m_run, mloc);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
+    // exponent argument: plain tiles hold raw scores (x scale), others scaled ones
+    const float mul = plain ? p.scale_log2 : 1.f;
+    float lsum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[c][u], mul, -m_use));
+        lsum += e;
+        pf[c][u >> 3][u & 7] = (__bf16)e;
+      }
+    }
+    st.l_run = st.l_run * alpha + lsum;
+    st.m_run = m_new;
+    // rescale O only when some row's running max moved
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) oacc[dc] *= alpha;
+    }
+
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int kb = (2 * half + c) * 32 + 16 * sb;
+          const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+          const int row0 = kb + 8 * (blk >> 1) + e4;
+          const int row1 = row0 + 4;
+          const __bf16* a0 = t.v + row0 * D + ((chunk ^ swz_v(row0)) * 8) + (g4 & 1) * 4;
+          const __bf16* a1 = t.v + row1 * D + ((chunk ^ swz_v(row1)) * 8) + (g4 & 1) * 4;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+          const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
+          const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
+          const bf16x8 a = __builtin_shufflevector(lob, hib, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c][sb], oacc[dc], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
+  constexpr int NS = V2Ctx<D>::NS;
+  constexpr int NDC = V2Ctx<D>::NDC;
+  constexpr int LOADS = V2Ctx<D>::LOADS;
+  __shared__ __align__(1024) Tiles<D> buf0;
+  __shared__ __align__(1024) Tiles<D> buf1;
+
+  // work item: contiguous ranges per XCD, heaviest query tile first in a pair
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds;
+  const int per = nWork / kXcds;
+  const int rem = nWork % kXcds;
+  const int wi = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
+  const int pairs = p.G / 2;
+  const int qt = p.nQ - 1 - wi % p.nQ;
+  int grp = wi / p.nQ;
+  const int hp = grp % pairs;
+  grp /= pairs;
+  const int kvh = grp % p.KVH;
+  const int b = grp / p.KVH;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int h = kvh * p.G + 2 * hp + (w >> 2);
+  const int q = qt * kTile + (w & 3) * 32 + n;
+  const bool qvalid = q < p.Sq;
+
+  bf16x8 qf[NS];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
+                         (int64_t)q * p.q_sq + (int64_t)h * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
+  }
+  RowIv32 iv{0, 0, 0, 0};
+  if (p.mask_kind == 1) {
+    const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
+  }
+  const uint8_t* mrow =
+      (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
+  const uint16_t* brow = (p.has_bias && qvalid)
+      ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
+                        (int64_t)kvh * p.k_sh;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
+                        (int64_t)kvh * p.v_sh;
+
+  f32x16 oacc[NDC];
+#pragma unroll
+  for (int i = 0; i < NDC; ++i) oacc[i] = f32x16{};
+  WaveState st{-INFINITY, 0.f};
+
+  Loader<D> ld;
+  ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+
+  TileList tl;
+  tl.init(p, b, kvh * p.G + 2 * hp, qt);  // identical for both heads of the pair
+  const int ntiles = tl.count();
+  bool full_cur = false;
+  int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
+  if (ntiles > 0) ld.issue(buf0, kt_cur, w);
+  for (int it = 0; it < ntiles; ++it) {
+    Tiles<D>& cur = (it & 1) ? buf1 : buf0;
+    Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
+    bool full_nxt = false;
+    int kt_nxt = 0;
+    if (it + 1 < ntiles) {
+      kt_nxt = tl.tile(it + 1, full_nxt);
+      ld.issue(nxt, kt_nxt, w);
+      wait_vmcnt<2 * LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier();
+    compute_tile<D>(cur, p, kt_cur, full_cur, qf, oacc, st, iv, mrow, brow, qvalid, lane);
+    barrier();
+    kt_cur = kt_nxt;
+    full_cur = full_nxt;
+  }
+
+  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+  if (qvalid) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb +
+                   (int64_t)q * p.o_sq + (int64_t)h * p.o_sh;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[dc][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dc * 32 + 8 * g + 4 * hh) = v4;
+      }
+    }
+    if (p.lse && hh == 0) {
+      const float lse =
+          l_tot > 0.f ? (st.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+bool attn_v2_applies(const AttnParams& p, int D) {
+  if (D != 64 && D != 128) return false;
+  // 32-bit buffer offsets within one (b, kv head)
+  if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
+  if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
+  if (p.G % 2) return false;
+  if (p.has_bm && p.bm.h_mode == 1) return false;  // per-head tile lists
+  return true;
+}
+
+hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
+  const int nWork = p.B * p.KVH * (p.G / 2) * p.nQ;
+  if (nWork == 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL(k_attn_bf16_v2<128>, dim3(nWork), dim3(kThreads), 0, s, p, nWork);
+  else
+    hipLaunchKernelGGL(k_attn_bf16_v2<64>, dim3(nWork), dim3(kThreads), 0, s, p, nWork);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

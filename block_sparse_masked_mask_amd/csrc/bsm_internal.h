@@ -97,5 +97,8 @@ hipError_t launch_block_mask_dense(const DenseMaskView& m, int32_t* kv_num,
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
+// pipelined bf16 kernel: two heads of a KV group per workgroup
+bool attn_v2_applies(const AttnParams& p, int D);
+hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
 
 }  // namespace bsm
