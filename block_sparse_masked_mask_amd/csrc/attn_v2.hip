@@ -37,6 +37,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -44,12 +45,21 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 
 __device__ inline int perm_row(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
-__device__ inline int swz_k(int r) { return (r & 3) | ((r >> 1) & 4); }
-__device__ inline int swz_v(int r) { return (r & 3) << 1; }
+// 16-byte chunk swizzles of the K and V tiles (row r). For D = 128 both are
+// conflict-free whether the LDS serves 8 lanes x 16 bytes (32 banks) or
+// 16 lanes x 16 bytes (64 banks) of a ds_read_b128 per cycle, and the same for
+// the 16 / 32 lanes of a transposed 8-byte read; D = 64 rows hold only 8 chunks.
+template <int D>
+__device__ inline int swz_k(int r) {
+  return D == 128 ? perm_row(r & 15) : ((r & 3) | ((r >> 1) & 4));
+}
+template <int D>
+__device__ inline int swz_v(int r) {
+  return D == 128 ? (((r & 3) << 2) | (r & 2)) : ((r & 3) << 1);
+}
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // vmcnt <= n, other counters unconstrained (gfx9 encoding)
@@ -65,10 +75,14 @@ struct Tiles {
   __bf16 v[kTile * D];
 };
 
-template <int D>
+// RB = 32-row query blocks per wave. A workgroup always covers 128 query rows
+// of two heads, so it has 8 / RB waves.
+template <int D, int RB>
 struct V2Ctx {
+  static constexpr int NT = 512 / RB;                      // threads per workgroup
+  static constexpr int NW = NT / 64;                       // waves
   static constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  static constexpr int LOADS = kTile * D * 2 / (kThreads * 16);  // per tensor per thread
+  static constexpr int LOADS = kTile * D * 2 / (NT * 16);  // per tensor per thread
   static constexpr int NS = D / 16;
   static constexpr int NDC = D / 32;
 };
@@ -76,16 +90,17 @@ struct V2Ctx {
 // Byte offsets (within one (b, kv head)) of this thread's LDS-DMA chunks of
 // key tile 0; tile kt adds kt * 128 rows. Rows >= Sk fall outside the buffer
 // resource's range and load as zeros.
-template <int D>
+template <int D, int RB>
 struct Loader {
-  uint32_t koff[V2Ctx<D>::LOADS];
-  uint32_t voff[V2Ctx<D>::LOADS];
+  using C = V2Ctx<D, RB>;
+  uint32_t koff[C::LOADS];
+  uint32_t voff[C::LOADS];
   uint32_t ktile_bytes, vtile_bytes;  // bytes per 128 rows
   __amdgpu_buffer_rsrc_t kr, vr;
 
   __device__ inline void init(const void* kbase, const void* vbase, int64_t k_sk, int64_t v_sk,
                               int Sk, int w, int lane) {
-    constexpr int CPR = V2Ctx<D>::CPR;
+    constexpr int CPR = C::CPR;
     kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), 0,
                                            (int)((int64_t)Sk * k_sk * 2), 0x00020000);
     vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), 0,
@@ -93,12 +108,12 @@ struct Loader {
     ktile_bytes = (uint32_t)(kTile * k_sk * 2);
     vtile_bytes = (uint32_t)(kTile * v_sk * 2);
 #pragma unroll
-    for (int j = 0; j < V2Ctx<D>::LOADS; ++j) {
-      const int f = (j * (kThreads / 64) + w) * 64 + lane;
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int f = (j * C::NW + w) * 64 + lane;
       const int r = f / CPR;
       const int c = f % CPR;
-      koff[j] = (uint32_t)(r * k_sk * 2 + ((c ^ swz_k(r)) * 16));
-      voff[j] = (uint32_t)(r * v_sk * 2 + ((c ^ swz_v(r)) * 16));
+      koff[j] = (uint32_t)(r * k_sk * 2 + ((c ^ swz_k<D>(r)) * 16));
+      voff[j] = (uint32_t)(r * v_sk * 2 + ((c ^ swz_v<D>(r)) * 16));
     }
   }
 
@@ -109,8 +124,8 @@ struct Loader {
   // destination register: data goes to LDS at m0 + 16 * lane.
   __device__ inline void issue(Tiles<D>& t, int kt, int w) const {
 #pragma unroll
-    for (int j = 0; j < V2Ctx<D>::LOADS; ++j) {
-      const int slot = (j * (kThreads / 64) + w) * 64;  // first 16-byte slot of the wave
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int slot = (j * C::NW + w) * 64;  // first 16-byte slot of the wave
       const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
       const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
       const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
@@ -137,175 +152,245 @@ struct RowIv32 {
   int lo1, hi1, lo2, hi2;
 };
 
-struct WaveState {
-  float m_run, l_run;
+// Keep bits of keys kb .. kb+7 that lie in [lo, hi).
+__device__ inline uint32_t range_bits(int lo, int hi, int kb) {
+  int a = lo - kb, c = hi - kb;
+  a = a < 0 ? 0 : (a > 8 ? 8 : a);
+  c = c < 0 ? 0 : (c > 8 ? 8 : c);
+  return ((1u << c) - 1u) & ~((1u << a) - 1u);
+}
+
+// max of x over lanes l and l ^ 32 (the two lanes that share a query row)
+__device__ inline float max_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+#ifdef BSM_MFMA_PRIO
+#define BSM_PRIO(x) __builtin_amdgcn_s_setprio(x)
+#else
+#define BSM_PRIO(x)
+#endif
+
+// A row's running max is raised only when a new score exceeds it by more than
+// this many powers of two; until then probabilities are taken against the
+// stale max and stay below 2^kRescaleLog2 (exact after the final division, which
+// uses the same max for the sum and for O).
+constexpr float kRescaleLog2 = 8.0f;
+
+// Per-row-block state of a wave: its 32 query rows.
+template <int D>
+struct RowBlock {
+  bf16x8 qf[D / 16];       // Q operand: row n, d = 16 s + 8 hh + [0, 8)
+  f32x16 oacc[D / 32];     // O^T accumulators
+  float m_run, l_run;      // running max (log2 units) and sum
+  RowIv32 iv;              // DFlash kept-key intervals of the row
+  const uint8_t* mrow;     // mask row or null
+  const uint16_t* brow;    // bias row or null
+  bool qvalid;
 };
 
-template <int D>
+template <int D, int RB>
 __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
-                                    bool is_full, const bf16x8* qf, f32x16* oacc,
-                                    WaveState& st, const RowIv32& iv, const uint8_t* mrow,
-                                    const uint16_t* brow, bool qvalid, int lane) {
-  constexpr int NS = V2Ctx<D>::NS;
-  constexpr int NDC = V2Ctx<D>::NDC;
+                                    bool is_full, RowBlock<D>* rbk, int lane) {
+  constexpr int NS = D / 16;
+  constexpr int NDC = D / 32;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int64_t k0 = (int64_t)kt * kTile;
+  const int k0 = kt * kTile;
   const bool check_k = k0 + kTile > p.Sk;
   const bool check_mask = !is_full && p.mask_kind != 0;
-  const bool plain = !check_k && !check_mask && brow == nullptr && qvalid;
   // transposed-read lane roles
   const int blk = lane >> 4;
   const int e4 = (lane >> 2) & 3;
   const int g4 = lane & 3;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    f32x16 sacc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    f32x16 sacc[RB][2];
+    BSM_PRIO(1);
+    // K operand i of this half: chunk c = i / NS, k-step s = i % NS
+    auto kop = [&](int i) {
+      const int c = i / NS, s = i % NS;
       const int row = (2 * half + c) * 32 + perm_row(n);
-      const __bf16* krow = t.k + row * D;
-      const int sw = swz_k(row);
-      sacc[c] = f32x16{};
+      return *reinterpret_cast<const bf16x8*>(t.k + row * D +
+                                             (((2 * s + hh) ^ swz_k<D>(row)) * 8));
+    };
+    bf16x8 ka = kop(0);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * s + hh) ^ sw) * 8));
-        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[c], 0, 0, 0);
-      }
+    for (int i = 0; i < 2 * NS; ++i) {
+      const int c = i / NS, s = i % NS;
+      const bf16x8 a = ka;
+      if (i + 1 < 2 * NS) ka = kop(i + 1);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        sacc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, rbk[r].qf[s], s == 0 ? f32x16{} : sacc[r][c], 0, 0, 0);
     }
+    BSM_PRIO(0);
+    // V operand i of this half: d-chunk dc = i / 4, key chunk c = (i / 2) % 2,
+    // 16-key step sb = i % 2; two transposed reads of 4 keys each
+    auto vop = [&](int i) {
+      const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
+      const int kb = (2 * half + c) * 32 + 16 * sb;
+      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+      const int row0 = kb + 8 * (blk >> 1) + e4;
+      const int row1 = row0 + 4;
+      const __bf16* a0 = t.v + row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4;
+      const __bf16* a1 = t.v + row1 * D + ((chunk ^ swz_v<D>(row1)) * 8) + (g4 & 1) * 4;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+      return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                     __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // the first V operands load while the softmax runs
+    bf16x8 va0 = vop(0);
+    bf16x8 va1 = vop(1);
 
-    float mloc = -INFINITY;
-    if (plain) {
-      // scores stay unscaled here: the scale is folded into the exponent below
+    bf16x8 pf[RB][2][2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int r = 0; r < RB; ++r) {
+      RowBlock<D>& R = rbk[r];
+      const bool plain = !check_k && !check_mask && R.brow == nullptr && R.qvalid;
+      float mloc = -INFINITY;
+      if (plain) {
+        // raw scores: the scale is folded into the exponent below
 #pragma unroll
-        for (int u = 0; u < 16; ++u) mloc = fmaxf(mloc, sacc[c][u]);
-      mloc *= p.scale_log2;
-    } else {
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int kc = 2 * half + c;
+          for (int u = 0; u < 16; ++u) mloc = fmaxf(mloc, sacc[r][c][u]);
+        mloc *= p.scale_log2;
+      } else {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int64_t kb = k0 + kc * 32 + 16 * sb + 8 * hh;
-          float bv[8];
-          if (brow) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(brow + kb);
-            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int c = 0; c < 2; ++c) {
+          const int kc = 2 * half + c;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
-          } else {
+          for (int sb = 0; sb < 2; ++sb) {
+            const int kb = k0 + kc * 32 + 16 * sb + 8 * hh;  // 8 consecutive keys
+            float bv[8];
+            if (R.brow) {
+              const uint4 raw = *reinterpret_cast<const uint4*>(R.brow + kb);
+              const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bv[e] = 0.f;
-          }
-          uint32_t mbits = 0xFFu;
-          if (check_mask) {
-            if (p.mask_kind == 2) {
-              uint2 mb = make_uint2(0, 0);
-              if (mrow) mb = *reinterpret_cast<const uint2*>(mrow + kb);
-              mbits = 0;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
-                mbits |= (byte != 0u ? 1u : 0u) << e;
-              }
+              for (int e = 0; e < 8; ++e)
+                bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
             } else {
-              mbits = 0;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int key = (int)kb + e;
-                const bool keep =
-                    (key >= iv.lo1 && key < iv.hi1) || (key >= iv.lo2 && key < iv.hi2);
-                mbits |= (keep ? 1u : 0u) << e;
+              for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+            }
+            uint32_t mbits = 0xFFu;
+            if (check_mask) {
+              if (p.mask_kind == 2) {
+                uint2 mb = make_uint2(0, 0);
+                if (R.mrow) mb = *reinterpret_cast<const uint2*>(R.mrow + kb);
+                mbits = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+                  mbits |= (byte != 0u ? 1u : 0u) << e;
+                }
+              } else {
+                mbits = range_bits(R.iv.lo1, R.iv.hi1, kb) | range_bits(R.iv.lo2, R.iv.hi2, kb);
               }
             }
-          }
-          if (!qvalid) mbits = 0;
-          if (check_k) {
+            if (!R.qvalid) mbits = 0;
+            if (check_k) mbits &= range_bits(0, p.Sk, kb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (kb + e >= p.Sk) mbits &= ~(1u << e);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int u = 8 * sb + e;
-            float sv = sacc[c][u] * p.scale_log2 + bv[e];
-            sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
-            sacc[c][u] = sv;
-            mloc = fmaxf(mloc, sv);
+            for (int e = 0; e < 8; ++e) {
+              const int u = 8 * sb + e;
+              float sv = sacc[r][c][u] * p.scale_log2 + bv[e];
+              sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+              sacc[r][c][u] = sv;
+              mloc = fmaxf(mloc, sv);
+            }
           }
         }
       }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(st.m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
-    // exponent argument: plain tiles hold raw scores (x scale), others scaled ones
-    const float mul = plain ? p.scale_log2 : 1.f;
-    float lsum = 0.f;
-    bf16x8 pf[2][2];
+      mloc = max_pair(mloc);
+      // conditional rescale (see kRescaleLog2)
+      const bool grow = mloc > R.m_run + kRescaleLog2;
+      if (__ballot(grow)) {
+        const float m_new = grow ? mloc : R.m_run;
+        // 1 where the max is kept (also for rows still at -inf: -inf - -inf is NaN)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(R.m_run - m_new) : 1.f;
+        R.l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[c][u], mul, -m_use));
-        lsum += e;
-        pf[c][u >> 3][u & 7] = (__bf16)e;
+        for (int dc = 0; dc < NDC; ++dc) R.oacc[dc] *= alpha;
+        R.m_run = m_new;
       }
-    }
-    st.l_run = st.l_run * alpha + lsum;
-    st.m_run = m_new;
-    // rescale O only when some row's running max moved
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) oacc[dc] *= alpha;
-    }
-
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
+      const float m_use = R.m_run == -INFINITY ? 0.f : R.m_run;
+      const float mul = plain ? p.scale_log2 : 1.f;
+      float lsum = R.l_run;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const int kb = (2 * half + c) * 32 + 16 * sb;
-          const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
-          const int row0 = kb + 8 * (blk >> 1) + e4;
-          const int row1 = row0 + 4;
-          const __bf16* a0 = t.v + row0 * D + ((chunk ^ swz_v(row0)) * 8) + (g4 & 1) * 4;
-          const __bf16* a1 = t.v + row1 * D + ((chunk ^ swz_v(row1)) * 8) + (g4 & 1) * 4;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
-          const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
-          const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
-          const bf16x8 a = __builtin_shufflevector(lob, hib, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c][sb], oacc[dc], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int u = 8 * sb + e;
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(sacc[r][c][u], mul, -m_use));
+            const float x1 = __builtin_amdgcn_exp2f(fmaf(sacc[r][c][u + 1], mul, -m_use));
+            const bf16x2 pr = {(__bf16)x0, (__bf16)x1};
+            pf[r][c][sb][e] = pr[0];
+            pf[r][c][sb][e + 1] = pr[1];
+            // row sum of the bf16 probabilities the PV product uses
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          }
         }
       }
+      R.l_run = lsum;
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    BSM_PRIO(1);
+#pragma unroll
+    for (int i = 0; i < 4 * NDC; ++i) {
+      const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
+      const bf16x8 a = va0;
+      va0 = va1;
+      if (i + 2 < 4 * NDC) va1 = vop(i + 2);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        rbk[r].oacc[dc] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r][c][sb], rbk[r].oacc[dc], 0, 0, 0);
+    }
+    BSM_PRIO(0);
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
-  constexpr int NS = V2Ctx<D>::NS;
-  constexpr int NDC = V2Ctx<D>::NDC;
-  constexpr int LOADS = V2Ctx<D>::LOADS;
+template <int D, int RB>
+__global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
+  using C = V2Ctx<D, RB>;
+  constexpr int NS = C::NS;
+  constexpr int NDC = C::NDC;
+  constexpr int WPH = C::NW / 2;  // waves per head
   __shared__ __align__(1024) Tiles<D> buf0;
   __shared__ __align__(1024) Tiles<D> buf1;
 
-  // work item: contiguous ranges per XCD, heaviest query tile first in a pair
+  // Work items: (head-pair group, query tile). Workgroup L runs on XCD L % 8.
+  // When the groups split evenly over the XCDs, XCD x takes groups
+  // [x * gx, (x + 1) * gx) and walks them query tile first, heaviest tile first
+  // (longest-processing-time order, since a query tile's cost grows with its
+  // index under these masks); otherwise each XCD takes a contiguous range.
   const int L = blockIdx.x;
   const int xcd = L % kXcds;
-  const int per = nWork / kXcds;
-  const int rem = nWork % kXcds;
-  const int wi = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
   const int pairs = p.G / 2;
-  const int qt = p.nQ - 1 - wi % p.nQ;
-  int grp = wi / p.nQ;
+  const int ngrp = nWork / p.nQ;
+  int qt, grp;
+  if (ngrp % kXcds == 0) {
+    const int gx = ngrp / kXcds;
+    const int li = L / kXcds;
+    qt = p.nQ - 1 - li / gx;
+    grp = xcd * gx + li % gx;
+  } else {
+    const int per = nWork / kXcds;
+    const int rem = nWork % kXcds;
+    const int wi = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
+    qt = p.nQ - 1 - wi % p.nQ;
+    grp = wi / p.nQ;
+  }
   const int hp = grp % pairs;
   grp /= pairs;
   const int kvh = grp % p.KVH;
@@ -316,38 +401,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_bf16_v2(AttnParams p, int 
   const int w = tid >> 6;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int h = kvh * p.G + 2 * hp + (w >> 2);
-  const int q = qt * kTile + (w & 3) * 32 + n;
-  const bool qvalid = q < p.Sq;
+  const int h = kvh * p.G + 2 * hp + w / WPH;
 
-  bf16x8 qf[NS];
-  {
+  RowBlock<D> rbk[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    RowBlock<D>& R = rbk[r];
+    const int q = qt * kTile + ((w % WPH) * RB + r) * 32 + n;
+    R.qvalid = q < p.Sq;
     const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
                          (int64_t)q * p.q_sq + (int64_t)h * p.q_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
+      R.qf[s] = R.qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
+    R.iv = RowIv32{0, 0, 0, 0};
+    if (p.mask_kind == 1) {
+      const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+      R.iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
+    }
+    R.mrow = (p.mask_kind == 2 && R.qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
+    R.brow = (p.has_bias && R.qvalid)
+        ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
+#pragma unroll
+    for (int i = 0; i < NDC; ++i) R.oacc[i] = f32x16{};
+    R.m_run = -INFINITY;
+    R.l_run = 0.f;
   }
-  RowIv32 iv{0, 0, 0, 0};
-  if (p.mask_kind == 1) {
-    const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
-    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
-  }
-  const uint8_t* mrow =
-      (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
-  const uint16_t* brow = (p.has_bias && qvalid)
-      ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
                         (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         (int64_t)kvh * p.v_sh;
-
-  f32x16 oacc[NDC];
-#pragma unroll
-  for (int i = 0; i < NDC; ++i) oacc[i] = f32x16{};
-  WaveState st{-INFINITY, 0.f};
-
-  Loader<D> ld;
+  Loader<D, RB> ld;
   ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
 
   TileList tl;
@@ -356,44 +440,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_bf16_v2(AttnParams p, int 
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
   if (ntiles > 0) ld.issue(buf0, kt_cur, w);
+  // One barrier per tile: it publishes tile i (every wave has awaited its own
+  // loads of it) and frees the other buffer (every wave has finished tile
+  // i - 1), so the loads of tile i + 1 go out right after it and overlap the
+  // whole of tile i's compute.
   for (int it = 0; it < ntiles; ++it) {
     Tiles<D>& cur = (it & 1) ? buf1 : buf0;
     Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
     bool full_nxt = false;
-    int kt_nxt = 0;
-    if (it + 1 < ntiles) {
-      kt_nxt = tl.tile(it + 1, full_nxt);
-      ld.issue(nxt, kt_nxt, w);
-      wait_vmcnt<2 * LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
+    wait_vmcnt<0>();
     barrier();
-    compute_tile<D>(cur, p, kt_cur, full_cur, qf, oacc, st, iv, mrow, brow, qvalid, lane);
-    barrier();
+    if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
+    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, lane);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   }
 
-  const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
-  if (qvalid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb +
-                   (int64_t)q * p.o_sq + (int64_t)h * p.o_sh;
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
+  for (int r = 0; r < RB; ++r) {
+    RowBlock<D>& R = rbk[r];
+    const int q = qt * kTile + ((w % WPH) * RB + r) * 32 + n;
+    const float l_tot = R.l_run + __shfl_xor(R.l_run, 32, 64);
+    if (R.qvalid) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb +
+                     (int64_t)q * p.o_sq + (int64_t)h * p.o_sh;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
+      for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(oacc[dc][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dc * 32 + 8 * g + 4 * hh) = v4;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(R.oacc[dc][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + dc * 32 + 8 * g + 4 * hh) = v4;
+        }
       }
-    }
-    if (p.lse && hh == 0) {
-      const float lse =
-          l_tot > 0.f ? (st.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+      if (p.lse && hh == 0) {
+        const float lse =
+            l_tot > 0.f ? (R.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+      }
     }
   }
 }
@@ -413,10 +500,16 @@ bool attn_v2_applies(const AttnParams& p, int D) {
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
   const int nWork = p.B * p.KVH * (p.G / 2) * p.nQ;
   if (nWork == 0) return hipSuccess;
+#ifndef BSM_V2_RB
+#define BSM_V2_RB 1
+#endif
+  constexpr int RB = BSM_V2_RB;
   if (D == 128)
-    hipLaunchKernelGGL(k_attn_bf16_v2<128>, dim3(nWork), dim3(kThreads), 0, s, p, nWork);
+    hipLaunchKernelGGL((k_attn_bf16_v2<128, RB>), dim3(nWork), dim3(V2Ctx<128, RB>::NT), 0, s,
+                       p, nWork);
   else
-    hipLaunchKernelGGL(k_attn_bf16_v2<64>, dim3(nWork), dim3(kThreads), 0, s, p, nWork);
+    hipLaunchKernelGGL((k_attn_bf16_v2<64, RB>), dim3(nWork), dim3(V2Ctx<64, RB>::NT), 0, s,
+                       p, nWork);
   return hipGetLastError();
 }
 
