@@ -109,22 +109,97 @@ def measure_mask_build(reps=5):
     for a, b in zip(bm, ref):
         if not torch.equal(a, b):
             raise RuntimeError("dense and predicate block masks differ")
-    stream = torch.cuda.current_stream()
-    times = []
-    for _ in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        bsm.build_block_mask(geom, mask=dense)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
     nbytes = dense.numel() + 4 * sum(t.numel() for t in bm)
-    ms = float(np.mean(times))
+    ms = _time_ms(lambda: bsm.build_block_mask(geom, mask=dense), reps=reps)
     del dense
     return {"workload": "long_dflash_dense_mask", "shape": [1, 1, d.Sq, 65536],
             "bytes": int(nbytes), "ms": ms, "GB/s": nbytes / ms / 1e6,
             "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def _time_ms(fn, reps=10):
+    """Average ms of fn() over reps back-to-back launches (HIP events on the stream)."""
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_components():
+    """Per-kernel times of the other workloads (parity cases, not the headline)."""
+    out = {}
+    # DFlash block masks from the predicate (integer work, output only)
+    for name in ("dflash_train_bf16", "long_dflash_bf16"):
+        cfg = synth.CONFIGS[name]
+        for lay in cfg["layers"]:
+            d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
+                           is_causal=lay["is_causal"], layer_type=lay["layer_type"],
+                           sliding_window=lay["window"])
+            geom = bsm.Geometry(cfg["B"], cfg["H"], cfg["KVH"], d.Sq, d.Sk, cfg["D"])
+            out[f"block_mask_pred/{name}/{lay['name']}_us"] = \
+                1e3 * _time_ms(lambda: bsm.build_block_mask(geom, pred=d))
+    # long-context attention
+    cfg = synth.CONFIGS["long_dflash_bf16"]
+    lay = cfg["layers"][0]
+    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"], is_causal=lay["is_causal"],
+                   layer_type=lay["layer_type"], sliding_window=lay["window"])
+    q, k, v = [t.cuda() for t in synth.qkv(cfg["B"], d.Sq, d.Sk, cfg["H"], cfg["KVH"], cfg["D"],
+                                           "bf16", seed=0)]
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, pred=d)
+    fl = counted_flops(bm, geom)
+    o = torch.empty_like(q)
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, out=o), reps=3)
+    out["attn/long_dflash_bf16_ms"] = ms
+    out["attn/long_dflash_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+    del q, k, v, o
+    # dynamic top-k attention: top-k, dense builder, attention
+    cfg = synth.CONFIGS["dynamic_topk_bf16"]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = [t.cuda() for t in synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0)]
+    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    fl = counted_flops(bm, geom)
+    o = torch.empty_like(q)
+    out["topk/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"], ))
+    out["block_mask_dense/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.build_block_mask(geom, mask=mask))
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o), reps=5)
+    out["attn/dynamic_topk_bf16_ms"] = ms
+    out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+    del q, k, v, o
+    # decode with the head-group swap: top-k, dense builder, attention (HBM-bound)
+    cfg = synth.CONFIGS["decode_swap_bf16"]
+    B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
+    q, k, v = [t.cuda() for t in synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0)]
+    bias, _ = synth.topk_inputs(cfg, seed=0)
+    bias = bias.cuda()
+    mask = torch.empty(bias.shape, dtype=torch.bool, device="cuda")
+    tk = 1e3 * _time_ms(lambda: bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"], out=mask))
+    out["topk/decode_swap_bf16_us"] = tk
+    out["topk/decode_swap_bf16_GB/s"] = (bias.numel() * 2 + mask.numel()) / (tk * 1e-6) / 1e9
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    bd = 1e3 * _time_ms(lambda: bsm.build_block_mask(geom, mask=mask))
+    out["block_mask_dense/decode_swap_bf16_us"] = bd
+    o = torch.empty_like(q)
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o), reps=5)
+    kv_bytes = 2 * k.numel() * 2 + bias.numel() * 2 + mask.numel() + 2 * q.numel() * 2
+    out["attn/decode_swap_bf16_ms"] = ms
+    out["attn/decode_swap_bf16_GB/s"] = kv_bytes / (ms * 1e-3) / 1e9
+    return out
 
 
 def cpu_baseline(step, budget_s=20.0):
@@ -170,6 +245,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mask-build", action="store_true")
+    ap.add_argument("--components", action="store_true",
+                    help="also time the other workloads' kernels (top-k, builders, attention)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
@@ -223,6 +300,8 @@ def main():
     }
     if not args.no_mask_build:
         line["mask_build"] = measure_mask_build()
+    if args.components:
+        line["components"] = measure_components()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(line), flush=True)

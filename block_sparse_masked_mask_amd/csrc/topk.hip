@@ -246,11 +246,213 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
 
 constexpr size_t kCacheMax = 64 * 1024;
 
+// Register-resident variant for rows of up to NSEG * 256 * (16 / sizeof(KeyT))
+// keys: each thread keeps its keys in registers through all passes. Segment s
+// of a row is the 4 KiB (bf16) / 4 KiB (f32) block [s * SEG, (s + 1) * SEG);
+// thread t owns the 16 contiguous bytes at t * EPL of every segment, so each
+// load and each store of a segment is one coalesced wave-wide access. The
+// index-order prefix count of keys equal to the threshold is one workgroup
+// scan of NSEG counters per thread (segment-major, then thread order).
+template <typename KeyT, int NSEG>
+__global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
+  using Tr = KeyTraits<KeyT>;
+  constexpr int EPL = 16 / sizeof(KeyT);  // keys per 16-byte load
+  constexpr int SEG = kThreads * EPL;
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_sel[2];
+  __shared__ int s_wsum[NSEG][kWaves];
+
+  const int64_t row = blockIdx.x;
+  const int64_t qb = row % p.Qb;
+  const int64_t hb = (row / p.Qb) % p.Hb;
+  const int64_t bb = row / (p.Qb * p.Hb);
+  const KeyT* brow = reinterpret_cast<const KeyT*>(p.bias) + bb * p.b_sb + hb * p.b_sh + qb * p.b_sq;
+  const uint8_t* prow = p.pm ? p.pm + bb * p.p_sb + hb * p.p_sh + qb * p.p_sq : nullptr;
+  uint8_t* orow = p.out + row * p.K;
+  const int K = (int)p.K;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const KeyT sent = Tr::sentinel();
+
+  auto valid = [&](int k) -> bool {
+    return k < p.Sk && (prow == nullptr || (k < p.pK && prow[k] != 0));
+  };
+
+  uint4 raw[NSEG];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const int k0 = s * SEG + t * EPL;
+    raw[s] = k0 < K ? *reinterpret_cast<const uint4*>(brow + k0) : make_uint4(0, 0, 0, 0);
+  }
+  KeyT kk[NSEG][EPL];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const int k0 = s * SEG + t * EPL;
+    const KeyT* e = reinterpret_cast<const KeyT*>(&raw[s]);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) kk[s][i] = valid(k0 + i) ? Tr::key(e[i]) : sent;
+  }
+
+  const int keff = p.k < K ? (int)p.k : K;
+  uint32_t prefix = 0;
+  uint32_t rem = (uint32_t)keff;
+  if (keff > 0 && keff < K) {
+    for (int shift = Tr::kBits - 8; shift >= 0; shift -= 8) {
+      for (int i = t; i < 256; i += kThreads) s_hist[i] = 0;
+      __syncthreads();
+      const int hs = shift + 8;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        if (s * SEG + t * EPL < K) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const uint32_t key = (uint32_t)kk[s][i];
+            const bool match = hs >= Tr::kBits || ((key ^ prefix) >> hs) == 0;
+            if (match) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      if (t < 64) {
+        uint32_t c[4];
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = s_hist[255 - 4 * t - j];
+          sum += c[j];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o, 64);
+          if (t >= o) incl += y;
+        }
+        const uint32_t excl = incl - sum;
+        if (excl < rem && rem <= incl) {
+          uint32_t above = excl;
+          int d = 255 - 4 * t;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (above + c[j] >= rem) {
+              d = 255 - 4 * t - j;
+              break;
+            }
+            above += c[j];
+          }
+          s_sel[0] = (uint32_t)d;
+          s_sel[1] = above;
+        }
+      }
+      __syncthreads();
+      prefix |= s_sel[0] << shift;
+      rem -= s_sel[1];
+      __syncthreads();
+    }
+  }
+  const uint32_t T = prefix;
+  const int need = (int)rem;  // keys equal to T to take, lowest index first
+
+  // prefix counts of keys == T in index order (segment-major, then thread)
+  int excl[NSEG];
+  if (keff > 0 && keff < K) {
+    int incl[NSEG];
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      int c = 0;
+      if (s * SEG + t * EPL < K) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) c += (uint32_t)kk[s][i] == T;
+      }
+      excl[s] = c;
+      int x = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      incl[s] = x;
+      if (lane == 63) s_wsum[s][w] = x;
+    }
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      int off = base;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const int v = s_wsum[s][i];
+        off += i < w ? v : 0;
+        base += v;
+      }
+      excl[s] = off + incl[s] - excl[s];
+    }
+  }
+
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const int k0 = s * SEG + t * EPL;
+    if (k0 >= K) continue;
+    uint32_t bits = 0;  // one bit per key
+    int r = excl[s];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      bool sel;
+      if (keff == 0) {
+        sel = false;
+      } else if (keff >= K) {
+        sel = true;
+      } else {
+        const uint32_t key = (uint32_t)kk[s][i];
+        sel = key > T;
+        if (key == T) {
+          sel = r < need;
+          ++r;
+        }
+      }
+      bits |= (uint32_t)(sel && valid(k0 + i)) << i;
+    }
+    if (EPL == 8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= ((bits >> i) & 1u) << (8 * i);
+        hi |= ((bits >> (i + 4)) & 1u) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(orow + k0) = make_uint2(lo, hi);
+    } else {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v |= ((bits >> i) & 1u) << (8 * i);
+      *reinterpret_cast<uint32_t*>(orow + k0) = v;
+    }
+  }
+}
+
+template <typename KeyT>
+bool launch_reg(const TopkParams& p, unsigned rows, hipStream_t s) {
+  constexpr int SEG = kThreads * (16 / sizeof(KeyT));
+  const int nseg = (int)((p.K + SEG - 1) / SEG);
+  const dim3 grid(rows), block(kThreads);
+  switch (nseg) {
+    case 1: hipLaunchKernelGGL((k_topk_reg<KeyT, 1>), grid, block, 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((k_topk_reg<KeyT, 2>), grid, block, 0, s, p); return true;
+    case 3:
+    case 4: hipLaunchKernelGGL((k_topk_reg<KeyT, 4>), grid, block, 0, s, p); return true;
+    case 5: case 6: case 7:
+    case 8: hipLaunchKernelGGL((k_topk_reg<KeyT, 8>), grid, block, 0, s, p); return true;
+    default: return false;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   const int64_t rows = p.Bb * p.Hb * p.Qb;
   if (rows == 0 || p.K == 0) return hipSuccess;
+  if (p.is_bf16 ? launch_reg<uint16_t>(p, (unsigned)rows, s)
+                : launch_reg<uint32_t>(p, (unsigned)rows, s))
+    return hipGetLastError();
   const size_t ksz = p.is_bf16 ? 2 : 4;
   const size_t bytes = (size_t)p.K * ksz;
   const bool cache = bytes <= kCacheMax;
