@@ -1,0 +1,292 @@
+// Masked attention forward, bf16, for short query blocks: at most 32 query rows
+// per (b, h) -- the seqlen_q == 1 head-group swap gives G rows per KV head
+// (flash-sparse-attention PR #190, Design: swapped path), and short prefill
+// chunks.
+//
+// Such a launch streams K and V once and does little arithmetic on them, so
+// the work is split along the keys inside the workgroup instead of along the
+// queries: 4 waves share each 128-key K/V tile (LDS-DMA double buffering as in
+// attn_v2.hip), wave w takes keys 32w .. 32w+31 of every tile for all the rows,
+// keeps its own online-softmax state, and the four partial (max, sum, O) states
+// are merged through LDS at the end. The mask bytes and bias values a wave needs
+// for the next tile are loaded into registers together with that tile's DMA,
+// so the wait for one covers the other.
+#include <math.h>
+
+#include "attn_common.h"
+#include "attn_pipe.h"
+#include "bsm_internal.h"
+#include "dflash_rows.h"
+
+namespace bsm {
+namespace {
+
+using namespace pipe;
+
+constexpr int kDecWaves = 4;
+constexpr int kDecRB = 512 / (64 * kDecWaves);  // Loader layout for 256 threads
+
+// Mask / bias words of one lane for one tile: keys kb .. kb+7 for sb = 0, 1
+// with kb = k0 + 32 w + 16 sb + 8 hh.
+struct AuxRegs {
+  uint4 bias[2];
+  uint2 mask[2];
+};
+
+__device__ inline void load_aux(const AttnParams& p, int kt, int w, int hh, const uint8_t* mrow,
+                                const uint16_t* brow, AuxRegs& a) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int kb = kt * kTile + 32 * w + 16 * sb + 8 * hh;
+    a.bias[sb] = brow ? *reinterpret_cast<const uint4*>(brow + kb) : make_uint4(0, 0, 0, 0);
+    a.mask[sb] = mrow ? *reinterpret_cast<const uint2*>(mrow + kb) : make_uint2(0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p) {
+  constexpr int NS = D / 16;
+  constexpr int NDC = D / 32;
+  __shared__ __align__(1024) Tiles<D> buf0;
+  __shared__ __align__(1024) Tiles<D> buf1;
+
+  const int h = blockIdx.x % p.H;
+  const int b = blockIdx.x / p.H;
+  const int kvh = h / p.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int q = n;
+  const bool qvalid = q < p.Sq;
+
+  bf16x8 qf[NS];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
+                         (int64_t)q * p.q_sq + (int64_t)h * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
+  }
+  RowIv32 iv{0, 0, 0, 0};
+  if (p.mask_kind == 1) {
+    const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
+  }
+  const uint8_t* mrow =
+      (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
+  const uint16_t* brow = (p.has_bias && qvalid)
+      ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
+                        (int64_t)kvh * p.k_sh;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
+                        (int64_t)kvh * p.v_sh;
+  Loader<D, kDecRB> ld;
+  ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+
+  f32x16 oacc[NDC];
+#pragma unroll
+  for (int i = 0; i < NDC; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  // transposed-read lane roles
+  const int blk = lane >> 4;
+  const int e4 = (lane >> 2) & 3;
+  const int g4 = lane & 3;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  TileList tl;
+  tl.init(p, b, h, 0);
+  const int ntiles = tl.count();
+  bool full_cur = false;
+  int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
+  AuxRegs aux_cur, aux_nxt;
+  if (ntiles > 0) {
+    ld.issue(buf0, kt_cur, w);
+    load_aux(p, kt_cur, w, hh, mrow, brow, aux_cur);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const Tiles<D>& t = (it & 1) ? buf1 : buf0;
+    Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
+    bool full_nxt = false;
+    const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
+    wait_vmcnt<0>();
+    barrier();
+    if (it + 1 < ntiles) {
+      ld.issue(nxt, kt_nxt, w);
+      load_aux(p, kt_nxt, w, hh, mrow, brow, aux_nxt);
+    }
+
+    // S^T for this wave's 32 keys
+    const int k0 = kt_cur * kTile;
+    const int row = w * 32 + perm_row(n);
+    f32x16 sc{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(t.k + row * D +
+                                                        (((2 * s + hh) ^ swz_k<D>(row)) * 8));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc, 0, 0, 0);
+    }
+    // scale, bias, mask
+    const bool check_k = k0 + kTile > p.Sk;
+    const bool check_mask = !full_cur && p.mask_kind != 0;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb = k0 + 32 * w + 16 * sb + 8 * hh;
+      uint32_t mbits = 0xFFu;
+      if (check_mask) {
+        if (p.mask_kind == 2) {
+          const uint2 mb = aux_cur.mask[sb];
+          mbits = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+            mbits |= (byte != 0u ? 1u : 0u) << e;
+          }
+        } else {
+          mbits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
+        }
+      }
+      if (!qvalid) mbits = 0;
+      if (check_k) mbits &= range_bits(0, p.Sk, kb);
+      const uint32_t wv[4] = {aux_cur.bias[sb].x, aux_cur.bias[sb].y, aux_cur.bias[sb].z,
+                              aux_cur.bias[sb].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int u = 8 * sb + e;
+        const float bv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+        float sv = fmaf(sc[u], p.scale_log2, bv);
+        sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+        sc[u] = sv;
+        mloc = fmaxf(mloc, sv);
+      }
+    }
+    mloc = max_pair(mloc);
+    const bool grow = mloc > m_run + kRescaleLog2;
+    const float m_new = grow ? mloc : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) oacc[dc] *= alpha;
+    }
+    m_run = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float lsum = l_run * alpha;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = __builtin_amdgcn_exp2f(sc[8 * sb + e] - m_use);
+        const float x1 = __builtin_amdgcn_exp2f(sc[8 * sb + e + 1] - m_use);
+        const bf16x2 pr = {(__bf16)x0, (__bf16)x1};
+        pf[sb][e] = pr[0];
+        pf[sb][e + 1] = pr[1];
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      }
+    }
+    l_run = lsum;
+    // O^T += V^T P^T over this wave's 32 keys
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kb = w * 32 + 16 * sb;
+        const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+        const int row0 = kb + 8 * (blk >> 1) + e4;
+        const int row1 = row0 + 4;
+        const __bf16* a0 = t.v + row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4;
+        const __bf16* a1 = t.v + row1 * D + ((chunk ^ swz_v<D>(row1)) * 8) + (g4 & 1) * 4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                 __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
+                                                 5, 6, 7);
+        oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[sb], oacc[dc], 0, 0, 0);
+      }
+    }
+    aux_cur = aux_nxt;
+    kt_cur = kt_nxt;
+    full_cur = full_nxt;
+  }
+
+  // merge the four waves' partial states through LDS (tiles are free now)
+  barrier();
+  float* sO = reinterpret_cast<float*>(&buf0);           // [wave][row][D]
+  float* sM = reinterpret_cast<float*>(&buf1);           // [wave][row]
+  float* sL = sM + kDecWaves * 32;                       // [wave][row]
+  const float l_pair = l_run + __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(&sO[(w * 32 + n) * D + dc * 32 + 8 * g + 4 * hh]) =
+          make_float4(oacc[dc][4 * g], oacc[dc][4 * g + 1], oacc[dc][4 * g + 2],
+                      oacc[dc][4 * g + 3]);
+  if (hh == 0) {
+    sM[w * 32 + n] = m_run;
+    sL[w * 32 + n] = l_pair;
+  }
+  __syncthreads();
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kDecWaves; ++i) mstar = fmaxf(mstar, sM[i * 32 + n]);
+  float f[kDecWaves];
+  float lstar = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDecWaves; ++i) {
+    const float mi = sM[i * 32 + n];
+    f[i] = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mstar);
+    lstar += f[i] * sL[i * 32 + n];
+  }
+  if (qvalid) {
+    const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
+    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb + (int64_t)q * p.o_sq +
+                   (int64_t)h * p.o_sh;
+    for (int dc = w; dc < NDC; dc += kDecWaves) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dc * 32 + 8 * g + 4 * hh;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < kDecWaves; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(&sO[(i * 32 + n) * D + d0]);
+          acc.x += f[i] * v.x;
+          acc.y += f[i] * v.y;
+          acc.z += f[i] * v.z;
+          acc.w += f[i] * v.w;
+        }
+        bf16x4 o4 = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv),
+                     (__bf16)(acc.w * inv)};
+        *reinterpret_cast<bf16x4*>(orow + d0) = o4;
+      }
+    }
+    if (p.lse && w == 0 && hh == 0) {
+      const float lse = lstar > 0.f ? (mstar + __builtin_amdgcn_logf(lstar)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+bool attn_decode_applies(const AttnParams& p, int D) {
+  if (D != 64 && D != 128) return false;
+  if (p.Sq > 32) return false;
+  if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
+  if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
+  return true;
+}
+
+hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s) {
+  const int nwg = p.B * p.H;
+  if (nwg == 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL(k_attn_decode<128>, dim3(nwg), dim3(64 * kDecWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_attn_decode<64>, dim3(nwg), dim3(64 * kDecWaves), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

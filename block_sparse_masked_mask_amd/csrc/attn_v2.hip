@@ -15,169 +15,30 @@
 //    buffered: the loads of tile i+1 are in flight while tile i is computed.
 //  * Both tiles stay row-major ([key][d]). Rows are XOR-swizzled in 16-byte
 //    chunks (the swizzle is applied to the global addresses, since an LDS-DMA
-//    instruction writes 64 consecutive 16-byte slots): K with
-//    (r & 3) | ((r >> 1) & 4), which spreads the 8 rows one 16-byte read group
-//    touches over 8 distinct bank groups; V with 2 (r & 3), which spreads the
-//    4 rows of one transposed read.
+//    instruction writes 64 consecutive 16-byte slots), chosen so that the rows
+//    one LDS read cycle touches land in distinct banks (attn_pipe.h).
 //  * V^T operands come from ds_read_b64_tr_b16: in each 16-lane group, lane
 //    4e + g points at 4 d-values of key row e; the hardware hands lane 4g + s
 //    the 4 keys of d-value s. Two such reads give a lane the 8 consecutive keys
 //    of one d column that the MFMA A operand needs, with no transpose pass.
 //  * Work items (b, KV group pair, query tile) are laid out so that each XCD
-//    gets a contiguous range (so the query tiles of one (b, kvh) share an L2)
-//    and, inside a head pair, the heaviest query tiles first.
+//    keeps the query tiles of the same (b, kvh) (one L2 per XCD) and runs the
+//    heaviest query tiles first.
+//  * The running max of a row is raised only when it grows by more than 2^8
+//    (otherwise O is not rescaled), row sums come from dot2 on the bf16
+//    probabilities the PV product uses, and tiles that need no mask test, no
+//    bias and have all rows valid take a leaner softmax.
 #include <math.h>
 
 #include "attn_common.h"
+#include "attn_pipe.h"
 #include "bsm_internal.h"
 #include "dflash_rows.h"
 
 namespace bsm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kXcds = 8;
-
-__device__ inline int perm_row(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
-// 16-byte chunk swizzles of the K and V tiles (row r). For D = 128 both are
-// conflict-free whether the LDS serves 8 lanes x 16 bytes (32 banks) or
-// 16 lanes x 16 bytes (64 banks) of a ds_read_b128 per cycle, and the same for
-// the 16 / 32 lanes of a transposed 8-byte read; D = 64 rows hold only 8 chunks.
-template <int D>
-__device__ inline int swz_k(int r) {
-  return D == 128 ? perm_row(r & 15) : ((r & 3) | ((r >> 1) & 4));
-}
-template <int D>
-__device__ inline int swz_v(int r) {
-  return D == 128 ? (((r & 3) << 2) | (r & 2)) : ((r & 3) << 1);
-}
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// vmcnt <= n, other counters unconstrained (gfx9 encoding)
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N < 64, "vmcnt field is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int D>
-struct Tiles {
-  __bf16 k[kTile * D];
-  __bf16 v[kTile * D];
-};
-
-// RB = 32-row query blocks per wave. A workgroup always covers 128 query rows
-// of two heads, so it has 8 / RB waves.
-template <int D, int RB>
-struct V2Ctx {
-  static constexpr int NT = 512 / RB;                      // threads per workgroup
-  static constexpr int NW = NT / 64;                       // waves
-  static constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  static constexpr int LOADS = kTile * D * 2 / (NT * 16);  // per tensor per thread
-  static constexpr int NS = D / 16;
-  static constexpr int NDC = D / 32;
-};
-
-// Byte offsets (within one (b, kv head)) of this thread's LDS-DMA chunks of
-// key tile 0; tile kt adds kt * 128 rows. Rows >= Sk fall outside the buffer
-// resource's range and load as zeros.
-template <int D, int RB>
-struct Loader {
-  using C = V2Ctx<D, RB>;
-  uint32_t koff[C::LOADS];
-  uint32_t voff[C::LOADS];
-  uint32_t ktile_bytes, vtile_bytes;  // bytes per 128 rows
-  __amdgpu_buffer_rsrc_t kr, vr;
-
-  __device__ inline void init(const void* kbase, const void* vbase, int64_t k_sk, int64_t v_sk,
-                              int Sk, int w, int lane) {
-    constexpr int CPR = C::CPR;
-    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), 0,
-                                           (int)((int64_t)Sk * k_sk * 2), 0x00020000);
-    vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), 0,
-                                           (int)((int64_t)Sk * v_sk * 2), 0x00020000);
-    ktile_bytes = (uint32_t)(kTile * k_sk * 2);
-    vtile_bytes = (uint32_t)(kTile * v_sk * 2);
-#pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-      const int f = (j * C::NW + w) * 64 + lane;
-      const int r = f / CPR;
-      const int c = f % CPR;
-      koff[j] = (uint32_t)(r * k_sk * 2 + ((c ^ swz_k<D>(r)) * 16));
-      voff[j] = (uint32_t)(r * v_sk * 2 + ((c ^ swz_v<D>(r)) * 16));
-    }
-  }
-
-  // The loads are written as inline asm so that the compiler does not treat
-  // them as LDS stores it must wait for before every LDS read (it cannot tell
-  // the two buffers apart); completion is awaited explicitly with wait_vmcnt
-  // before the barrier that publishes a buffer. The instruction has no
-  // destination register: data goes to LDS at m0 + 16 * lane.
-  __device__ inline void issue(Tiles<D>& t, int kt, int w) const {
-#pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-      const int slot = (j * C::NW + w) * 64;  // first 16-byte slot of the wave
-      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
-      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
-      const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
-      const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-          "s_mov_b32 m0, %3\n\t"
-          "buffer_load_dwordx4 %4, %5, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(lk)), "v"(ok), "s"(kr),
-            "s"(__builtin_amdgcn_readfirstlane(lv)), "v"(ov), "s"(vr)
-          : "memory");
-    }
-  }
-};
-
-// Workgroup barrier without a memory fence: LDS-DMA completion is awaited
-// explicitly with wait_vmcnt, and a fence would wait for the prefetch as well.
-__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Row intervals in 32 bits (keys < 2^31 here).
-struct RowIv32 {
-  int lo1, hi1, lo2, hi2;
-};
-
-// Keep bits of keys kb .. kb+7 that lie in [lo, hi).
-__device__ inline uint32_t range_bits(int lo, int hi, int kb) {
-  int a = lo - kb, c = hi - kb;
-  a = a < 0 ? 0 : (a > 8 ? 8 : a);
-  c = c < 0 ? 0 : (c > 8 ? 8 : c);
-  return ((1u << c) - 1u) & ~((1u << a) - 1u);
-}
-
-// max of x over lanes l and l ^ 32 (the two lanes that share a query row)
-__device__ inline float max_pair(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-#ifdef BSM_MFMA_PRIO
-#define BSM_PRIO(x) __builtin_amdgcn_s_setprio(x)
-#else
-#define BSM_PRIO(x)
-#endif
-
-// A row's running max is raised only when a new score exceeds it by more than
-// this many powers of two; until then probabilities are taken against the
-// stale max and stay below 2^kRescaleLog2 (exact after the final division, which
-// uses the same max for the sum and for O).
-constexpr float kRescaleLog2 = 8.0f;
+using namespace pipe;
 
 // Per-row-block state of a wave: its 32 query rows.
 template <int D>

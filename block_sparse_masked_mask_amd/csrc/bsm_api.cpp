@@ -498,9 +498,14 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
   p.has_bm = a->bm != nullptr;
   p.bm = bmv;
   hipError_t he;
-  if (dt == BSM_BF16)
-    he = attn_v2_applies(p, (int)g.D) ? launch_attn_bf16_v2(p, (int)g.D, stream)
-                                      : launch_attn_bf16(p, (int)g.D, stream);
+  if (dt == BSM_BF16) {
+    if (attn_decode_applies(p, (int)g.D))
+      he = launch_attn_decode(p, (int)g.D, stream);
+    else if (attn_v2_applies(p, (int)g.D))
+      he = launch_attn_bf16_v2(p, (int)g.D, stream);
+    else
+      he = launch_attn_bf16(p, (int)g.D, stream);
+  }
   else
     he = launch_attn_f32(p, (int)g.D, stream);
   return hip_status(he, "masked_attn_fwd");

@@ -100,5 +100,8 @@ hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
 // pipelined bf16 kernel: two heads of a KV group per workgroup
 bool attn_v2_applies(const AttnParams& p, int D);
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
+// bf16 kernel for at most 32 query rows per (b, h), split along the keys
+bool attn_decode_applies(const AttnParams& p, int D);
+hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s);
 
 }  // namespace bsm

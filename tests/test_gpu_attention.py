@@ -198,3 +198,26 @@ def test_decode_full_size():
             want_o, want_l = oracle_rows(q, k, v, b, h, [0], mask=mask, bias=bias)
             assert_close(o[b, 0, h].float().cpu().numpy()[None], want_o, "bf16", f"O b={b} h={h}")
             assert_close(lse[b, h].cpu().numpy(), want_l, "bf16", f"LSE b={b} h={h}")
+
+
+@pytest.mark.parametrize("Sq", [1, 7, 20, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_short_query_blocks(Sq, D):
+    """At most 32 query rows per (b, h): the key-split kernel, with a per-head
+    mask, a query-broadcast bias, ragged Sk and a GQA group of 2."""
+    B, Sk, H, KVH = 2, 700, 4, 2
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=10 + Sq))
+    m = synth.random_bool((B, H, Sq, 768), 0.4, 7, synth.TID_MASK)
+    m[..., 3] = True
+    mask = torch.from_numpy(m).cuda()
+    bias = synth.normal_tensor((B, KVH, 1, 768), 7, synth.TID_BIAS, "bf16").cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, what=f"short Sq={Sq} D={D}")
+
+
+def test_short_dflash_block():
+    """Two draft blocks of 16 (32 queries) against a long context."""
+    d = bsm.DFlash(1200, 2, 16, is_causal=True, layer_type="sliding", sliding_window=500)
+    q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 8, 2, 128, "bf16", seed=12))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what="short dflash")
