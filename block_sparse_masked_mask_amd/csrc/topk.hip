@@ -9,15 +9,17 @@
 //
 // How: every value is mapped to an unsigned key whose integer order is the
 // value order (sign bit set -> bitwise NOT, else set the sign bit; -0 folded to
-// +0 first). The k-th largest key T is found one 8-bit digit at a time, most
-// significant first (2 passes for bf16, 4 for f32): an LDS histogram of the
-// digit among the keys that share the prefix found so far, then one wave walks
-// the 256 bins from the top to find the digit where the running count reaches
-// the remaining k. Keys > T are selected, and of the keys == T the `need`
-// lowest-indexed ones, found with a workgroup prefix count taken in index order
-// during the single write pass (16 keys per thread, one 16-byte store). When the
-// row fits, its keys stay in LDS between passes so the bias is read from HBM
-// once; otherwise each pass re-reads the row (L2-resident at these sizes).
+// +0 first). The k-th largest key T is then found and the row written in index
+// order: keys > T are selected, and of the keys == T the `need` lowest-indexed
+// ones, found with a workgroup prefix count taken in index order.
+//  * k_topk_reg (rows up to 16K bf16 / 8K f32 keys): the row stays in
+//    registers, 16 contiguous bytes per thread per 4 KiB segment (coalesced
+//    loads and stores); T comes from a radix select with 12-bit digits, so
+//    the histogram atomics of a concentrated row rarely hit the same bin.
+//  * k_topk (longer rows): T is found one 8-bit digit at a time, most
+//    significant first, from LDS histograms of the digit among the keys that
+//    share the prefix found so far; the keys stay in LDS when they fit,
+//    otherwise each pass re-reads the row.
 #include "bsm_internal.h"
 
 namespace bsm {
@@ -34,6 +36,7 @@ struct KeyTraits;
 template <>
 struct KeyTraits<uint16_t> {
   static constexpr int kBits = 16;
+  static constexpr uint32_t kMax = 0xFFFFu;
   // order-preserving key of a bf16 bit pattern
   __device__ static uint16_t key(uint16_t b) {
     if ((b & 0x7FFFu) == 0) b = 0;
@@ -46,6 +49,7 @@ struct KeyTraits<uint16_t> {
 template <>
 struct KeyTraits<uint32_t> {
   static constexpr int kBits = 32;
+  static constexpr uint32_t kMax = 0xFFFFFFFFu;
   __device__ static uint32_t key(uint32_t b) {
     if ((b & 0x7FFFFFFFu) == 0) b = 0;
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -247,18 +251,20 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
 constexpr size_t kCacheMax = 64 * 1024;
 
 // Register-resident variant for rows of up to NSEG * 256 * (16 / sizeof(KeyT))
-// keys: each thread keeps its keys in registers through all passes. Segment s
+// keys: each thread keeps its keys in registers throughout; the threshold
+// comes from a wide-digit radix select (below). Segment s
 // of a row is the 4 KiB (bf16) / 4 KiB (f32) block [s * SEG, (s + 1) * SEG);
 // thread t owns the 16 contiguous bytes at t * EPL of every segment, so each
 // load and each store of a segment is one coalesced wave-wide access. The
 // index-order prefix count of keys equal to the threshold is one workgroup
 // scan of NSEG counters per thread (segment-major, then thread order).
-template <typename KeyT, int NSEG>
+template <typename KeyT, int NSEG, bool HAS_PM>
 __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
   using Tr = KeyTraits<KeyT>;
   constexpr int EPL = 16 / sizeof(KeyT);  // keys per 16-byte load
   constexpr int SEG = kThreads * EPL;
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[4096];
+  __shared__ uint32_t s_scan[kWaves];
   __shared__ uint32_t s_sel[2];
   __shared__ int s_wsum[NSEG][kWaves];
 
@@ -274,9 +280,8 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
   const int lane = t & 63;
   const int w = t >> 6;
   const KeyT sent = Tr::sentinel();
-
   auto valid = [&](int k) -> bool {
-    return k < p.Sk && (prow == nullptr || (k < p.pK && prow[k] != 0));
+    return k < p.Sk && (!HAS_PM || (k < p.pK && prow[k] != 0));
   };
 
   uint4 raw[NSEG];
@@ -288,70 +293,90 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
   KeyT kk[NSEG][EPL];
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
-    const int k0 = s * SEG + t * EPL;
     const KeyT* e = reinterpret_cast<const KeyT*>(&raw[s]);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) kk[s][i] = valid(k0 + i) ? Tr::key(e[i]) : sent;
+    for (int i = 0; i < EPL; ++i)
+      kk[s][i] = valid(s * SEG + t * EPL + i) ? Tr::key(e[i]) : sent;
   }
 
+  // The k-th largest key T, by radix select with wide digits: 12 bits first
+  // (4096 LDS bins, so the few exponent values a bias row concentrates in are
+  // still spread over many bins and the LDS atomics rarely collide), then the
+  // remaining 4 (bf16) or 12 + 8 (f32) bits among the keys that share the
+  // prefix found so far. After each histogram the bins are scanned from the
+  // top (16 per thread, one workgroup scan) to find the digit at which the
+  // running count reaches the remaining k.
   const int keff = p.k < K ? (int)p.k : K;
   uint32_t prefix = 0;
   uint32_t rem = (uint32_t)keff;
   if (keff > 0 && keff < K) {
-    for (int shift = Tr::kBits - 8; shift >= 0; shift -= 8) {
-      for (int i = t; i < 256; i += kThreads) s_hist[i] = 0;
+    int hi_bits = Tr::kBits;  // bits above the current digit are fixed
+    while (hi_bits > 0) {
+      const int dw = hi_bits >= 12 ? 12 : hi_bits;
+      const int sh = hi_bits - dw;
+      const int nb = 1 << dw;
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      for (int i = t; i < nb; i += kThreads) s_hist[i] = 0;
       __syncthreads();
-      const int hs = shift + 8;
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) {
         if (s * SEG + t * EPL < K) {
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const uint32_t key = (uint32_t)kk[s][i];
-            const bool match = hs >= Tr::kBits || ((key ^ prefix) >> hs) == 0;
-            if (match) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+            const bool match = hi_bits >= Tr::kBits ||
+                               ((key ^ prefix) >> (sh + dw)) == 0;
+            if (match) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
           }
         }
       }
       __syncthreads();
-      if (t < 64) {
-        uint32_t c[4];
-        uint32_t sum = 0;
+      // thread t sums bins nb-1-16t .. nb-16-16t (descending digit order)
+      const int per = nb >= 16 * kThreads ? nb / kThreads : 16;
+      const int first = nb - 1 - per * t;
+      uint32_t c = 0;
+      for (int j = 0; j < per; ++j) {
+        const int d = first - j;
+        c += d >= 0 ? s_hist[d] : 0u;
+      }
+      uint32_t incl = c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c[j] = s_hist[255 - 4 * t - j];
-          sum += c[j];
-        }
-        uint32_t incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) s_scan[w] = incl;
+      __syncthreads();
+      uint32_t off = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(incl, o, 64);
-          if (t >= o) incl += y;
-        }
-        const uint32_t excl = incl - sum;
-        if (excl < rem && rem <= incl) {
-          uint32_t above = excl;
-          int d = 255 - 4 * t;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (above + c[j] >= rem) {
-              d = 255 - 4 * t - j;
-              break;
-            }
-            above += c[j];
+      for (int i = 0; i < kWaves; ++i) off += i < w ? s_scan[i] : 0u;
+      incl += off;
+      const uint32_t excl = incl - c;
+      if (c > 0 && excl < rem && rem <= incl) {
+        uint32_t above = excl;
+        int dsel = first;
+        for (int j = 0; j < per; ++j) {
+          const int d = first - j;
+          const uint32_t cd = s_hist[d];
+          if (above + cd >= rem) {
+            dsel = d;
+            break;
           }
-          s_sel[0] = (uint32_t)d;
-          s_sel[1] = above;
+          above += cd;
         }
+        s_sel[0] = (uint32_t)dsel;
+        s_sel[1] = above;
       }
       __syncthreads();
-      prefix |= s_sel[0] << shift;
+      prefix |= s_sel[0] << sh;
       rem -= s_sel[1];
-      __syncthreads();
+      hi_bits = sh;
+      __syncthreads();  // s_hist / s_scan / s_sel reuse
     }
   }
   const uint32_t T = prefix;
-  const int need = (int)rem;  // keys equal to T to take, lowest index first
+  const int cnt_gt = keff - (int)rem;  // #{key > T}
+  const int need = keff - cnt_gt;  // keys equal to T to take, lowest index first
 
   // prefix counts of keys == T in index order (segment-major, then thread)
   int excl[NSEG];
@@ -397,19 +422,11 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
     int r = excl[s];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      bool sel;
-      if (keff == 0) {
-        sel = false;
-      } else if (keff >= K) {
-        sel = true;
-      } else {
-        const uint32_t key = (uint32_t)kk[s][i];
-        sel = key > T;
-        if (key == T) {
-          sel = r < need;
-          ++r;
-        }
-      }
+      const uint32_t key = (uint32_t)kk[s][i];
+      const bool eq = key == T;
+      bool sel = key > T || (eq && r < need);
+      r += eq ? 1 : 0;
+      sel = keff >= K ? true : (keff == 0 ? false : sel);
       bits |= (uint32_t)(sel && valid(k0 + i)) << i;
     }
     if (EPL == 8) {
@@ -429,20 +446,25 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
   }
 }
 
-template <typename KeyT>
-bool launch_reg(const TopkParams& p, unsigned rows, hipStream_t s) {
+template <typename KeyT, bool HAS_PM>
+bool launch_reg2(const TopkParams& p, unsigned rows, hipStream_t s) {
   constexpr int SEG = kThreads * (16 / sizeof(KeyT));
   const int nseg = (int)((p.K + SEG - 1) / SEG);
   const dim3 grid(rows), block(kThreads);
   switch (nseg) {
-    case 1: hipLaunchKernelGGL((k_topk_reg<KeyT, 1>), grid, block, 0, s, p); return true;
-    case 2: hipLaunchKernelGGL((k_topk_reg<KeyT, 2>), grid, block, 0, s, p); return true;
+    case 1: hipLaunchKernelGGL((k_topk_reg<KeyT, 1, HAS_PM>), grid, block, 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((k_topk_reg<KeyT, 2, HAS_PM>), grid, block, 0, s, p); return true;
     case 3:
-    case 4: hipLaunchKernelGGL((k_topk_reg<KeyT, 4>), grid, block, 0, s, p); return true;
+    case 4: hipLaunchKernelGGL((k_topk_reg<KeyT, 4, HAS_PM>), grid, block, 0, s, p); return true;
     case 5: case 6: case 7:
-    case 8: hipLaunchKernelGGL((k_topk_reg<KeyT, 8>), grid, block, 0, s, p); return true;
+    case 8: hipLaunchKernelGGL((k_topk_reg<KeyT, 8, HAS_PM>), grid, block, 0, s, p); return true;
     default: return false;
   }
+}
+
+template <typename KeyT>
+bool launch_reg(const TopkParams& p, unsigned rows, hipStream_t s) {
+  return p.pm ? launch_reg2<KeyT, true>(p, rows, s) : launch_reg2<KeyT, false>(p, rows, s);
 }
 
 }  // namespace
