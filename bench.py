@@ -42,6 +42,31 @@ WORKLOAD = "dflash_train_bf16"
 METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build GB/s"
 
 
+# HBM bytes per launch of the attention kernel on this workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, averaged over
+# both layers) scaled by what the same counters read for a 1 GiB device copy
+# (FETCH_SIZE reads 0.5 GiB for it, so x2.0; WRITE_SIZE reads 1 GiB, so x1.0).
+# The figure holds only for the kernel sources it was taken on: when their hash
+# differs, traffic is reported as null.
+ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
+                            "dflash_rows.h"],
+                "sha256_16": "cd6e0ea75d01457a",
+                "fetch_kib": 86462.8, "write_kib": 65536.0,
+                "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+def attn_traffic_bytes():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, "block_sparse_masked_mask_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != ATTN_TRAFFIC["sha256_16"]:
+        return None
+    t = ATTN_TRAFFIC
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
+
 def counted_flops(bm, geom):
     """4*D*rows*keys over non-empty tiles of every (b, h), from a block mask."""
     B, H, KVH, Sq, Sk, D = geom
@@ -115,6 +140,18 @@ def measure_mask_build(reps=5):
     return {"workload": "long_dflash_dense_mask", "shape": [1, 1, d.Sq, 65536],
             "bytes": int(nbytes), "ms": ms, "GB/s": nbytes / ms / 1e6,
             "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def copy_probe(mib=1024, reps=3):
+    """Plain device-to-device copy of a known size: the calibration run for the
+    HBM byte counters (each copy reads and writes mib MiB)."""
+    n = mib << 20
+    src = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "reps": reps}), flush=True)
 
 
 def _time_ms(fn, reps=10):
@@ -247,12 +284,17 @@ def main():
     ap.add_argument("--no-mask-build", action="store_true")
     ap.add_argument("--components", action="store_true",
                     help="also time the other workloads' kernels (top-k, builders, attention)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
               "is measured on a single MI355X; sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
+    if args.copy_probe:
+        copy_probe()
+        return
     step = Step()
     for _ in range(args.warmup):
         step.run()
@@ -293,7 +335,7 @@ def main():
                    "flops_per_step": int(flops_step)},
         "roofline": {"bound": "mfma", "kernel": "k_attn_bf16_v2<128>", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": attn_traffic_bytes(),
                      "avg_launch_ms": float(np.mean(attn_ms)),
                      "flops_per_launch": float(np.mean(attn_flops))},
         "per_layer": per_layer,
