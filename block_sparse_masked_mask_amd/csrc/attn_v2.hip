@@ -52,20 +52,47 @@ struct RowBlock {
   bool qvalid;
 };
 
+// Per-lane byte offsets of the LDS operand reads, computed once: the K operand
+// of d-step s in key chunk 0 (chunk c adds 32 rows), and the first transposed
+// V read of d-chunk dc at key 0 (the key step adds rows). The swizzles depend
+// only on a row's low bits, which the added rows leave alone.
+template <int D>
+struct LaneOffs {
+  uint32_t k[D / 16];
+  uint32_t v[D / 32];
+  __device__ inline void init(int lane) {
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+    const int row = perm_row(n);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      k[s] = (uint32_t)((row * D + (((2 * s + hh) ^ swz_k<D>(row)) * 8)) * 2);
+    // transposed reads: in each 16-lane group, lane 4e + g reads 4 d-values of
+    // key row e (and e + 4 for the second read)
+    const int blk = lane >> 4;
+    const int e4 = (lane >> 2) & 3;
+    const int g4 = lane & 3;
+    const int row0 = 8 * (blk >> 1) + e4;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+      v[dc] = (uint32_t)((row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4) * 2);
+    }
+  }
+};
+
 template <int D, int RB>
 __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
-                                    bool is_full, RowBlock<D>* rbk, int lane) {
+                                    bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
+                                    int lane) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
-  const int n = lane & 31;
   const int hh = lane >> 5;
   const int k0 = kt * kTile;
   const bool check_k = k0 + kTile > p.Sk;
   const bool check_mask = !is_full && p.mask_kind != 0;
-  // transposed-read lane roles
-  const int blk = lane >> 4;
-  const int e4 = (lane >> 2) & 3;
-  const int g4 = lane & 3;
+  const char* kbase = reinterpret_cast<const char*>(t.k);
+  const char* vbase = reinterpret_cast<const char*>(t.v);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 #pragma unroll
@@ -75,9 +102,7 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
     // K operand i of this half: chunk c = i / NS, k-step s = i % NS
     auto kop = [&](int i) {
       const int c = i / NS, s = i % NS;
-      const int row = (2 * half + c) * 32 + perm_row(n);
-      return *reinterpret_cast<const bf16x8*>(t.k + row * D +
-                                             (((2 * s + hh) ^ swz_k<D>(row)) * 8));
+      return *reinterpret_cast<const bf16x8*>(kbase + off.k[s] + (2 * half + c) * 32 * D * 2);
     };
     bf16x8 ka = kop(0);
 #pragma unroll
@@ -96,11 +121,8 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
     auto vop = [&](int i) {
       const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
       const int kb = (2 * half + c) * 32 + 16 * sb;
-      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
-      const int row0 = kb + 8 * (blk >> 1) + e4;
-      const int row1 = row0 + 4;
-      const __bf16* a0 = t.v + row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4;
-      const __bf16* a1 = t.v + row1 * D + ((chunk ^ swz_v<D>(row1)) * 8) + (g4 & 1) * 4;
+      const char* a0 = vbase + off.v[dc] + kb * D * 2;
+      const char* a1 = a0 + 4 * D * 2;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
       return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
@@ -292,6 +314,8 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
                         (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         (int64_t)kvh * p.v_sh;
+  LaneOffs<D> off;
+  off.init(lane);
   Loader<D, RB> ld;
   ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
 
@@ -313,7 +337,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
-    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, lane);
+    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   }

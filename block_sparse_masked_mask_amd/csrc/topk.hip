@@ -36,7 +36,6 @@ struct KeyTraits;
 template <>
 struct KeyTraits<uint16_t> {
   static constexpr int kBits = 16;
-  static constexpr uint32_t kMax = 0xFFFFu;
   // order-preserving key of a bf16 bit pattern
   __device__ static uint16_t key(uint16_t b) {
     if ((b & 0x7FFFu) == 0) b = 0;
@@ -49,7 +48,6 @@ struct KeyTraits<uint16_t> {
 template <>
 struct KeyTraits<uint32_t> {
   static constexpr int kBits = 32;
-  static constexpr uint32_t kMax = 0xFFFFFFFFu;
   __device__ static uint32_t key(uint32_t b) {
     if ((b & 0x7FFFFFFFu) == 0) b = 0;
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);

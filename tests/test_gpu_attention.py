@@ -221,3 +221,34 @@ def test_short_dflash_block():
     q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 8, 2, 128, "bf16", seed=12))
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
     _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what="short dflash")
+
+
+# ---------------------------------------------------------------------------
+# bf16, D = 128, no bias and no dense mask: the two-head interleaved kernel.
+# Its visit list splits into a run of plain tiles and a run of tested tiles;
+# these cases cover an all-plain list, a single tile, a list with no plain
+# tile, ragged query and key ends, and GQA groups of 2 and 4.
+
+@pytest.mark.parametrize("B,Sq,Sk,H,KVH", [
+    (1, 256, 512, 2, 1),     # every tile plain
+    (2, 100, 128, 4, 2),     # one key tile, rows past Sq in every wave
+    (1, 130, 129, 8, 2),     # ragged: 2 query tiles, key tile straddling Sk
+    (2, 384, 1000, 4, 1),    # G = 4, ragged keys
+])
+def test_no_mask_bf16_d128(B, Sq, Sk, H, KVH):
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, 128, "bf16", seed=20 + Sq))
+    _run_and_check(q, k, v, "bf16", what=f"no mask B={B} Sq={Sq} Sk={Sk} H={H} KVH={KVH}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(ctx_len=512, num_blocks=16, block_size=16, layer_type="sliding", sliding_window=200),
+    dict(ctx_len=300, num_blocks=10, block_size=16),
+])
+@pytest.mark.parametrize("with_bm", [True, False])
+def test_dflash_bf16_d128_block_mask_or_not(case, with_bm):
+    """Predicate partial tiles after full ones (with a block mask), or every
+    tile tested (without)."""
+    d = bsm.DFlash(**case)
+    q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 4, 2, 128, "bf16", seed=30))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d) if with_bm else None
+    _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what=f"dflash bm={with_bm} {case}")
