@@ -39,6 +39,9 @@ Modules:
   attention  -- float64 softmax attention over the kept keys (pinned: SDPA in
                 float64, single-key rows, convexity, GQA and broadcast
                 identities).
+  attention_bwd -- float64 gradients dQ / dK / dV / dbias of the same
+                attention (pinned: central finite differences of the forward
+                oracle, torch autograd in float64, broadcast dbias reductions).
   normalize  -- 2D/4D pre-mask normalisation and key-length rounding.
 
 No function here is "parity unpinned" except where its docstring says so.
