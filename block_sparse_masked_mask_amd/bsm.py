@@ -26,7 +26,8 @@ BSM_OK, BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE, BSM_E_UNSUPPORTED, BS
 BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
-           "dynamic_topk_mask", "dflash_dense_mask", "masked_attn_fwd", "bsm_last_error")
+           "dynamic_topk_mask", "dflash_dense_mask", "masked_attn_fwd",
+           "attn_bwd_workspace_size", "masked_attn_bwd", "bsm_last_error")
 
 
 class Tensor4(ctypes.Structure):
@@ -57,6 +58,16 @@ class AttnArgs(ctypes.Structure):
                 ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC))]
 
 
+class AttnBwdArgs(ctypes.Structure):
+    _fields_ = [("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("o", Tensor4),
+                ("dout", Tensor4), ("lse", c_void_p), ("dq", Tensor4), ("dk", Tensor4),
+                ("dv", Tensor4), ("softmax_scale", c_float), ("reserved", c_int32),
+                ("pred", POINTER(DFlashC)), ("mask", POINTER(Tensor4)),
+                ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC)),
+                ("dbias", POINTER(Tensor4)), ("workspace", c_void_p),
+                ("workspace_bytes", c_int64)]
+
+
 _lib = None
 
 
@@ -79,6 +90,9 @@ def lib():
                                         c_void_p, c_void_p]
         L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
         L.masked_attn_fwd.argtypes = [POINTER(Geom), POINTER(AttnArgs), c_void_p]
+        L.attn_bwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs),
+                                              POINTER(c_int64)]
+        L.masked_attn_bwd.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs), c_void_p]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = c_int32
         _lib = L
@@ -309,6 +323,55 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
         a.bm = ctypes.pointer(bmc)
     _check(lib().masked_attn_fwd(ctypes.byref(geom.c()), ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def masked_attn_bwd(q, k, v, out, dout, lse, pred=None, mask=None, bias=None, block_mask=None,
+                    softmax_scale=None, need_dbias=False, stream=None):
+    """Masked attention backward; returns (dq, dk, dv, dbias). dbias is None
+    unless need_dbias (with a bias); it has the bias's shape, K-dim rounded to
+    128, and is returned sliced to Sk like the gradients of PR #190."""
+    geom = geometry_of(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = None
+    a = AttnBwdArgs()
+    a.q, a.k, a.v = tensor4(q), tensor4(k), tensor4(v)
+    a.o, a.dout = tensor4(out), tensor4(dout)
+    a.lse = lse.data_ptr() if lse.numel() else None
+    a.dq, a.dk, a.dv = tensor4(dq), tensor4(dk), tensor4(dv)
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.reserved = 0
+    keep = []
+    if pred is not None:
+        pc = pred.c()
+        keep.append(pc)
+        a.pred = ctypes.pointer(pc)
+    if mask is not None:
+        mc = tensor4(mask)
+        keep.append(mc)
+        a.mask = ctypes.pointer(mc)
+    if bias is not None:
+        bc = tensor4(bias)
+        keep.append(bc)
+        a.bias = ctypes.pointer(bc)
+        if need_dbias:
+            dbias = torch.empty(bias.shape, dtype=bias.dtype, device=bias.device)
+            dc = tensor4(dbias)
+            keep.append(dc)
+            a.dbias = ctypes.pointer(dc)
+    if block_mask is not None:
+        bmc = block_mask.c()
+        keep.append(bmc)
+        a.bm = ctypes.pointer(bmc)
+    gc = geom.c()
+    nbytes = c_int64(0)
+    _check(lib().attn_bwd_workspace_size(ctypes.byref(gc), ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    a.workspace = ws.data_ptr()
+    a.workspace_bytes = nbytes.value
+    _check(lib().masked_attn_bwd(ctypes.byref(gc), ctypes.byref(a), _stream(stream)))
+    if dbias is not None:
+        dbias = dbias[..., :geom.Sk]
+    return dq, dk, dv, dbias
 
 
 def default_scale(D):

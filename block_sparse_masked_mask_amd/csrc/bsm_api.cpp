@@ -383,6 +383,130 @@ int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred, uint8_t* out
   return hip_status(launch_dflash_dense(r, g.Sq, g.Sk, g.Kr, out_mask, stream), "dflash_dense");
 }
 
+}  // extern "C"
+
+namespace {
+
+// ---- shared by the attention forward and backward
+
+struct AttnInputs {
+  DFlashRule rule{};
+  Aux mk{}, bs{};
+  BlockMaskView bmv{};
+};
+
+// Mask source, bias and block mask of an attention call.
+int check_attn_aux(const Geo& g, int32_t dt, const bsm_dflash* pred, const bsm_tensor4* mask,
+                   const bsm_tensor4* bias, const bsm_block_mask* bm, float softmax_scale,
+                   AttnInputs& in) {
+  int e;
+  if (pred && mask) return fail(BSM_E_ARG, "give at most one of pred and mask");
+  if (std::isnan(softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
+  if (pred && (e = check_dflash(pred, g, in.rule))) return e;
+  if (mask && (e = check_aux(mask, "mask", g, BSM_BOOL, in.mk))) return e;
+  if (bias && (e = check_aux(bias, "bias", g, dt, in.bs))) return e;
+  if (bm) {
+    if (!pred && !mask) return fail(BSM_E_ARG, "a block mask needs pred or mask");
+    int64_t shp[4];
+    expected_bm(g, pred, &in.mk, shp);
+    if (bm->Bm != shp[0] || bm->Hm != shp[1] || bm->nQm != shp[2] || bm->nK != shp[3])
+      return fail(BSM_E_SHAPE, "block mask dims (%lld,%lld,%lld,%lld) do not match this call "
+                  "(%lld,%lld,%lld,%lld)", (long long)bm->Bm, (long long)bm->Hm,
+                  (long long)bm->nQm, (long long)bm->nK, (long long)shp[0], (long long)shp[1],
+                  (long long)shp[2], (long long)shp[3]);
+    if (shp[0] * shp[1] * shp[2] > 0 &&
+        (!bm->kv_num_blocks || !bm->full_kv_num_blocks ||
+         (shp[3] > 0 && (!bm->kv_indices || !bm->full_kv_indices))))
+      return fail(BSM_E_ARG, "block mask buffer is NULL");
+    in.bmv.kv_num = bm->kv_num_blocks;
+    in.bmv.kv_idx = bm->kv_indices;
+    in.bmv.full_num = bm->full_kv_num_blocks;
+    in.bmv.full_idx = bm->full_kv_indices;
+    in.bmv.Bm = bm->Bm;
+    in.bmv.Hm = bm->Hm;
+    in.bmv.nQm = bm->nQm;
+    in.bmv.nK = bm->nK;
+    in.bmv.h_mode = bm_head_mode(g, bm->Hm);
+  }
+  return BSM_OK;
+}
+
+// (b, q, h) element strides of a (B, Sq, H, D) tensor in the iteration space:
+// under the swap, head kvh*G + i of a KV group is row i of KV head kvh.
+void qlike_strides(const Geo& g, const int64_t* st, int64_t& sb, int64_t& sq, int64_t& sh) {
+  sb = st[0];
+  if (!g.swap) {
+    sq = st[1];
+    sh = st[2];
+  } else {
+    sq = st[2];
+    sh = g.G * st[2];
+  }
+}
+
+void fill_params(const Geo& g, const bsm_tensor4& q, const bsm_tensor4& k,
+                 const bsm_tensor4& v, void* o, const int64_t* o_stride, float* lse,
+                 float softmax_scale, bool has_pred, bool has_mask, bool has_bias,
+                 bool has_bm, const AttnInputs& in, AttnParams& p) {
+  p = AttnParams{};
+  p.q = q.data;
+  p.k = k.data;
+  p.v = v.data;
+  p.o = o;
+  p.lse = lse;
+  p.k_sb = k.stride[0];
+  p.k_sk = k.stride[1];
+  p.k_sh = k.stride[2];
+  p.v_sb = v.stride[0];
+  p.v_sk = v.stride[1];
+  p.v_sh = v.stride[2];
+  p.B = (int32_t)g.B;
+  p.Sk = (int32_t)g.Sk;
+  p.nK = (int32_t)g.nK;
+  qlike_strides(g, q.stride, p.q_sb, p.q_sq, p.q_sh);
+  if (o_stride) qlike_strides(g, o_stride, p.o_sb, p.o_sq, p.o_sh);
+  p.KVH = (int32_t)g.KVH;
+  if (!g.swap) {
+    p.lse_sb = g.H * g.Sq;
+    p.lse_sh = g.Sq;
+    p.lse_sq = 1;
+    p.H = (int32_t)g.H;
+    p.G = (int32_t)g.G;
+    p.Sq = (int32_t)g.Sq;
+  } else {
+    p.lse_sb = g.H;
+    p.lse_sh = g.G;
+    p.lse_sq = 1;
+    p.H = (int32_t)g.KVH;
+    p.G = 1;
+    p.Sq = (int32_t)g.G;
+  }
+  p.nQ = (p.Sq + kTile - 1) / kTile;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)g.D);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.mask_kind = has_pred ? 1 : (has_mask ? 2 : 0);
+  p.pred_row0 = g.swap && has_pred;
+  p.rule = in.rule;
+  p.mask = in.mk.view;
+  p.bias = in.bs.view;
+  p.has_bias = has_bias;
+  p.has_bm = has_bm;
+  p.bm = in.bmv;
+}
+
+// Float workspace of the backward: Delta (B*H*Sq), then the dbias accumulator
+// (the bias's element count) when dbias is requested; each part 256-byte aligned.
+int64_t bwd_delta_bytes(const Geo& g) { return round_multiple(g.B * g.H * g.Sq * 4, 256); }
+int64_t bwd_workspace_bytes(const Geo& g, const bsm_tensor4* bias, const bsm_tensor4* dbias) {
+  int64_t n = bwd_delta_bytes(g);
+  if (bias && dbias) n += round_multiple(numel(bias) * 4, 256);
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
 int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t stream) {
   Geo g;
   int e = check_geom(geom, g);
@@ -407,96 +531,14 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
     for (int i = 0; i < 4; ++i) o.stride[i] = a->o_stride[i];
     if ((e = check_tensor_qkv(&o, "o", g.B, g.Sq, g.H, g.D, dt))) return e;
   }
-  if (a->pred && a->mask) return fail(BSM_E_ARG, "give at most one of pred and mask");
-  if (std::isnan(a->softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
-  DFlashRule rule{};
-  if (a->pred && (e = check_dflash(a->pred, g, rule))) return e;
-  Aux mk{}, bs{};
-  if (a->mask && (e = check_aux(a->mask, "mask", g, BSM_BOOL, mk))) return e;
-  if (a->bias && (e = check_aux(a->bias, "bias", g, dt, bs))) return e;
-  BlockMaskView bmv{};
-  if (a->bm) {
-    if (!a->pred && !a->mask) return fail(BSM_E_ARG, "a block mask needs pred or mask");
-    int64_t shp[4];
-    expected_bm(g, a->pred, &mk, shp);
-    const bsm_block_mask* m = a->bm;
-    if (m->Bm != shp[0] || m->Hm != shp[1] || m->nQm != shp[2] || m->nK != shp[3])
-      return fail(BSM_E_SHAPE, "block mask dims (%lld,%lld,%lld,%lld) do not match this call "
-                  "(%lld,%lld,%lld,%lld)", (long long)m->Bm, (long long)m->Hm,
-                  (long long)m->nQm, (long long)m->nK, (long long)shp[0], (long long)shp[1],
-                  (long long)shp[2], (long long)shp[3]);
-    if (shp[0] * shp[1] * shp[2] > 0 &&
-        (!m->kv_num_blocks || !m->full_kv_num_blocks ||
-         (shp[3] > 0 && (!m->kv_indices || !m->full_kv_indices))))
-      return fail(BSM_E_ARG, "block mask buffer is NULL");
-    bmv.kv_num = m->kv_num_blocks;
-    bmv.kv_idx = m->kv_indices;
-    bmv.full_num = m->full_kv_num_blocks;
-    bmv.full_idx = m->full_kv_indices;
-    bmv.Bm = m->Bm;
-    bmv.Hm = m->Hm;
-    bmv.nQm = m->nQm;
-    bmv.nK = m->nK;
-    bmv.h_mode = bm_head_mode(g, m->Hm);
-  }
+  AttnInputs in;
+  if ((e = check_attn_aux(g, dt, a->pred, a->mask, a->bias, a->bm, a->softmax_scale, in)))
+    return e;
   if (g.B == 0 || g.Sq == 0) return BSM_OK;
 
-  AttnParams p{};
-  p.q = a->q.data;
-  p.k = a->k.data;
-  p.v = a->v.data;
-  p.o = a->o;
-  p.lse = a->lse;
-  p.k_sb = a->k.stride[0];
-  p.k_sk = a->k.stride[1];
-  p.k_sh = a->k.stride[2];
-  p.v_sb = a->v.stride[0];
-  p.v_sk = a->v.stride[1];
-  p.v_sh = a->v.stride[2];
-  p.B = (int32_t)g.B;
-  p.Sk = (int32_t)g.Sk;
-  p.nK = (int32_t)g.nK;
-  if (!g.swap) {
-    p.q_sb = a->q.stride[0];
-    p.q_sq = a->q.stride[1];
-    p.q_sh = a->q.stride[2];
-    p.o_sb = a->o_stride[0];
-    p.o_sq = a->o_stride[1];
-    p.o_sh = a->o_stride[2];
-    p.lse_sb = g.H * g.Sq;
-    p.lse_sh = g.Sq;
-    p.lse_sq = 1;
-    p.H = (int32_t)g.H;
-    p.KVH = (int32_t)g.KVH;
-    p.G = (int32_t)g.G;
-    p.Sq = (int32_t)g.Sq;
-  } else {
-    // heads kvh*G + i of one KV group -> rows i of KV head kvh
-    p.q_sb = a->q.stride[0];
-    p.q_sq = a->q.stride[2];
-    p.q_sh = g.G * a->q.stride[2];
-    p.o_sb = a->o_stride[0];
-    p.o_sq = a->o_stride[2];
-    p.o_sh = g.G * a->o_stride[2];
-    p.lse_sb = g.H;
-    p.lse_sh = g.G;
-    p.lse_sq = 1;
-    p.H = (int32_t)g.KVH;
-    p.KVH = (int32_t)g.KVH;
-    p.G = 1;
-    p.Sq = (int32_t)g.G;
-  }
-  p.nQ = (p.Sq + kTile - 1) / kTile;
-  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)g.D);
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.mask_kind = a->pred ? 1 : (a->mask ? 2 : 0);
-  p.pred_row0 = g.swap && a->pred;
-  p.rule = rule;
-  p.mask = mk.view;
-  p.bias = bs.view;
-  p.has_bias = a->bias != nullptr;
-  p.has_bm = a->bm != nullptr;
-  p.bm = bmv;
+  AttnParams p;
+  fill_params(g, a->q, a->k, a->v, a->o, a->o_stride, a->lse, a->softmax_scale, a->pred,
+              a->mask, a->bias, a->bm, in, p);
   hipError_t he;
   if (dt == BSM_BF16) {
     if (attn_decode_applies(p, (int)g.D))
@@ -509,6 +551,110 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
   else
     he = launch_attn_f32(p, (int)g.D, stream);
   return hip_status(he, "masked_attn_fwd");
+}
+
+int attn_bwd_workspace_size(const bsm_geom* geom, const bsm_attn_bwd_args* a, int64_t* bytes) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!a || !bytes) return fail(BSM_E_ARG, "args or bytes is NULL");
+  *bytes = bwd_workspace_bytes(g, a->bias, a->dbias);
+  return BSM_OK;
+}
+
+int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_t stream) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!a) return fail(BSM_E_ARG, "args is NULL");
+  if (a->reserved != 0) return fail(BSM_E_ARG, "args.reserved must be 0");
+  if (g.D != 64 && g.D != 128)
+    return fail(BSM_E_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)g.D);
+  const int32_t dt = a->q.dtype;
+  if (dt != BSM_BF16 && dt != BSM_F32) return fail(BSM_E_DTYPE, "q must be bf16 or f32");
+  if ((e = check_tensor_qkv(&a->q, "q", g.B, g.Sq, g.H, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->k, "k", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->v, "v", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->o, "o", g.B, g.Sq, g.H, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dout, "dout", g.B, g.Sq, g.H, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dq, "dq", g.B, g.Sq, g.H, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dk, "dk", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dv, "dv", g.B, g.Sk, g.KVH, g.D, dt))) return e;
+  if (!a->lse && g.B * g.H * g.Sq > 0) return fail(BSM_E_ARG, "lse is NULL");
+  AttnInputs in;
+  if ((e = check_attn_aux(g, dt, a->pred, a->mask, a->bias, a->bm, a->softmax_scale, in)))
+    return e;
+  if (a->dbias) {
+    if (!a->bias) return fail(BSM_E_ARG, "dbias needs bias");
+    const bsm_tensor4* b = a->bias;
+    const bsm_tensor4* d = a->dbias;
+    for (int i = 0; i < 4; ++i)
+      if (d->size[i] != b->size[i]) return fail(BSM_E_SHAPE, "dbias: sizes must equal bias's");
+    if (d->dtype != dt) return fail(BSM_E_DTYPE, "dbias: dtype must equal bias's");
+    if ((e = check_strides(d, "dbias", elem_size(dt)))) return e;
+    if (!d->data && numel(d) > 0) return fail(BSM_E_ARG, "dbias: data is NULL");
+  }
+  const int64_t need = bwd_workspace_bytes(g, a->bias, a->dbias);
+  if (a->workspace_bytes < need)
+    return fail(BSM_E_ARG, "workspace of %lld bytes, %lld needed", (long long)a->workspace_bytes,
+                (long long)need);
+  if (need > 0 && (!a->workspace || (uintptr_t)a->workspace % 256))
+    return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
+  if (g.B == 0) return BSM_OK;
+
+  AttnBwdParams p{};
+  fill_params(g, a->q, a->k, a->v, const_cast<void*>(a->o.data), a->o.stride,
+              const_cast<float*>(a->lse),
+              a->softmax_scale, a->pred, a->mask, a->bias, a->bm, in, p.f);
+  p.scale = p.f.scale_log2 / 1.4426950408889634f;
+  p.dout = a->dout.data;
+  qlike_strides(g, a->dout.stride, p.do_sb, p.do_sq, p.do_sh);
+  p.dq = const_cast<void*>(a->dq.data);
+  qlike_strides(g, a->dq.stride, p.dq_sb, p.dq_sq, p.dq_sh);
+  p.dk = const_cast<void*>(a->dk.data);
+  p.dk_sb = a->dk.stride[0];
+  p.dk_sk = a->dk.stride[1];
+  p.dk_sh = a->dk.stride[2];
+  p.dv = const_cast<void*>(a->dv.data);
+  p.dv_sb = a->dv.stride[0];
+  p.dv_sk = a->dv.stride[1];
+  p.dv_sh = a->dv.stride[2];
+  char* ws = static_cast<char*>(a->workspace);
+  p.delta = reinterpret_cast<float*>(ws);
+  DbiasOut dout{};
+  hipError_t he = hipSuccess;
+  if (a->dbias) {
+    float* acc = reinterpret_cast<float*>(ws + bwd_delta_bytes(g));
+    // the accumulator: contiguous float with the bias's sizes, seen like the bias
+    bsm_tensor4 t{};
+    t.data = acc;
+    t.dtype = BSM_F32;
+    for (int i = 0; i < 4; ++i) t.size[i] = a->bias->size[i];
+    t.stride[3] = 1;
+    t.stride[2] = t.size[3];
+    t.stride[1] = t.size[2] * t.stride[2];
+    t.stride[0] = t.size[1] * t.stride[1];
+    Aux av;
+    if ((e = check_aux(&t, "dbias workspace", g, BSM_F32, av))) return e;
+    p.dbias_acc = acc;
+    p.dbias = av.view;
+    he = launch_fill_zero(acc, numel(&t), stream);
+    if (he != hipSuccess) return hip_status(he, "masked_attn_bwd");
+    dout.acc = acc;
+    dout.out = const_cast<void*>(a->dbias->data);
+    dout.n0 = t.size[0];
+    dout.n1 = t.size[1];
+    dout.n2 = t.size[2];
+    dout.K = t.size[3];
+    dout.Sk = g.Sk;
+    dout.s0 = a->dbias->size[0] == 1 ? 0 : a->dbias->stride[0];
+    dout.s1 = a->dbias->size[1] == 1 ? 0 : a->dbias->stride[1];
+    dout.s2 = a->dbias->size[2] == 1 ? 0 : a->dbias->stride[2];
+    dout.is_bf16 = dt == BSM_BF16;
+  }
+  he = launch_attn_bwd(p, (int)g.D, dt == BSM_BF16, stream);
+  if (he == hipSuccess && a->dbias) he = launch_dbias_out(dout, stream);
+  return hip_status(he, "masked_attn_bwd");
 }
 
 }  // extern "C"

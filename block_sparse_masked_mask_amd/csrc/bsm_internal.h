@@ -66,6 +66,37 @@ struct AttnParams {
   BlockMaskView bm;
 };
 
+// Backward: the forward's view plus the incoming gradient, the gradient
+// outputs and the float scratch (all in the kernels' iteration space, i.e.
+// after the head-group swap when it applies).
+struct AttnBwdParams {
+  AttnParams f;             // q, k, v, o, lse, geometry, mask, bias, block mask
+  const void* dout;
+  int64_t do_sb, do_sq, do_sh;
+  void* dq;
+  int64_t dq_sb, dq_sq, dq_sh;
+  void* dk;
+  int64_t dk_sb, dk_sk, dk_sh;
+  void* dv;
+  int64_t dv_sb, dv_sk, dv_sh;
+  float* delta;             // (B, H, Sq) rowsum(dO * O), contiguous
+  float* dbias_acc;         // float accumulator of dbias, or null
+  AuxView dbias;            // dbias_acc addressed like the bias
+  float scale;              // softmax scale (natural units)
+  int32_t pad;
+};
+
+// Float dbias accumulator -> dbias (bias dtype, caller strides), original
+// (unswapped) index space; keys >= Sk get 0.
+struct DbiasOut {
+  const float* acc;         // contiguous (n0, n1, n2, K)
+  void* out;
+  int64_t n0, n1, n2, K, Sk;
+  int64_t s0, s1, s2;       // out element strides (last dim contiguous)
+  int32_t is_bf16;
+  int32_t pad;
+};
+
 struct DenseMaskView {
   const uint8_t* data;
   int64_t sb, sh, sq;
@@ -100,6 +131,10 @@ hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
 // pipelined bf16 kernel: two heads of a KV group per workgroup
 bool attn_v2_applies(const AttnParams& p, int D);
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
+// backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
+hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
+hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
 // bf16 kernel for at most 32 query rows per (b, h), split along the keys
 bool attn_decode_applies(const AttnParams& p, int D);
 hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s);

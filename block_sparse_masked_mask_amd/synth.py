@@ -20,7 +20,7 @@ import torch
 
 CHUNK = 1 << 22
 
-TID_Q, TID_K, TID_V, TID_BIAS, TID_PADLEN, TID_MASK = 1, 2, 3, 4, 5, 6
+TID_Q, TID_K, TID_V, TID_BIAS, TID_PADLEN, TID_MASK, TID_DOUT = 1, 2, 3, 4, 5, 6, 7
 
 
 def normal(shape, seed, tensor_id, scale=1.0):

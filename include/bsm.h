@@ -192,6 +192,49 @@ int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred,
 int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* args,
                     hipStream_t stream);
 
+/* Arguments of masked_attn_bwd: the forward's inputs, its output O and LSE,
+ * the incoming gradient dL/dO, and the gradient outputs. */
+typedef struct {
+  bsm_tensor4 q, k, v;       /* as in bsm_attn_args */
+  bsm_tensor4 o, dout;       /* forward output and dL/dO, q's dtype, (B, Sq, H, D) */
+  const float* lse;          /* forward LSE, float (B, H, Sq) contiguous */
+  bsm_tensor4 dq;            /* output, q's dtype, (B, Sq, H, D) */
+  bsm_tensor4 dk, dv;        /* outputs, q's dtype, (B, Sk, KVH, D) */
+  float softmax_scale;       /* as given to the forward; <= 0 selects 1 / sqrt(D) */
+  int32_t reserved;          /* must be 0 */
+  const bsm_dflash* pred;    /* mask source, bias and block mask exactly as given */
+  const bsm_tensor4* mask;   /*   to the forward call that produced o and lse */
+  const bsm_tensor4* bias;
+  const bsm_block_mask* bm;
+  const bsm_tensor4* dbias;  /* nullable; gradient of bias: bias's sizes and dtype, its
+                                own strides (last dim contiguous); needs bias */
+  void* workspace;           /* device scratch, 256-byte aligned, >= workspace_bytes */
+  int64_t workspace_bytes;   /*   as reported by attn_bwd_workspace_size */
+} bsm_attn_bwd_args;
+
+/* Bytes of device workspace masked_attn_bwd needs for these arguments (only
+ * geometry, bias and dbias are read): float Delta = rowsum(dO * O) for every
+ * (b, h, q), plus a float accumulator of the bias's size when dbias is
+ * requested. */
+int attn_bwd_workspace_size(const bsm_geom* geom, const bsm_attn_bwd_args* args,
+                            int64_t* bytes);
+
+/* Masked attention backward ([FSA-190] Changes: mha_bwd; Tests: backward
+ * equivalence). With the forward's P = exp(s - LSE) on kept keys (0 on masked
+ * keys and on rows with LSE = -inf), dP = dO V^T, Delta = rowsum(dO * O) and
+ * dS = P * (dP - Delta):
+ *   dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO,
+ * dK and dV summed over the G heads of each KV group, and
+ *   dbias = dS summed over every (b, h, q) that reads the same bias element,
+ * i.e. reduced over the dims where the bias broadcasts (batch, head groups,
+ * query); dbias keys >= Sk are written as 0. Tiles are visited as in the
+ * forward (the same block mask, full tiles without a mask test); the head-group
+ * swap applies as in the forward. Every output element is written. Arithmetic
+ * is float; outputs are rounded to q's dtype (nearest even). The workspace is
+ * overwritten; dq, dk, dv and dbias must not alias any input. */
+int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* args,
+                    hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call into the library on this thread. */
 const char* bsm_last_error(void);

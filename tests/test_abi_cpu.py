@@ -48,6 +48,35 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(bsm.DFlashC) == 56
     assert ctypes.sizeof(bsm.BlockMaskC) == 64
     assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 4 * 8
+    assert ctypes.sizeof(bsm.AttnBwdArgs) == 8 * 80 + 8 + 8 + 5 * 8 + 8 + 8
+
+
+def test_struct_layouts_match_c_compiler(tmp_path):
+    """sizeof and field offsets as the C compiler lays out include/bsm.h."""
+    structs = {"bsm_tensor4": bsm.Tensor4, "bsm_dflash": bsm.DFlashC,
+               "bsm_block_mask": bsm.BlockMaskC, "bsm_geom": bsm.Geom,
+               "bsm_attn_args": bsm.AttnArgs, "bsm_attn_bwd_args": bsm.AttnBwdArgs}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "bsm.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("no C compiler for the header: " + r.stderr[:200])
+    got = dict(ln.rsplit(" ", 1) for ln in
+               subprocess.run([str(exe)], capture_output=True, text=True, check=True)
+               .stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[f"{cname} sizeof"]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname} {f}"]) == getattr(py, f).offset, (cname, f)
 
 
 def test_resolve_is_causal_table(L):
@@ -195,3 +224,56 @@ def test_topk_validation(L):
     bad = _t4((2, 4, 1, 8064), bsm.BSM_BOOL)
     st = L.dynamic_topk_mask(ctypes.byref(bad), None, 8000, 10, 1 << 21, None)
     assert st == bsm.BSM_E_DTYPE
+
+
+def _bwd_args(geom, dtype=bsm.BSM_BF16):
+    B, H, KVH, Sq, Sk, D = geom
+    a = bsm.AttnBwdArgs()
+    for name in ("q", "o", "dout", "dq"):
+        setattr(a, name, _t4((B, Sq, H, D), dtype))
+    for name in ("k", "v", "dk", "dv"):
+        setattr(a, name, _t4((B, Sk, KVH, D), dtype))
+    a.lse = 1 << 21
+    return a
+
+
+def _bwd(L, geom, a, ws=None):
+    g = bsm.Geom(*geom)
+    need = ctypes.c_int64(0)
+    assert L.attn_bwd_workspace_size(ctypes.byref(g), ctypes.byref(a), ctypes.byref(need)) == 0
+    if ws is None:
+        a.workspace, a.workspace_bytes = 1 << 24, need.value
+    return L.masked_attn_bwd(ctypes.byref(g), ctypes.byref(a), None), need.value
+
+
+def test_attention_bwd_validation(L):
+    geom = (2, 16, 4, 64, 300, 128)
+    a = _bwd_args(geom)
+    a.dk = _t4((2, 300, 16, 128), bsm.BSM_BF16)        # dk with H heads instead of KVH
+    assert _bwd(L, geom, a)[0] == bsm.BSM_E_SHAPE
+    a = _bwd_args(geom)
+    a.lse = None
+    assert _bwd(L, geom, a)[0] == bsm.BSM_E_ARG
+    geom96 = (2, 16, 4, 64, 300, 96)
+    assert _bwd(L, geom96, _bwd_args(geom96))[0] == bsm.BSM_E_UNSUPPORTED
+    a = _bwd_args(geom)
+    db = _t4((2, 4, 1, 384), bsm.BSM_BF16)
+    a.dbias = ctypes.pointer(db)                       # dbias without bias
+    assert _bwd(L, geom, a)[0] == bsm.BSM_E_ARG
+    a = _bwd_args(geom)
+    bias = _t4((2, 4, 1, 384), bsm.BSM_BF16)
+    dbias = _t4((2, 4, 1, 384), bsm.BSM_BF16)
+    a.bias, a.dbias = ctypes.pointer(bias), ctypes.pointer(dbias)
+    g = bsm.Geom(*geom)
+    need = ctypes.c_int64(0)
+    assert L.attn_bwd_workspace_size(ctypes.byref(g), ctypes.byref(a), ctypes.byref(need)) == 0
+    # Delta (2*16*64 floats) + the bias accumulator (2*4*384 floats), 256-byte parts
+    assert need.value == 2 * 16 * 64 * 4 + 2 * 4 * 384 * 4
+    a.workspace, a.workspace_bytes = 1 << 24, need.value - 4
+    assert L.masked_attn_bwd(ctypes.byref(g), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    assert b"workspace" in L.bsm_last_error()
+    a.workspace, a.workspace_bytes = (1 << 24) + 16, need.value
+    assert L.masked_attn_bwd(ctypes.byref(g), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    wrong = _t4((2, 4, 1, 384), bsm.BSM_F32)           # dbias dtype != bias dtype
+    a.dbias = ctypes.pointer(wrong)
+    assert _bwd(L, geom, a)[0] == bsm.BSM_E_DTYPE
