@@ -169,9 +169,34 @@ def _time_ms(fn, reps=10):
     return e0.elapsed_time(e1) / reps
 
 
+def measure_backward():
+    """Backward of the DFlash training shape, both layers: dQ/dK/dV from the
+    forward's O and LSE. Counted flops: 2.5x the forward's (the five products
+    QK^T, dO V^T, P^T dO, dS^T Q, dS K over the kept tiles)."""
+    out = {}
+    cfg = synth.CONFIGS["dflash_train_bf16"]
+    for lay in cfg["layers"]:
+        d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
+                       is_causal=lay["is_causal"], layer_type=lay["layer_type"],
+                       sliding_window=lay["window"])
+        q, k, v = [t.cuda() for t in synth.qkv(cfg["B"], d.Sq, d.Sk, cfg["H"], cfg["KVH"],
+                                               cfg["D"], "bf16", seed=0, scale=cfg["qkv_scale"])]
+        geom = bsm.geometry_of(q, k)
+        bm = bsm.build_block_mask(geom, pred=d)
+        o, lse = bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, return_lse=True)
+        do = synth.normal_tensor(tuple(q.shape), 0, synth.TID_DOUT, "bf16").cuda()
+        ms = _time_ms(lambda: bsm.masked_attn_bwd(q, k, v, o, do, lse, pred=d, block_mask=bm),
+                      reps=3)
+        fl = 2.5 * counted_flops(bm, geom)
+        out[f"attn_bwd/dflash_train_bf16/{lay['name']}_ms"] = ms
+        out[f"attn_bwd/dflash_train_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+        del q, k, v, o, do
+    return out
+
+
 def measure_components():
     """Per-kernel times of the other workloads (parity cases, not the headline)."""
-    out = {}
+    out = measure_backward()
     # DFlash block masks from the predicate (integer work, output only)
     for name in ("dflash_train_bf16", "long_dflash_bf16"):
         cfg = synth.CONFIGS[name]

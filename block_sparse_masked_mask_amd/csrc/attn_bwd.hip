@@ -257,6 +257,7 @@ hipError_t launch_typed(const AttnBwdParams& p, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
                      blk, 0, s, p);
+  if (sizeof(T) == 2 && attn_bwd_mfma_applies(p, D)) return launch_attn_bwd_mfma(p, s);
   hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), blk,
                      0, s, p);
   if (keys > 0)

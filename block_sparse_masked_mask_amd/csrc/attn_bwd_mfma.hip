@@ -1,0 +1,422 @@
+// Masked attention backward on the bf16 matrix cores (gfx950), D = 128, for
+// calls without bias and without a dense mask (no mask, or the DFlash
+// predicate): the training path of the DFlash layers.
+//
+// Same gradients as the generic kernels (attn_bwd.hip; flash-sparse-attention
+// PR #190, Changes: mha_bwd): P = exp(s - LSE) on kept keys, dS = P (dP - Delta)
+// with dP = dO V^T and Delta = rowsum(dO * O); dQ = scale dS K, dK = scale dS^T Q,
+// dV = P^T dO, all products on v_mfma_f32_32x32x16_bf16 with float accumulation
+// and P, dS rounded to bf16 as MFMA operands.
+//
+//  * dQ: one workgroup per (b, h, query tile), 4 waves of 32 rows; K and V tiles
+//    go through LDS. Per 32-key chunk: S^T = K Q^T and dP^T = V dO^T with Q and
+//    dO rows held in registers, then dQ^T += K^T dS^T with K^T from transposed
+//    LDS reads. Keys are permuted (bits 2 and 3 of the MFMA row swapped) so that
+//    a lane's accumulators hold 8 consecutive keys of its row: the B-operand
+//    layout of the dQ product, and the layout the row's interval test uses.
+//  * dK / dV: one workgroup per (b, KV head, key tile), 4 waves of 32 keys,
+//    visiting every (head of the group, query tile) whose tile is not empty.
+//    Per 32-row block: S = Q K^T and dP = dO V^T with the wave's K and V rows
+//    held in registers and query rows permuted the same way, then
+//    dV^T += dO^T P and dK^T += Q^T dS with transposed LDS reads of dO and Q.
+//    Partial tiles of the predicate use a keep-bit table of the query tile
+//    built in LDS (one 64-key word per row and half tile).
+#include <math.h>
+
+#include "attn_common.h"
+#include "attn_pipe.h"
+#include "bsm_internal.h"
+#include "dflash_rows.h"
+
+namespace bsm {
+namespace {
+
+using namespace pipe;
+
+constexpr int kD = 128;
+constexpr int kNS = kD / 16;    // 16-wide d steps
+constexpr int kNDC = kD / 32;   // 32-wide d chunks
+constexpr int kRowB = kD * 2;   // bytes per bf16 row
+constexpr int kThreads = 256;
+
+// 128 x 128 bf16 tile in LDS, rows swizzled in 16-byte chunks like the forward's
+// K tiles (conflict-free row reads).
+struct Tile {
+  __bf16 e[kTile * kD];
+};
+
+// Cooperative copy of rows r0 .. r0+127 of a (rows, stride) bf16 matrix into t;
+// rows >= nrows are zero.
+__device__ inline void load_tile(Tile& t, const __bf16* base, int64_t stride, int r0, int nrows,
+                                 int tid) {
+#pragma unroll
+  for (int j = 0; j < kTile * kD / 8 / kThreads; ++j) {
+    const int f = j * kThreads + tid;
+    const int r = f / (kD / 8);
+    const int c = f % (kD / 8);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < nrows)
+      v = *reinterpret_cast<const uint4*>(base + (int64_t)(r0 + r) * stride + c * 8);
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(t.e) + r * kRowB +
+                              ((c ^ swz_k<kD>(r)) * 16)) = v;
+  }
+}
+
+// Row operand (A of a 32x32x16 MFMA): rows rb*32 + perm_row(n), d-step s.
+__device__ inline bf16x8 row_op(const Tile& t, int rb, int s, int lane) {
+  const int row = rb * 32 + perm_row(lane & 31);
+  const int hh = lane >> 5;
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(t.e) + row * kRowB +
+                                          (((2 * s + hh) ^ swz_k<kD>(row)) * 16));
+}
+
+// Transposed operand (A of a 32x32x16 MFMA over the tile's rows): d = 32 dc +
+// (lane % 32), rows kb .. kb+15 of the tile with lane holding 8 consecutive
+// rows (two 4-row transposed reads).
+__device__ inline bf16x8 col_op(const Tile& t, int dc, int kb, int lane) {
+  const int blk = lane >> 4;
+  const int e4 = (lane >> 2) & 3;
+  const int g4 = lane & 3;
+  const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+  const int row0 = kb + 8 * (blk >> 1) + e4;
+  const int row1 = row0 + 4;
+  const char* b = reinterpret_cast<const char*>(t.e);
+  const char* a0 = b + row0 * kRowB + ((chunk ^ swz_k<kD>(row0)) * 16) + (g4 & 1) * 8;
+  const char* a1 = b + row1 * kRowB + ((chunk ^ swz_k<kD>(row1)) * 16) + (g4 & 1) * 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+  return r;
+}
+
+// ---------------------------------------------------------------- dQ
+
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
+  const AttnParams& f = P.f;
+  __shared__ __align__(1024) Tile sk;
+  __shared__ __align__(1024) Tile sv;
+  const int qt = blockIdx.x % f.nQ;
+  const int bh = blockIdx.x / f.nQ;
+  const int h = bh % f.H;
+  const int b = bh / f.H;
+  const int kvh = h / f.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int q = qt * kTile + 32 * w + n;
+  const bool qvalid = q < f.Sq;
+
+  // this lane's row: Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T)
+  bf16x8 qf[kNS], df[kNS];
+  {
+    const __bf16* qr = reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb +
+                       (int64_t)q * f.q_sq + (int64_t)h * f.q_sh;
+    const __bf16* dr = reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb +
+                       (int64_t)q * P.do_sq + (int64_t)h * P.do_sh;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hh) : bf16x8{};
+      df[s] = qvalid ? *reinterpret_cast<const bf16x8*>(dr + 16 * s + 8 * hh) : bf16x8{};
+    }
+  }
+  const float lse2 =
+      qvalid ? f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
+                   kLog2e
+             : -INFINITY;
+  const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
+  const bool live = lse2 != -INFINITY;  // rows with no kept key have zero gradients
+  RowIv32 iv{0, 0, 0, 0};
+  if (f.mask_kind == 1) {
+    const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
+  }
+  f32x16 dq[kNDC];
+#pragma unroll
+  for (int i = 0; i < kNDC; ++i) dq[i] = f32x16{};
+
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb +
+                        (int64_t)kvh * f.k_sh;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb +
+                        (int64_t)kvh * f.v_sh;
+  TileList tl;
+  tl.init(f, b, h, qt);
+  const int ntiles = tl.count();
+  for (int it = 0; it < ntiles; ++it) {
+    bool full;
+    const int kt = tl.tile(it, full);
+    const int k0 = kt * kTile;
+    __syncthreads();  // previous tile's readers are done
+    load_tile(sk, kbase, f.k_sk, k0, f.Sk, tid);
+    load_tile(sv, vbase, f.v_sk, k0, f.Sk, tid);
+    __syncthreads();
+    const bool test = !full || k0 + kTile > f.Sk || !qvalid;
+#pragma unroll
+    for (int c = 0; c < kTile / 32; ++c) {
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sk, c, s, lane), qf[s], st, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sv, c, s, lane), df[s], dpt, 0, 0,
+                                                      0);
+      }
+      // lane: row q, keys k0 + 32 c + 16 sb + 8 hh + e (e = 0..7) for value 8 sb + e
+      float ds[16];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kb = k0 + 32 * c + 16 * sb + 8 * hh;
+        uint32_t bits = 0xFFu;
+        if (test) {
+          // partial tiles of the predicate test the row's intervals; keys past
+          // Sk and rows past Sq keep nothing
+          if (!full && f.mask_kind == 1)
+            bits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
+          bits &= range_bits(0, f.Sk, kb);
+          if (!qvalid) bits = 0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * sb + e;
+          const float pr = (live && ((bits >> e) & 1u))
+                               ? __builtin_amdgcn_exp2f(st[u] * f.scale_log2 - lse2)
+                               : 0.f;
+          ds[u] = pr * (dpt[u] - delta);
+        }
+      }
+      const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+#pragma unroll
+      for (int dc = 0; dc < kNDC; ++dc) {
+        dq[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sk, dc, 32 * c, lane), d0, dq[dc],
+                                                         0, 0, 0);
+        dq[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sk, dc, 32 * c + 16, lane), d1,
+                                                         dq[dc], 0, 0, 0);
+      }
+    }
+  }
+  // dQ^T accumulators: lane holds d = 32 dc + 8 (r / 4) + 4 hh + r % 4 of row q
+  if (qvalid) {
+    __bf16* out = reinterpret_cast<__bf16*>(P.dq) + (int64_t)b * P.dq_sb + (int64_t)q * P.dq_sq +
+                  (int64_t)h * P.dq_sh;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dq[dc][4 * g + e] * P.scale);
+        *reinterpret_cast<bf16x4*>(out + dc * 32 + 8 * g + 4 * hh) = v4;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK / dV
+
+__device__ inline int tile_class_of(const AttnParams& f, int b, int h, int qt, int kt) {
+  if (!f.has_bm) return f.mask_kind == 0 ? 2 : 1;
+  const BlockMaskView& m = f.bm;
+  const int64_t mb = m.Bm == 1 ? 0 : b;
+  const int64_t mh = head_index(m.h_mode, h, f.G);
+  const int64_t mq = m.nQm == 1 ? 0 : qt;
+  const int64_t r = (mb * m.Hm + mh) * m.nQm + mq;
+  auto find = [&](const int32_t* idx, int cnt) {
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int v = idx[mid];
+      if (v == kt) return true;
+      if (v < kt) lo = mid + 1; else hi = mid;
+    }
+    return false;
+  };
+  if (find(m.full_idx + r * m.nK, m.full_num[r])) return 2;
+  if (find(m.kv_idx + r * m.nK, m.kv_num[r])) return 1;
+  return 0;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) {
+  const AttnParams& f = P.f;
+  __shared__ __align__(1024) Tile sq;
+  __shared__ __align__(1024) Tile sdo;
+  __shared__ float s_lse2[kTile];
+  __shared__ float s_delta[kTile];
+  __shared__ uint64_t s_keep[kTile][2];  // keep bits: row, 64-key half
+  // key tile major, lowest key tile first: under causal-like masks the low key
+  // tiles are seen by the most query tiles, so the longest work items start first
+  const int kt = blockIdx.x / (f.B * f.KVH);
+  const int bk = blockIdx.x % (f.B * f.KVH);
+  const int kvh = bk % f.KVH;
+  const int b = bk / f.KVH;
+  const int k0 = kt * kTile;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int key = k0 + 32 * w + n;  // this lane's key (column of S, dP, P, dS)
+  const bool kvalid = key < f.Sk;
+
+  // the lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[kNS], vf[kNS];
+  {
+    const __bf16* kr = reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb +
+                       (int64_t)key * f.k_sk + (int64_t)kvh * f.k_sh;
+    const __bf16* vr = reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb +
+                       (int64_t)key * f.v_sk + (int64_t)kvh * f.v_sh;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(kr + 16 * s + 8 * hh) : bf16x8{};
+      vf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(vr + 16 * s + 8 * hh) : bf16x8{};
+    }
+  }
+  f32x16 dk[kNDC], dv[kNDC];
+#pragma unroll
+  for (int i = 0; i < kNDC; ++i) dk[i] = dv[i] = f32x16{};
+
+  for (int g = 0; g < f.G; ++g) {
+    const int h = kvh * f.G + g;
+    const __bf16* qbase = reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb +
+                          (int64_t)h * f.q_sh;
+    const __bf16* dbase = reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb +
+                          (int64_t)h * P.do_sh;
+    for (int qt = 0; qt < f.nQ; ++qt) {
+      const int cls = __builtin_amdgcn_readfirstlane(tile_class_of(f, b, h, qt, kt));
+      if (cls == 0) continue;
+      const int q0 = qt * kTile;
+      __syncthreads();  // previous readers are done
+      load_tile(sq, qbase, f.q_sq, q0, f.Sq, tid);
+      load_tile(sdo, dbase, P.do_sq, q0, f.Sq, tid);
+      if (tid < kTile) {
+        const int q = q0 + tid;
+        float l2 = -INFINITY, dl = 0.f;
+        if (q < f.Sq) {
+          l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
+               kLog2e;
+          dl = P.delta[((int64_t)b * f.H + h) * f.Sq + q];
+        }
+        s_lse2[tid] = l2;
+        s_delta[tid] = dl;
+      }
+      // keep bits of this (query tile, key tile): row tid / 2, keys of half tid % 2
+      const bool test = cls == 1 || k0 + kTile > f.Sk;
+      if (test) {
+        const int r = tid >> 1, half = tid & 1;
+        const int q = q0 + r;
+        uint64_t bits = 0;
+        if (q < f.Sq) {
+          int lo1 = 0, hi1 = f.Sk, lo2 = 0, hi2 = 0;
+          if (cls == 1 && f.mask_kind == 1) {
+            const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+            lo1 = (int)v.lo1;
+            hi1 = (int)v.hi1;
+            lo2 = (int)v.lo2;
+            hi2 = (int)v.hi2;
+          }
+          hi1 = hi1 < f.Sk ? hi1 : f.Sk;
+          hi2 = hi2 < f.Sk ? hi2 : f.Sk;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int kb = k0 + 64 * half + 8 * j;
+            bits |= (uint64_t)(range_bits(lo1, hi1, kb) | range_bits(lo2, hi2, kb)) << (8 * j);
+          }
+        }
+        s_keep[r][half] = bits;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < kTile / 32; ++rb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ds_ = 0; ds_ < kNS; ++ds_) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sq, rb, ds_, lane), kf[ds_], s, 0, 0,
+                                                      0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sdo, rb, ds_, lane), vf[ds_], dp, 0,
+                                                       0, 0);
+        }
+        // lane: key, rows rb*32 + 16 st + 8 hh + e for value u = 8 st + e
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = rb * 32 + 16 * st + 8 * hh;
+          const float4 la = *reinterpret_cast<const float4*>(&s_lse2[r0]);
+          const float4 lb = *reinterpret_cast<const float4*>(&s_lse2[r0 + 4]);
+          const float4 da = *reinterpret_cast<const float4*>(&s_delta[r0]);
+          const float4 db = *reinterpret_cast<const float4*>(&s_delta[r0 + 4]);
+          const float l2[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+          const float dl[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 8 * st + e;
+            bool keep = l2[e] != -INFINITY;
+            if (test) {
+              const int kk = 32 * w + n;  // key within the tile
+              keep = keep && ((s_keep[r0 + e][kk >> 6] >> (kk & 63)) & 1u);
+            }
+            const float pr = keep ? __builtin_amdgcn_exp2f(s[u] * f.scale_log2 - l2[e]) : 0.f;
+            pv[u] = pr;
+            dsv[u] = pr * (dp[u] - dl[e]);
+          }
+        }
+        const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
+        const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+#pragma unroll
+        for (int dc = 0; dc < kNDC; ++dc) {
+          dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sdo, dc, rb * 32, lane), p0,
+                                                           dv[dc], 0, 0, 0);
+          dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sdo, dc, rb * 32 + 16, lane),
+                                                           p1, dv[dc], 0, 0, 0);
+          dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sq, dc, rb * 32, lane), s0,
+                                                           dk[dc], 0, 0, 0);
+          dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sq, dc, rb * 32 + 16, lane), s1,
+                                                           dk[dc], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // dK^T / dV^T accumulators: lane holds d = 32 dc + 8 (r / 4) + 4 hh + r % 4 of its key
+  if (kvalid) {
+    __bf16* ko = reinterpret_cast<__bf16*>(P.dk) + (int64_t)b * P.dk_sb + (int64_t)key * P.dk_sk +
+                 (int64_t)kvh * P.dk_sh;
+    __bf16* vo = reinterpret_cast<__bf16*>(P.dv) + (int64_t)b * P.dv_sb + (int64_t)key * P.dv_sk +
+                 (int64_t)kvh * P.dv_sh;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 a, c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (__bf16)(dk[dc][4 * g + e] * P.scale);
+          c[e] = (__bf16)dv[dc][4 * g + e];
+        }
+        *reinterpret_cast<bf16x4*>(ko + dc * 32 + 8 * g + 4 * hh) = a;
+        *reinterpret_cast<bf16x4*>(vo + dc * 32 + 8 * g + 4 * hh) = c;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D) {
+  return D == kD && !p.f.has_bias && p.f.mask_kind != 2 && !p.dbias_acc;
+}
+
+hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
+  const AttnParams& f = p.f;
+  const int64_t nq = (int64_t)f.B * f.H * f.nQ;
+  const int64_t nk = (int64_t)f.B * f.KVH * f.nK;
+  if (nq > 0) hipLaunchKernelGGL(k_bwd_dq_mfma, dim3(nq), dim3(kThreads), 0, s, p);
+  if (nk > 0) hipLaunchKernelGGL(k_bwd_dkdv_mfma, dim3(nk), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

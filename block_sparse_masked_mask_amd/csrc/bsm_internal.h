@@ -134,6 +134,9 @@ hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
 // backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
 hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
+// bf16 matrix-core dQ and dK / dV (D = 128, no bias, no dense mask)
+bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D);
+hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s);
 hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
 // bf16 kernel for at most 32 query rows per (b, h), split along the keys
 bool attn_decode_applies(const AttnParams& p, int D);
