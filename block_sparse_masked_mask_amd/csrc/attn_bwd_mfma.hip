@@ -62,31 +62,46 @@ __device__ inline void load_tile(Tile& t, const __bf16* base, int64_t stride, in
   }
 }
 
+// 16-byte chunk swizzle of a tile row: the K-tile one, or (VSW) the V-tile one
+// the LDS-DMA loader applies to its second tensor.
+template <bool VSW>
+__device__ inline int swz(int r) {
+  return VSW ? swz_v<kD>(r) : swz_k<kD>(r);
+}
+
 // Row operand (A of a 32x32x16 MFMA): rows rb*32 + perm_row(n), d-step s.
-__device__ inline bf16x8 row_op(const Tile& t, int rb, int s, int lane) {
+template <bool VSW = false>
+__device__ inline bf16x8 row_op(const __bf16* t, int rb, int s, int lane) {
   const int row = rb * 32 + perm_row(lane & 31);
   const int hh = lane >> 5;
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(t.e) + row * kRowB +
-                                          (((2 * s + hh) ^ swz_k<kD>(row)) * 16));
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(t) + row * kRowB +
+                                          (((2 * s + hh) ^ swz<VSW>(row)) * 16));
+}
+__device__ inline bf16x8 row_op(const Tile& t, int rb, int s, int lane) {
+  return row_op<false>(t.e, rb, s, lane);
 }
 
 // Transposed operand (A of a 32x32x16 MFMA over the tile's rows): d = 32 dc +
 // (lane % 32), rows kb .. kb+15 of the tile with lane holding 8 consecutive
 // rows (two 4-row transposed reads).
-__device__ inline bf16x8 col_op(const Tile& t, int dc, int kb, int lane) {
+template <bool VSW = false>
+__device__ inline bf16x8 col_op(const __bf16* t, int dc, int kb, int lane) {
   const int blk = lane >> 4;
   const int e4 = (lane >> 2) & 3;
   const int g4 = lane & 3;
   const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
   const int row0 = kb + 8 * (blk >> 1) + e4;
   const int row1 = row0 + 4;
-  const char* b = reinterpret_cast<const char*>(t.e);
-  const char* a0 = b + row0 * kRowB + ((chunk ^ swz_k<kD>(row0)) * 16) + (g4 & 1) * 8;
-  const char* a1 = b + row1 * kRowB + ((chunk ^ swz_k<kD>(row1)) * 16) + (g4 & 1) * 8;
+  const char* b = reinterpret_cast<const char*>(t);
+  const char* a0 = b + row0 * kRowB + ((chunk ^ swz<VSW>(row0)) * 16) + (g4 & 1) * 8;
+  const char* a1 = b + row1 * kRowB + ((chunk ^ swz<VSW>(row1)) * 16) + (g4 & 1) * 8;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
   return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
                                  0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ inline bf16x8 col_op(const Tile& t, int dc, int kb, int lane) {
+  return col_op<false>(t.e, dc, kb, lane);
 }
 
 __device__ inline bf16x8 pack8(const float* x) {
@@ -244,11 +259,13 @@ __device__ inline int tile_class_of(const AttnParams& f, int b, int h, int qt, i
 
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) {
   const AttnParams& f = P.f;
-  __shared__ __align__(1024) Tile sq;
-  __shared__ __align__(1024) Tile sdo;
-  __shared__ float s_lse2[kTile];
-  __shared__ float s_delta[kTile];
-  __shared__ uint64_t s_keep[kTile][2];  // keep bits: row, 64-key half
+  // two slots: Q tile (.k) and dO tile (.v) of a visited (head, query tile), with
+  // its rows' LSE (log2 units), Delta and the key test's keep bits; the loads of
+  // the next visit go out while the current one is computed
+  __shared__ __align__(1024) Tiles<kD> buf[2];
+  __shared__ float s_lse2[2][kTile];
+  __shared__ float s_delta[2][kTile];
+  __shared__ uint64_t s_keep[2][kTile][2];  // keep bits: row, 64-key half
   // key tile major, lowest key tile first: under causal-like masks the low key
   // tiles are seen by the most query tiles, so the longest work items start first
   const int kt = blockIdx.x / (f.B * f.KVH);
@@ -263,6 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   const int hh = lane >> 5;
   const int key = k0 + 32 * w + n;  // this lane's key (column of S, dP, P, dS)
   const bool kvalid = key < f.Sk;
+  const bool test_k = k0 + kTile > f.Sk;
 
   // the lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
   bf16x8 kf[kNS], vf[kNS];
@@ -281,105 +299,124 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
 #pragma unroll
   for (int i = 0; i < kNDC; ++i) dk[i] = dv[i] = f32x16{};
 
-  for (int g = 0; g < f.G; ++g) {
-    const int h = kvh * f.G + g;
-    const __bf16* qbase = reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb +
-                          (int64_t)h * f.q_sh;
-    const __bf16* dbase = reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb +
-                          (int64_t)h * P.do_sh;
-    for (int qt = 0; qt < f.nQ; ++qt) {
-      const int cls = __builtin_amdgcn_readfirstlane(tile_class_of(f, b, h, qt, kt));
-      if (cls == 0) continue;
-      const int q0 = qt * kTile;
-      __syncthreads();  // previous readers are done
-      load_tile(sq, qbase, f.q_sq, q0, f.Sq, tid);
-      load_tile(sdo, dbase, P.do_sq, q0, f.Sq, tid);
-      if (tid < kTile) {
-        const int q = q0 + tid;
-        float l2 = -INFINITY, dl = 0.f;
-        if (q < f.Sq) {
-          l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
-               kLog2e;
-          dl = P.delta[((int64_t)b * f.H + h) * f.Sq + q];
-        }
-        s_lse2[tid] = l2;
-        s_delta[tid] = dl;
+  // visits: positions pos = g * nQ + qt whose tile (qt, kt) of head g is not empty
+  const int end = f.G * f.nQ;
+  auto next_visit = [&](int pos, int& cls) {
+    for (; pos < end; ++pos) {
+      cls = __builtin_amdgcn_readfirstlane(
+          tile_class_of(f, b, kvh * f.G + pos / f.nQ, pos % f.nQ, kt));
+      if (cls != 0) return pos;
+    }
+    return end;
+  };
+  // row data of visit pos into slot sl, then its tile loads (after the row
+  // data's own loads, so no later wait for them also waits for the tiles)
+  auto prepare = [&](int sl, int pos, int cls) {
+    const int h = kvh * f.G + pos / f.nQ;
+    const int q0 = (pos % f.nQ) * kTile;
+    if (tid < kTile) {
+      const int q = q0 + tid;
+      float l2 = -INFINITY, dl = 0.f;
+      if (q < f.Sq) {
+        l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] * kLog2e;
+        dl = P.delta[((int64_t)b * f.H + h) * f.Sq + q];
       }
-      // keep bits of this (query tile, key tile): row tid / 2, keys of half tid % 2
-      const bool test = cls == 1 || k0 + kTile > f.Sk;
-      if (test) {
-        const int r = tid >> 1, half = tid & 1;
-        const int q = q0 + r;
-        uint64_t bits = 0;
-        if (q < f.Sq) {
-          int lo1 = 0, hi1 = f.Sk, lo2 = 0, hi2 = 0;
-          if (cls == 1 && f.mask_kind == 1) {
-            const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
-            lo1 = (int)v.lo1;
-            hi1 = (int)v.hi1;
-            lo2 = (int)v.lo2;
-            hi2 = (int)v.hi2;
-          }
-          hi1 = hi1 < f.Sk ? hi1 : f.Sk;
-          hi2 = hi2 < f.Sk ? hi2 : f.Sk;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int kb = k0 + 64 * half + 8 * j;
-            bits |= (uint64_t)(range_bits(lo1, hi1, kb) | range_bits(lo2, hi2, kb)) << (8 * j);
-          }
+      s_lse2[sl][tid] = l2;
+      s_delta[sl][tid] = dl;
+    }
+    if (cls == 1 || test_k) {  // keep bits: row tid / 2, keys of half tid % 2
+      const int r = tid >> 1, half = tid & 1;
+      const int q = q0 + r;
+      uint64_t bits = 0;
+      if (q < f.Sq) {
+        int lo1 = 0, hi1 = f.Sk, lo2 = 0, hi2 = 0;
+        if (cls == 1 && f.mask_kind == 1) {
+          const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+          lo1 = (int)v.lo1;
+          hi1 = (int)v.hi1;
+          lo2 = (int)v.lo2;
+          hi2 = (int)v.hi2;
         }
-        s_keep[r][half] = bits;
+        hi1 = hi1 < f.Sk ? hi1 : f.Sk;
+        hi2 = hi2 < f.Sk ? hi2 : f.Sk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kb = k0 + 64 * half + 8 * j;
+          bits |= (uint64_t)(range_bits(lo1, hi1, kb) | range_bits(lo2, hi2, kb)) << (8 * j);
+        }
       }
-      __syncthreads();
+      s_keep[sl][r][half] = bits;
+    }
+    Loader<kD, 2> ld;
+    ld.init(reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb + (int64_t)h * f.q_sh,
+            reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb + (int64_t)h * P.do_sh,
+            f.q_sq, P.do_sq, f.Sq, w, lane);
+    ld.issue(buf[sl], pos % f.nQ, w);
+  };
+
+  int cls = 0;
+  int pos = next_visit(0, cls);
+  if (pos < end) prepare(0, pos, cls);
+  for (int it = 0; pos < end; ++it) {
+    const int sl = it & 1;
+    wait_vmcnt<0>();   // this visit's tiles (this thread's share)
+    __syncthreads();   // everyone's share, and the row data; slot sl ^ 1 is free
+    int ncls = 0;
+    const int npos = next_visit(pos + 1, ncls);
+    if (npos < end) prepare(sl ^ 1, npos, ncls);
+    const bool test = cls == 1 || test_k;
+    const __bf16* tq = buf[sl].k;
+    const __bf16* tdo = buf[sl].v;
 #pragma unroll
-      for (int rb = 0; rb < kTile / 32; ++rb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int rb = 0; rb < kTile / 32; ++rb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ds_ = 0; ds_ < kNS; ++ds_) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sq, rb, ds_, lane), kf[ds_], s, 0, 0,
-                                                      0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op(sdo, rb, ds_, lane), vf[ds_], dp, 0,
-                                                       0, 0);
-        }
-        // lane: key, rows rb*32 + 16 st + 8 hh + e for value u = 8 st + e
-        float pv[16], dsv[16];
+      for (int ds_ = 0; ds_ < kNS; ++ds_) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<false>(tq, rb, ds_, lane), kf[ds_], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<true>(tdo, rb, ds_, lane), vf[ds_],
+                                                     dp, 0, 0, 0);
+      }
+      // lane: key, rows rb*32 + 16 st + 8 hh + e for value u = 8 st + e
+      float pv[16], dsv[16];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = rb * 32 + 16 * st + 8 * hh;
-          const float4 la = *reinterpret_cast<const float4*>(&s_lse2[r0]);
-          const float4 lb = *reinterpret_cast<const float4*>(&s_lse2[r0 + 4]);
-          const float4 da = *reinterpret_cast<const float4*>(&s_delta[r0]);
-          const float4 db = *reinterpret_cast<const float4*>(&s_delta[r0 + 4]);
-          const float l2[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-          const float dl[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+      for (int st = 0; st < 2; ++st) {
+        const int r0 = rb * 32 + 16 * st + 8 * hh;
+        const float4 la = *reinterpret_cast<const float4*>(&s_lse2[sl][r0]);
+        const float4 lb = *reinterpret_cast<const float4*>(&s_lse2[sl][r0 + 4]);
+        const float4 da = *reinterpret_cast<const float4*>(&s_delta[sl][r0]);
+        const float4 db = *reinterpret_cast<const float4*>(&s_delta[sl][r0 + 4]);
+        const float l2[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const float dl[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int u = 8 * st + e;
-            bool keep = l2[e] != -INFINITY;
-            if (test) {
-              const int kk = 32 * w + n;  // key within the tile
-              keep = keep && ((s_keep[r0 + e][kk >> 6] >> (kk & 63)) & 1u);
-            }
-            const float pr = keep ? __builtin_amdgcn_exp2f(s[u] * f.scale_log2 - l2[e]) : 0.f;
-            pv[u] = pr;
-            dsv[u] = pr * (dp[u] - dl[e]);
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * st + e;
+          bool keep = l2[e] != -INFINITY;
+          if (test) {
+            const int kk = 32 * w + n;  // key within the tile
+            keep = keep && ((s_keep[sl][r0 + e][kk >> 6] >> (kk & 63)) & 1u);
           }
+          const float pr = keep ? __builtin_amdgcn_exp2f(s[u] * f.scale_log2 - l2[e]) : 0.f;
+          pv[u] = pr;
+          dsv[u] = pr * (dp[u] - dl[e]);
         }
-        const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
-        const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+      }
+      const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
+      const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
 #pragma unroll
-        for (int dc = 0; dc < kNDC; ++dc) {
-          dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sdo, dc, rb * 32, lane), p0,
-                                                           dv[dc], 0, 0, 0);
-          dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sdo, dc, rb * 32 + 16, lane),
-                                                           p1, dv[dc], 0, 0, 0);
-          dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sq, dc, rb * 32, lane), s0,
-                                                           dk[dc], 0, 0, 0);
-          dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(sq, dc, rb * 32 + 16, lane), s1,
-                                                           dk[dc], 0, 0, 0);
-        }
+      for (int dc = 0; dc < kNDC; ++dc) {
+        dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<true>(tdo, dc, rb * 32, lane), p0,
+                                                         dv[dc], 0, 0, 0);
+        dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<true>(tdo, dc, rb * 32 + 16, lane),
+                                                         p1, dv[dc], 0, 0, 0);
+        dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<false>(tq, dc, rb * 32, lane), s0,
+                                                         dk[dc], 0, 0, 0);
+        dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<false>(tq, dc, rb * 32 + 16, lane),
+                                                         s1, dk[dc], 0, 0, 0);
       }
     }
+    pos = npos;
+    cls = ncls;
   }
   // dK^T / dV^T accumulators: lane holds d = 32 dc + 8 (r / 4) + 4 hh + r % 4 of its key
   if (kvalid) {
@@ -407,7 +444,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
 }  // namespace
 
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D) {
-  return D == kD && !p.f.has_bias && p.f.mask_kind != 2 && !p.dbias_acc;
+  // the dK / dV kernel's tile loads use 32-bit offsets within one (b, head)
+  return D == kD && !p.f.has_bias && p.f.mask_kind != 2 && !p.dbias_acc &&
+         (int64_t)p.f.Sq * p.f.q_sq * 2 < ((int64_t)1 << 31) &&
+         (int64_t)p.f.Sq * p.do_sq * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
