@@ -50,8 +50,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "cd6e0ea75d01457a",
-                "fetch_kib": 86462.8, "write_kib": 65536.0,
+                "sha256_16": "528eb9eafb8f5910",
+                "fetch_kib": 86491.8, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -311,6 +311,8 @@ def main():
                     help="also time the other workloads' kernels (top-k, builders, attention)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the DFlash training-shape backward and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
@@ -319,6 +321,9 @@ def main():
     torch.cuda.init()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.backward_only:
+        print(json.dumps(measure_backward()), flush=True)
         return
     step = Step()
     for _ in range(args.warmup):

@@ -55,4 +55,5 @@ from .dflash import (  # noqa: F401
 from .blockmask import TILE, classify_tiles, expand_block_mask  # noqa: F401
 from .topk import finfo_min, topk_keep_mask, topk_rank_bruteforce  # noqa: F401
 from .attention import attention_rows, attention_full  # noqa: F401
+from .attention_bwd import attention_bwd, group_grads, head_grads  # noqa: F401
 from .normalize import round_multiple, normalize_premask  # noqa: F401
