@@ -43,6 +43,9 @@ Modules:
                 attention (pinned: central finite differences of the forward
                 oracle, torch autograd in float64, broadcast dbias reductions).
   normalize  -- 2D/4D pre-mask normalisation and key-length rounding.
+  keylist    -- kept-key list of a dense mask over at most 32 query rows, with
+                a bit per row (pinned: hand-worked example, round trip,
+                top-k count invariant, attention over the gathered keys).
 
 No function here is "parity unpinned" except where its docstring says so.
 """
@@ -57,3 +60,4 @@ from .topk import finfo_min, topk_keep_mask, topk_rank_bruteforce  # noqa: F401
 from .attention import attention_rows, attention_full  # noqa: F401
 from .attention_bwd import attention_bwd, group_grads, head_grads  # noqa: F401
 from .normalize import round_multiple, normalize_premask  # noqa: F401
+from .keylist import key_list, expand_key_list  # noqa: F401
