@@ -241,7 +241,16 @@ def measure_components():
     out["attn/dynamic_topk_bf16_ms"] = ms
     out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
     del q, k, v, o
-    # decode with the head-group swap: top-k, dense builder, attention (HBM-bound)
+    out.update(measure_decode())
+    return out
+
+
+def measure_decode():
+    """Decode with the head-group swap (B=64, H=32, KVH=8, Sk=16384, per-head
+    bias, top-1024): top-k, then either the dense block-mask builder and the
+    tile-visiting kernel, or the key-list builder and the key-gather kernel.
+    GB/s counts the bytes each path must move: all K/V rows, or the listed ones."""
+    out = {}
     cfg = synth.CONFIGS["decode_swap_bf16"]
     B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
     q, k, v = [t.cuda() for t in synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0)]
@@ -258,9 +267,22 @@ def measure_components():
     o = torch.empty_like(q)
     ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
                                               out=o), reps=5)
-    kv_bytes = 2 * k.numel() * 2 + bias.numel() * 2 + mask.numel() + 2 * q.numel() * 2
+    row_bytes = 2 * D * 2  # one K row and one V row, bf16
+    kv_bytes = row_bytes * B * KVH * Sk + bias.numel() * 2 + mask.numel() + 2 * q.numel() * 2
     out["attn/decode_swap_bf16_ms"] = ms
     out["attn/decode_swap_bf16_GB/s"] = kv_bytes / (ms * 1e-3) / 1e9
+    # key gather
+    keys = bsm.build_key_list(geom, mask)
+    kb = 1e3 * _time_ms(lambda: bsm.build_key_list(geom, mask))
+    listed = int(keys.num_keys.sum())
+    out["key_list/decode_swap_bf16_us"] = kb
+    out["key_list/decode_swap_bf16_listed_frac"] = listed / (B * KVH * Sk)
+    out["key_list/decode_swap_bf16_GB/s"] = (mask.numel() + listed * 8) / (kb * 1e-6) / 1e9
+    mg = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, keys=keys, out=o),
+                  reps=5)
+    g_bytes = row_bytes * listed + listed * 8 + bias.numel() * 2 + 2 * q.numel() * 2
+    out["attn_gather/decode_swap_bf16_ms"] = mg
+    out["attn_gather/decode_swap_bf16_GB/s"] = g_bytes / (mg * 1e-3) / 1e9
     return out
 
 

@@ -5,7 +5,8 @@ memory, shapes/strides and the current stream. There is no fallback: if the
 library is not built, or a call fails, this module raises.
 
 Names follow the C ABI: resolve_dflash_is_causal, block_mask_shape,
-build_block_mask, dynamic_topk_mask, dflash_dense_mask, masked_attn_fwd, plus
+build_block_mask, key_list_shape, build_key_list, dynamic_topk_mask,
+dflash_dense_mask, masked_attn_fwd, attn_bwd_workspace_size, masked_attn_bwd, plus
 create_mask, the 2D/4D pre-mask normalisation of flash-sparse-attention PR #197
 (Implementation Notes) done as zero-copy views before dynamic_topk_mask.
 """
@@ -26,8 +27,8 @@ BSM_OK, BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE, BSM_E_UNSUPPORTED, BS
 BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
-           "dynamic_topk_mask", "dflash_dense_mask", "masked_attn_fwd",
-           "attn_bwd_workspace_size", "masked_attn_bwd", "bsm_last_error")
+           "key_list_shape", "build_key_list", "dynamic_topk_mask", "dflash_dense_mask",
+           "masked_attn_fwd", "attn_bwd_workspace_size", "masked_attn_bwd", "bsm_last_error")
 
 
 class Tensor4(ctypes.Structure):
@@ -51,11 +52,17 @@ class BlockMaskC(ctypes.Structure):
                 ("Bm", c_int64), ("Hm", c_int64), ("nQm", c_int64), ("nK", c_int64)]
 
 
+class KeyListC(ctypes.Structure):
+    _fields_ = [("num_keys", c_void_p), ("key_indices", c_void_p), ("row_bits", c_void_p),
+                ("Bm", c_int64), ("Hm", c_int64), ("R", c_int64), ("K", c_int64)]
+
+
 class AttnArgs(ctypes.Structure):
     _fields_ = [("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("o", c_void_p),
                 ("o_stride", c_int64 * 4), ("lse", c_void_p), ("softmax_scale", c_float),
                 ("reserved", c_int32), ("pred", POINTER(DFlashC)), ("mask", POINTER(Tensor4)),
-                ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC))]
+                ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC)),
+                ("keys", POINTER(KeyListC))]
 
 
 class AttnBwdArgs(ctypes.Structure):
@@ -86,6 +93,9 @@ def lib():
                                        POINTER(c_int64)]
         L.build_block_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), POINTER(Tensor4),
                                        POINTER(BlockMaskC), c_void_p]
+        L.key_list_shape.argtypes = [POINTER(Geom), POINTER(Tensor4), POINTER(c_int64)]
+        L.build_key_list.argtypes = [POINTER(Geom), POINTER(Tensor4), POINTER(KeyListC),
+                                     c_void_p]
         L.dynamic_topk_mask.argtypes = [POINTER(Tensor4), POINTER(Tensor4), c_int64, c_int64,
                                         c_void_p, c_void_p]
         L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
@@ -200,6 +210,21 @@ class BlockMask(NamedTuple):
                           Bm, Hm, nQm, nK)
 
 
+class KeyList(NamedTuple):
+    """Kept keys of a mask over a short query block: num_keys (Bm, Hm), ascending
+    key_indices (Bm, Hm, K) and per-key row words row_bits (Bm, Hm, K, int32
+    holding the uint32 bits); entries past num_keys are unspecified."""
+    num_keys: torch.Tensor
+    key_indices: torch.Tensor
+    row_bits: torch.Tensor
+    rows: int
+
+    def c(self):
+        Bm, Hm, K = self.key_indices.shape
+        return KeyListC(self.num_keys.data_ptr(), self.key_indices.data_ptr(),
+                        self.row_bits.data_ptr(), Bm, Hm, self.rows, K)
+
+
 def round_multiple(x, m=128):
     return (int(x) + m - 1) // m * m
 
@@ -238,6 +263,27 @@ def build_block_mask(geom, pred=None, mask=None, device=None, stream=None):
                                   ctypes.byref(mc) if mc else None, ctypes.byref(bc),
                                   _stream(stream)))
     return bm
+
+
+def key_list_shape(geom, mask):
+    out = (c_int64 * 4)()
+    mc = tensor4(mask)
+    _check(lib().key_list_shape(ctypes.byref(Geometry(*geom).c()), ctypes.byref(mc), out))
+    return tuple(int(x) for x in out)
+
+
+def build_key_list(geom, mask, stream=None):
+    """Kept-key list of a bool mask (at most 32 rows per (b, h) after the swap)."""
+    Bm, Hm, R, K = key_list_shape(geom, mask)
+    dev = mask.device
+    kl = KeyList(torch.empty((Bm, Hm), dtype=torch.int32, device=dev),
+                 torch.empty((Bm, Hm, K), dtype=torch.int32, device=dev),
+                 torch.empty((Bm, Hm, K), dtype=torch.int32, device=dev), R)
+    mc = tensor4(mask)
+    kc = kl.c()
+    _check(lib().build_key_list(ctypes.byref(Geometry(*geom).c()), ctypes.byref(mc),
+                                ctypes.byref(kc), _stream(stream)))
+    return kl
 
 
 def dynamic_topk_mask(bias, premask, seqlen_k, k, out=None, stream=None):
@@ -289,7 +335,8 @@ def dflash_dense_mask(geom, pred, out=None, stream=None):
 
 
 def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
-                    softmax_scale=None, return_lse=False, out=None, lse=None, stream=None):
+                    softmax_scale=None, return_lse=False, out=None, lse=None, stream=None,
+                    keys=None):
     """Masked attention forward; returns O (and LSE if return_lse)."""
     geom = geometry_of(q, k)
     if out is None:
@@ -321,6 +368,10 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
         bmc = block_mask.c()
         keep.append(bmc)
         a.bm = ctypes.pointer(bmc)
+    if keys is not None:
+        kc = keys.c()
+        keep.append(kc)
+        a.keys = ctypes.pointer(kc)
     _check(lib().masked_attn_fwd(ctypes.byref(geom.c()), ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
 

@@ -11,6 +11,15 @@
 // are merged through LDS at the end. The mask bytes and bias values a wave needs
 // for the next tile are loaded into registers together with that tile's DMA,
 // so the wait for one covers the other.
+//
+// Key-gather mode: with a kept-key list (key_list.hip) a "tile" is 128
+// consecutive list positions instead of 128 consecutive keys. Each DMA chunk
+// is fetched from the K / V row of its position's key (positions past the
+// list's end, or keys outside [0, Sk), fall outside the buffer resource and
+// load as zeros), the mask bit of a (row, position) pair is bit `row` of the
+// position's row word, and the bias is gathered per key. The key indices a
+// tile's DMA needs are loaded two tiles ahead, so no load waits on another
+// inside the loop. Only the kept keys' K / V rows cross HBM.
 #include <math.h>
 
 #include "attn_common.h"
@@ -43,7 +52,119 @@ __device__ inline void load_aux(const AttnParams& p, int kt, int w, int hh, cons
   }
 }
 
+// LDS-DMA loader of gathered rows: load j of this thread moves 16-byte chunk
+// c_j of tile row r_j (the Loader layout); its source row is the key at list
+// position 128 t + r_j.
 template <int D>
+struct GatherLoader {
+  using C = V2Ctx<D, kDecRB>;
+  uint32_t kc[C::LOADS], vc[C::LOADS];  // swizzled chunk byte offset in the row
+  int row[C::LOADS];
+  uint32_t krow, vrow;                  // bytes per K / V row
+  uint32_t nkeys;
+  __amdgpu_buffer_rsrc_t kr, vr;
+
+  __device__ inline void init(const void* kbase, const void* vbase, int64_t k_sk, int64_t v_sk,
+                              int Sk, int w, int lane) {
+    constexpr int CPR = C::CPR;
+    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), 0,
+                                           (int)((int64_t)Sk * k_sk * 2), 0x00020000);
+    vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), 0,
+                                           (int)((int64_t)Sk * v_sk * 2), 0x00020000);
+    krow = (uint32_t)(k_sk * 2);
+    vrow = (uint32_t)(v_sk * 2);
+    nkeys = (uint32_t)Sk;
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int f = (j * C::NW + w) * 64 + lane;
+      const int r = f / CPR;
+      const int c = f % CPR;
+      row[j] = r;
+      kc[j] = (uint32_t)((c ^ swz_k<D>(r)) * 16);
+      vc[j] = (uint32_t)((c ^ swz_v<D>(r)) * 16);
+    }
+  }
+
+  // keys of this thread's rows of tile t (-1 past the list's end)
+  __device__ inline void keys(const int32_t* lidx, int t, int nlist, int (&key)[C::LOADS]) const {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int pos = t * kTile + row[j];
+      key[j] = pos < nlist ? lidx[pos] : -1;
+    }
+  }
+
+  // Offsets at or past 2^31 exceed the resource's range (Sk rows, < 2^31
+  // bytes), so such chunks load as zeros.
+  __device__ inline void issue(Tiles<D>& t, const int (&key)[C::LOADS], int w) const {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int slot = (j * C::NW + w) * 64;
+      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
+      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
+      const bool in = (uint32_t)key[j] < nkeys;
+      const uint32_t ok = in ? (uint32_t)key[j] * krow + kc[j] : 0x80000000u;
+      const uint32_t ov = in ? (uint32_t)key[j] * vrow + vc[j] : 0x80000000u;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+          "s_mov_b32 m0, %3\n\t"
+          "buffer_load_dwordx4 %4, %5, 0 offen lds"
+          :
+          : "s"(__builtin_amdgcn_readfirstlane(lk)), "v"(ok), "s"(kr),
+            "s"(__builtin_amdgcn_readfirstlane(lv)), "v"(ov), "s"(vr)
+          : "memory");
+    }
+  }
+};
+
+// Gathered-key aux of one lane for one tile: list positions
+// 128 t + 32 w + 16 sb + 8 hh + e (e < 8) -- their keys, row words and the
+// lane's bias values at those keys.
+struct GatherKeys {
+  int4 key[2][2];
+};
+struct GatherAux {
+  uint4 bits[2][2];
+  uint16_t bias[16];
+  int4 key[2][2];
+};
+
+__device__ inline void load_gather_keys(const int32_t* lidx, int t, int w, int hh,
+                                        GatherKeys& g) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int pos = t * kTile + 32 * w + 16 * sb + 8 * hh;
+    g.key[sb][0] = *reinterpret_cast<const int4*>(lidx + pos);
+    g.key[sb][1] = *reinterpret_cast<const int4*>(lidx + pos + 4);
+  }
+}
+
+__device__ inline int key_at(const int4 (&k)[2][2], int u) {
+  const int4 v = k[u >> 3][(u >> 2) & 1];
+  const int e = u & 3;
+  return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+}
+
+__device__ inline void load_gather_aux(const uint32_t* lbits, const uint16_t* brow, int Sk,
+                                       int t, int w, int hh, const GatherKeys& g,
+                                       GatherAux& a) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int pos = t * kTile + 32 * w + 16 * sb + 8 * hh;
+    a.bits[sb][0] = *reinterpret_cast<const uint4*>(lbits + pos);
+    a.bits[sb][1] = *reinterpret_cast<const uint4*>(lbits + pos + 4);
+    a.key[sb][0] = g.key[sb][0];
+    a.key[sb][1] = g.key[sb][1];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int key = key_at(g.key, u);
+    a.bias[u] = (brow && (uint32_t)key < (uint32_t)Sk) ? brow[key] : (uint16_t)0;
+  }
+}
+
+template <int D, bool GATHER>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
@@ -83,7 +204,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         (int64_t)kvh * p.v_sh;
   Loader<D, kDecRB> ld;
-  ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+  GatherLoader<D> gl;
+  if constexpr (GATHER)
+    gl.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+  else
+    ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
 
   f32x16 oacc[NDC];
 #pragma unroll
@@ -96,28 +221,67 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   TileList tl;
-  tl.init(p, b, h, 0);
-  const int ntiles = tl.count();
+  int ntiles;
+  const int32_t* lidx = nullptr;
+  const uint32_t* lbits = nullptr;
+  int nlist = 0;
+  if constexpr (GATHER) {
+    const KeyListView& kl = p.keys;
+    const int64_t li = (kl.Bm == 1 ? 0 : (int64_t)b) * kl.Hm + head_index(kl.h_mode, h, p.G);
+    nlist = kl.num[li];
+    nlist = __builtin_amdgcn_readfirstlane(nlist < 0 ? 0 : (nlist > kl.K ? (int)kl.K : nlist));
+    lidx = kl.idx + li * kl.K;
+    lbits = kl.bits + li * kl.K;
+    ntiles = (nlist + kTile - 1) / kTile;
+  } else {
+    tl.init(p, b, h, 0);
+    ntiles = tl.count();
+  }
   bool full_cur = false;
-  int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
+  int kt_cur = 0;
   AuxRegs aux_cur, aux_nxt;
+  GatherAux ga_cur, ga_nxt;
+  int dkey[V2Ctx<D, kDecRB>::LOADS];  // DMA keys of the next tile to issue
+  GatherKeys gk;                      // lane keys of the next tile's aux loads
   if (ntiles > 0) {
-    ld.issue(buf0, kt_cur, w);
-    load_aux(p, kt_cur, w, hh, mrow, brow, aux_cur);
+    if constexpr (GATHER) {
+      gl.keys(lidx, 0, nlist, dkey);
+      gl.issue(buf0, dkey, w);
+      load_gather_keys(lidx, 0, w, hh, gk);
+      load_gather_aux(lbits, brow, p.Sk, 0, w, hh, gk, ga_cur);
+      if (ntiles > 1) {
+        gl.keys(lidx, 1, nlist, dkey);
+        load_gather_keys(lidx, 1, w, hh, gk);
+      }
+    } else {
+      kt_cur = tl.tile(0, full_cur);
+      ld.issue(buf0, kt_cur, w);
+      load_aux(p, kt_cur, w, hh, mrow, brow, aux_cur);
+    }
   }
   for (int it = 0; it < ntiles; ++it) {
     const Tiles<D>& t = (it & 1) ? buf1 : buf0;
     Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
     bool full_nxt = false;
-    const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
+    int kt_nxt = 0;
+    if constexpr (!GATHER) kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) {
-      ld.issue(nxt, kt_nxt, w);
-      load_aux(p, kt_nxt, w, hh, mrow, brow, aux_nxt);
+      if constexpr (GATHER) {
+        gl.issue(nxt, dkey, w);
+        load_gather_aux(lbits, brow, p.Sk, it + 1, w, hh, gk, ga_nxt);
+        if (it + 2 < ntiles) {
+          gl.keys(lidx, it + 2, nlist, dkey);
+          load_gather_keys(lidx, it + 2, w, hh, gk);
+        }
+      } else {
+        ld.issue(nxt, kt_nxt, w);
+        load_aux(p, kt_nxt, w, hh, mrow, brow, aux_nxt);
+      }
     }
 
-    // S^T for this wave's 32 keys
+    // S^T for this wave's 32 keys (list positions in gather mode)
     const int k0 = kt_cur * kTile;
     const int row = w * 32 + perm_row(n);
     f32x16 sc{};
@@ -128,38 +292,66 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc, 0, 0, 0);
     }
     // scale, bias, mask
-    const bool check_k = k0 + kTile > p.Sk;
-    const bool check_mask = !full_cur && p.mask_kind != 0;
     float mloc = -INFINITY;
+    if constexpr (GATHER) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int kb = k0 + 32 * w + 16 * sb + 8 * hh;
-      uint32_t mbits = 0xFFu;
-      if (check_mask) {
-        if (p.mask_kind == 2) {
-          const uint2 mb = aux_cur.mask[sb];
-          mbits = 0;
+      for (int sb = 0; sb < 2; ++sb) {
+        const int pb = it * kTile + 32 * w + 16 * sb + 8 * hh;
+        uint32_t mbits = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
-            mbits |= (byte != 0u ? 1u : 0u) << e;
-          }
-        } else {
-          mbits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
+        for (int e = 0; e < 8; ++e) {
+          const uint4 wq = ga_cur.bits[sb][e >> 2];
+          const uint32_t word =
+              (e & 3) == 0 ? wq.x : ((e & 3) == 1 ? wq.y : ((e & 3) == 2 ? wq.z : wq.w));
+          const int key = key_at(ga_cur.key, 8 * sb + e);
+          const bool keep = ((word >> q) & 1u) && (uint32_t)key < (uint32_t)p.Sk;
+          mbits |= (keep ? 1u : 0u) << e;
+        }
+        mbits &= range_bits(0, nlist, pb);
+        if (!qvalid) mbits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * sb + e;
+          const float bv = bf16_to_f32(ga_cur.bias[u]) * kLog2e;
+          float sv = fmaf(sc[u], p.scale_log2, bv);
+          sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+          sc[u] = sv;
+          mloc = fmaxf(mloc, sv);
         }
       }
-      if (!qvalid) mbits = 0;
-      if (check_k) mbits &= range_bits(0, p.Sk, kb);
-      const uint32_t wv[4] = {aux_cur.bias[sb].x, aux_cur.bias[sb].y, aux_cur.bias[sb].z,
-                              aux_cur.bias[sb].w};
+    } else {
+      const bool check_k = k0 + kTile > p.Sk;
+      const bool check_mask = !full_cur && p.mask_kind != 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int u = 8 * sb + e;
-        const float bv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
-        float sv = fmaf(sc[u], p.scale_log2, bv);
-        sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
-        sc[u] = sv;
-        mloc = fmaxf(mloc, sv);
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kb = k0 + 32 * w + 16 * sb + 8 * hh;
+        uint32_t mbits = 0xFFu;
+        if (check_mask) {
+          if (p.mask_kind == 2) {
+            const uint2 mb = aux_cur.mask[sb];
+            mbits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+              mbits |= (byte != 0u ? 1u : 0u) << e;
+            }
+          } else {
+            mbits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
+          }
+        }
+        if (!qvalid) mbits = 0;
+        if (check_k) mbits &= range_bits(0, p.Sk, kb);
+        const uint32_t wv[4] = {aux_cur.bias[sb].x, aux_cur.bias[sb].y, aux_cur.bias[sb].z,
+                                aux_cur.bias[sb].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * sb + e;
+          const float bv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+          float sv = fmaf(sc[u], p.scale_log2, bv);
+          sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+          sc[u] = sv;
+          mloc = fmaxf(mloc, sv);
+        }
       }
     }
     mloc = max_pair(mloc);
@@ -206,9 +398,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
         oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[sb], oacc[dc], 0, 0, 0);
       }
     }
-    aux_cur = aux_nxt;
-    kt_cur = kt_nxt;
-    full_cur = full_nxt;
+    if constexpr (GATHER) {
+      ga_cur = ga_nxt;
+    } else {
+      aux_cur = aux_nxt;
+      kt_cur = kt_nxt;
+      full_cur = full_nxt;
+    }
   }
 
   // merge the four waves' partial states through LDS (tiles are free now)
@@ -282,10 +478,18 @@ bool attn_decode_applies(const AttnParams& p, int D) {
 hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s) {
   const int nwg = p.B * p.H;
   if (nwg == 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL(k_attn_decode<128>, dim3(nwg), dim3(64 * kDecWaves), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_attn_decode<64>, dim3(nwg), dim3(64 * kDecWaves), 0, s, p);
+  const dim3 blk(64 * kDecWaves);
+  if (D == 128) {
+    if (p.gather)
+      hipLaunchKernelGGL((k_attn_decode<128, true>), dim3(nwg), blk, 0, s, p);
+    else
+      hipLaunchKernelGGL((k_attn_decode<128, false>), dim3(nwg), blk, 0, s, p);
+  } else {
+    if (p.gather)
+      hipLaunchKernelGGL((k_attn_decode<64, true>), dim3(nwg), blk, 0, s, p);
+    else
+      hipLaunchKernelGGL((k_attn_decode<64, false>), dim3(nwg), blk, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -216,6 +216,38 @@ int bm_head_mode(const Geo& g, int64_t Hm) {
   return Hm == Hi ? 1 : (Hm == KVHi ? 2 : 0);
 }
 
+// Key-list dims of a bool mask: its (Bm, Hm) in the iteration space, the
+// iteration rows R (<= 32) and K_round.
+constexpr int64_t kMaxListRows = 32;
+
+int key_list_dims(const Geo& g, const bsm_tensor4* mask, Aux& a, int64_t out[4]) {
+  if (!mask) return fail(BSM_E_ARG, "mask is NULL");
+  int e = check_aux(mask, "mask", g, BSM_BOOL, a);
+  if (e) return e;
+  const int64_t R = iter_rows(g);
+  if (R > kMaxListRows)
+    return fail(BSM_E_UNSUPPORTED, "key list needs at most 32 rows per (b, h), got %lld",
+                (long long)R);
+  out[0] = a.Bm;
+  out[1] = a.Hm;
+  out[2] = R;
+  out[3] = g.Kr;
+  return BSM_OK;
+}
+
+int check_key_list(const bsm_key_list* kl, const int64_t shp[4]) {
+  if (kl->Bm != shp[0] || kl->Hm != shp[1] || kl->R != shp[2] || kl->K != shp[3])
+    return fail(BSM_E_SHAPE, "key list dims (%lld,%lld,%lld,%lld) expected (%lld,%lld,%lld,%lld)",
+                (long long)kl->Bm, (long long)kl->Hm, (long long)kl->R, (long long)kl->K,
+                (long long)shp[0], (long long)shp[1], (long long)shp[2], (long long)shp[3]);
+  if (shp[0] * shp[1] > 0 &&
+      (!kl->num_keys || (shp[3] > 0 && (!kl->key_indices || !kl->row_bits))))
+    return fail(BSM_E_ARG, "key list buffer is NULL");
+  if ((uintptr_t)kl->key_indices % 16 || (uintptr_t)kl->row_bits % 16)
+    return fail(BSM_E_STRIDE, "key list arrays must be 16-byte aligned");
+  return BSM_OK;
+}
+
 int check_tensor_qkv(const bsm_tensor4* t, const char* name, int64_t d0, int64_t d1,
                      int64_t d2, int64_t d3, int32_t dtype) {
   if (t->dtype != dtype) return fail(BSM_E_DTYPE, "%s: dtype mismatch", name);
@@ -367,6 +399,43 @@ int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64
   }
   if (n == 0) return BSM_OK;
   return hip_status(launch_topk(p, stream), "dynamic_topk_mask");
+}
+
+int key_list_shape(const bsm_geom* geom, const bsm_tensor4* mask, int64_t out_shape[4]) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!out_shape) return fail(BSM_E_ARG, "out_shape is NULL");
+  Aux a;
+  return key_list_dims(g, mask, a, out_shape);
+}
+
+int build_key_list(const bsm_geom* geom, const bsm_tensor4* mask, const bsm_key_list* out,
+                   hipStream_t stream) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!out) return fail(BSM_E_ARG, "out is NULL");
+  Aux a;
+  int64_t shp[4];
+  if ((e = key_list_dims(g, mask, a, shp))) return e;
+  if ((e = check_key_list(out, shp))) return e;
+  if (shp[0] * shp[1] > INT32_MAX) return fail(BSM_E_UNSUPPORTED, "too many key lists");
+  KeyListParams p{};
+  p.mask = reinterpret_cast<const uint8_t*>(a.view.data);
+  p.sb = a.view.sb;
+  p.sh = a.view.sh;
+  p.sq = a.view.sq;
+  p.Bm = a.Bm;
+  p.Hm = a.Hm;
+  p.K = g.Kr;
+  p.Sk = g.Sk;
+  p.R = (int32_t)shp[2];
+  p.Qm = (int32_t)a.Qm;
+  p.num = out->num_keys;
+  p.idx = out->key_indices;
+  p.bits = out->row_bits;
+  return hip_status(launch_key_list(p, stream), "build_key_list");
 }
 
 int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred, uint8_t* out_mask,
@@ -534,11 +603,33 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
   AttnInputs in;
   if ((e = check_attn_aux(g, dt, a->pred, a->mask, a->bias, a->bm, a->softmax_scale, in)))
     return e;
+  int64_t klist[4] = {0, 0, 0, 0};
+  if (a->keys) {
+    if (!a->mask || a->bm)
+      return fail(BSM_E_ARG, "a key list needs the mask it was built from and no block mask");
+    if (dt != BSM_BF16) return fail(BSM_E_UNSUPPORTED, "key-gather attention is bf16 only");
+    Aux ka;
+    if ((e = key_list_dims(g, a->mask, ka, klist))) return e;
+    if ((e = check_key_list(a->keys, klist))) return e;
+  }
   if (g.B == 0 || g.Sq == 0) return BSM_OK;
 
   AttnParams p;
   fill_params(g, a->q, a->k, a->v, a->o, a->o_stride, a->lse, a->softmax_scale, a->pred,
               a->mask, a->bias, a->bm, in, p);
+  if (a->keys) {
+    p.gather = 1;
+    p.keys.num = a->keys->num_keys;
+    p.keys.idx = a->keys->key_indices;
+    p.keys.bits = a->keys->row_bits;
+    p.keys.Bm = klist[0];
+    p.keys.Hm = klist[1];
+    p.keys.K = klist[3];
+    p.keys.h_mode = bm_head_mode(g, klist[1]);
+    if (!attn_decode_applies(p, (int)g.D))
+      return fail(BSM_E_UNSUPPORTED, "key-gather attention: K/V too large for 32-bit offsets");
+    return hip_status(launch_attn_decode(p, (int)g.D, stream), "masked_attn_fwd");
+  }
   hipError_t he;
   if (dt == BSM_BF16) {
     if (attn_decode_applies(p, (int)g.D))

@@ -34,6 +34,17 @@ struct BlockMaskView {
   int32_t pad;
 };
 
+// Kept-key list view in the attention's iteration space: for list (bk, hk),
+// num[bk * Hm + hk] keys at idx / bits + (bk * Hm + hk) * K.
+struct KeyListView {
+  const int32_t* num;
+  const int32_t* idx;
+  const uint32_t* bits;
+  int64_t Bm, Hm, K;
+  int32_t h_mode;  // 0: head index 0, 1: h, 2: h / G
+  int32_t pad;
+};
+
 // Aux tensor (mask or bias) addressed as base + b*sb + hidx*sh + q*sq + k,
 // with stride 0 on broadcast dims and hidx chosen by h_mode.
 struct AuxView {
@@ -64,6 +75,9 @@ struct AttnParams {
   int32_t has_bias;
   int32_t has_bm;
   BlockMaskView bm;
+  int32_t gather;   // visit the keys of `keys` instead of key tiles
+  int32_t pad2;
+  KeyListView keys;
 };
 
 // Backward: the forward's view plus the incoming gradient, the gradient
@@ -104,6 +118,18 @@ struct DenseMaskView {
   int64_t Sk;
 };
 
+// Kept-key list builder: mask (bm, hm, r) rows at data + bm*sb + hm*sh + r*sq
+// (sq unused when Qm == 1), R rows, keys < Sk of K_round.
+struct KeyListParams {
+  const uint8_t* mask;
+  int64_t sb, sh, sq;
+  int64_t Bm, Hm, K, Sk;
+  int32_t R, Qm;
+  int32_t* num;
+  int32_t* idx;
+  uint32_t* bits;
+};
+
 struct TopkParams {
   const void* bias;
   int64_t b_sb, b_sh, b_sq;
@@ -126,6 +152,7 @@ hipError_t launch_block_mask_dense(const DenseMaskView& m, int32_t* kv_num,
                                    int32_t* kv_idx, int32_t* full_num,
                                    int32_t* full_idx, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_key_list(const KeyListParams& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
 // pipelined bf16 kernel: two heads of a KV group per workgroup
@@ -138,7 +165,8 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D);
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s);
 hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
-// bf16 kernel for at most 32 query rows per (b, h), split along the keys
+// bf16 kernel for at most 32 query rows per (b, h), split along the keys; with
+// p.gather it visits the kept keys of p.keys in tiles of 128 list positions
 bool attn_decode_applies(const AttnParams& p, int D);
 hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s);
 

@@ -20,6 +20,7 @@
 //    significant first, from LDS histograms of the digit among the keys that
 //    share the prefix found so far; the keys stay in LDS when they fit,
 //    otherwise each pass re-reads the row.
+#include "block_scan.h"
 #include "bsm_internal.h"
 
 namespace bsm {
@@ -55,30 +56,6 @@ struct KeyTraits<uint32_t> {
   // finfo(float32).min = -(2 - 2^-23) * 2^127 (bits 0xFF7FFFFF)
   __device__ static uint32_t sentinel() { return ~0xFF7FFFFFu; }
 };
-
-// Exclusive prefix sum of v over the workgroup in thread order.
-__device__ inline int block_excl_sum(int v, int* s_wave, int& tot) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_wave[w] = x;
-  __syncthreads();
-  int off = 0;
-  tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int t = s_wave[i];
-    off += i < w ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  return off + x - v;
-}
 
 template <typename KeyT, bool kCache>
 __global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
@@ -227,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
       for (int i = 0; i < kPer; ++i) neq += (uint32_t)kk[i] == T;
     }
     int tot;
-    int r = taken + block_excl_sum(neq, s_wave, tot);
+    int r = taken + block_excl_sum<kWaves>(neq, s_wave, tot);
     if (k0 < K) {
       uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll

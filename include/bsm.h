@@ -121,6 +121,27 @@ typedef struct {
   int64_t Bm, Hm, nQm, nK;
 } bsm_block_mask;
 
+/* Kept-key list of a dense mask over a short query block: at most 32 rows per
+ * (b, h) in the attention's iteration space, as under the seqlen_q == 1
+ * head-group swap ([FSA-190] Design), where the rows are the G heads of a KV
+ * group. For a dynamic top-k mask ([FSA-197] Design: window_size keys kept per
+ * row) the union over the rows is a small part of the keys, and attention that
+ * is given the list reads only those keys' K / V rows. For each (bm, hm) of the
+ * mask's dims in the iteration space, with R rows (row r reads mask row r, or
+ * row 0 when the mask broadcasts over queries):
+ *   num_keys[bm, hm]        = number of keys j < Sk kept by at least one row;
+ *   key_indices[bm, hm, p]  = those keys in ascending order, p < num_keys;
+ *   row_bits[bm, hm, p]     = sum of 2^r over the rows r that keep that key.
+ * Arrays: int32 (Bm, Hm), int32 (Bm, Hm, K) and uint32 (Bm, Hm, K),
+ * contiguous, K = K_round; key_indices and row_bits 16-byte aligned. Entries
+ * at p >= num_keys are left unspecified. */
+typedef struct {
+  int32_t* num_keys;
+  int32_t* key_indices;
+  uint32_t* row_bits;
+  int64_t Bm, Hm, R, K;
+} bsm_key_list;
+
 typedef struct {
   bsm_tensor4 q, k, v;       /* bf16 or f32, all the same dtype */
   void* o;                   /* output, q's dtype, sizes (B, Sq, H, D) */
@@ -132,6 +153,8 @@ typedef struct {
   const bsm_tensor4* mask;   /* nullable; bool aux tensor (not with pred) */
   const bsm_tensor4* bias;   /* nullable; additive aux tensor */
   const bsm_block_mask* bm;  /* nullable; NULL visits every key tile */
+  const bsm_key_list* keys;  /* nullable; key-gather visit: needs mask, no bm, bf16,
+                                and the list build_key_list made from that mask */
 } bsm_attn_args;
 
 /* In-block causality of a DFlash layer ([SF-905] Motivation; #934):
@@ -173,6 +196,18 @@ int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask,
                       int64_t seqlen_k, int64_t k, uint8_t* out_mask,
                       hipStream_t stream);
 
+/* Dims (Bm, Hm, R, K) of the key list build_key_list makes from this bool
+ * mask: the mask's batch and head dims in the iteration space (after the swap
+ * when it applies), R = rows per (b, h) there (G under the swap, else Sq), and
+ * K = K_round. R > 32 is BSM_E_UNSUPPORTED. Host only. */
+int key_list_shape(const bsm_geom* geom, const bsm_tensor4* mask, int64_t out_shape[4]);
+
+/* Build the kept-key list of a bool mask (see bsm_key_list). out's dims must
+ * equal key_list_shape's. Reads the mask once; writes num_keys and the first
+ * num_keys entries of key_indices and row_bits for every (bm, hm). */
+int build_key_list(const bsm_geom* geom, const bsm_tensor4* mask, const bsm_key_list* out,
+                   hipStream_t stream);
+
 /* Dense DFlash mask, materialised: out_mask is a device, contiguous bool array
  * (Sq, K_round) (the [B,1,Q_LEN,KV_LEN] mask of [SF-474] Suggestion 2 with the
  * batch dim dropped, keys rounded to 128, tail False). For consumers that need
@@ -186,7 +221,12 @@ int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred,
  *   LSE = log sum_j exp(s_j);
  * a row with no kept key gets O = 0 and LSE = -inf. With a block mask only its
  * listed tiles are visited (full tiles skip the mask test); it must have been
- * built by build_block_mask for the same geometry and mask source. bf16 runs on
+ * built by build_block_mask for the same geometry and mask source. With a key
+ * list instead (keys, bf16 only, at most 32 rows per (b, h) in the iteration
+ * space) only the listed keys are visited, row r keeping listed key p iff bit r
+ * of its row word is set; the list must have been built by build_key_list from
+ * the same mask, and listed keys outside [0, Sk) are treated as masked. Either
+ * way the result is that of the dense mask. bf16 runs on
  * bf16 MFMA with float accumulation and a float online softmax, O rounded to
  * nearest even; f32 computes in float. D must be 64 or 128. */
 int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* args,

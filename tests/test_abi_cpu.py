@@ -47,7 +47,8 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(bsm.Tensor4) == 80
     assert ctypes.sizeof(bsm.DFlashC) == 56
     assert ctypes.sizeof(bsm.BlockMaskC) == 64
-    assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 4 * 8
+    assert ctypes.sizeof(bsm.KeyListC) == 3 * 8 + 4 * 8
+    assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 5 * 8
     assert ctypes.sizeof(bsm.AttnBwdArgs) == 8 * 80 + 8 + 8 + 5 * 8 + 8 + 8
 
 
@@ -55,6 +56,7 @@ def test_struct_layouts_match_c_compiler(tmp_path):
     """sizeof and field offsets as the C compiler lays out include/bsm.h."""
     structs = {"bsm_tensor4": bsm.Tensor4, "bsm_dflash": bsm.DFlashC,
                "bsm_block_mask": bsm.BlockMaskC, "bsm_geom": bsm.Geom,
+               "bsm_key_list": bsm.KeyListC,
                "bsm_attn_args": bsm.AttnArgs, "bsm_attn_bwd_args": bsm.AttnBwdArgs}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "bsm.h"', "int main(void) {"]
     for cname, py in structs.items():
@@ -210,6 +212,53 @@ def test_attention_validation(L):
     a.bm = ctypes.pointer(bm)
     assert _attn(L, geom, a) == bsm.BSM_E_SHAPE       # block mask for another geometry
     assert b"block mask" in L.bsm_last_error()
+
+
+def _kl_shape(L, geom, mask):
+    out = (ctypes.c_int64 * 4)()
+    st = L.key_list_shape(ctypes.byref(bsm.Geom(*geom)), ctypes.byref(mask), out)
+    return st, tuple(out)
+
+
+def test_key_list_shapes_and_validation(L):
+    # decode with the swap: (B, H, 1, K) -> lists per (b, KV head) over G = 4 rows
+    dec = (64, 32, 8, 1, 16384, 128)
+    assert _kl_shape(L, dec, _t4((64, 32, 1, 16384))) == (0, (64, 8, 4, 16384))
+    # mask per KV head under the swap broadcasts over the G rows
+    assert _kl_shape(L, dec, _t4((64, 8, 1, 16384))) == (0, (64, 8, 4, 16384))
+    # a short prefill chunk without the swap: Sq rows per (b, h)
+    assert _kl_shape(L, (2, 8, 2, 20, 300, 64), _t4((2, 2, 20, 384))) == (0, (2, 2, 20, 384))
+    # more than 32 rows is outside what a row word holds
+    st, _ = _kl_shape(L, (2, 8, 2, 40, 300, 64), _t4((2, 2, 40, 384)))
+    assert st == bsm.BSM_E_UNSUPPORTED
+    assert _kl_shape(L, dec, _t4((64, 32, 1, 16384), bsm.BSM_BF16))[0] == bsm.BSM_E_DTYPE
+    g = bsm.Geom(*dec)
+    m = _t4((64, 32, 1, 16384))
+    kl = bsm.KeyListC(1 << 22, 1 << 23, 1 << 24, 64, 8, 4, 16384)
+    wrong = bsm.KeyListC(1 << 22, 1 << 23, 1 << 24, 64, 8, 2, 16384)
+    assert L.build_key_list(ctypes.byref(g), ctypes.byref(m), ctypes.byref(wrong), None) == \
+        bsm.BSM_E_SHAPE
+    odd = bsm.KeyListC(1 << 22, (1 << 23) + 4, 1 << 24, 64, 8, 4, 16384)
+    assert L.build_key_list(ctypes.byref(g), ctypes.byref(m), ctypes.byref(odd), None) == \
+        bsm.BSM_E_STRIDE
+    null = bsm.KeyListC(None, 1 << 23, 1 << 24, 64, 8, 4, 16384)
+    assert L.build_key_list(ctypes.byref(g), ctypes.byref(m), ctypes.byref(null), None) == \
+        bsm.BSM_E_ARG
+    # attention with a key list: needs the mask and no block mask, bf16 only
+    a = _attn_args(dec)
+    a.keys = ctypes.pointer(kl)
+    assert _attn(L, dec, a) == bsm.BSM_E_ARG
+    a.mask = ctypes.pointer(m)
+    bm = bsm.BlockMaskC(1 << 22, 1 << 22, 1 << 22, 1 << 22, 64, 8, 1, 128)
+    a.bm = ctypes.pointer(bm)
+    assert _attn(L, dec, a) == bsm.BSM_E_ARG
+    a = _attn_args(dec, dtype=bsm.BSM_F32)
+    a.mask, a.keys = ctypes.pointer(m), ctypes.pointer(kl)
+    assert _attn(L, dec, a) == bsm.BSM_E_UNSUPPORTED
+    a = _attn_args(dec)
+    a.mask, a.keys = ctypes.pointer(m), ctypes.pointer(wrong)
+    assert _attn(L, dec, a) == bsm.BSM_E_SHAPE
+    assert b"key list" in L.bsm_last_error()
 
 
 def test_topk_validation(L):
