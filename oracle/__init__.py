@@ -31,7 +31,9 @@ Sources (cited by title and section throughout):
 
 Modules:
   dflash     -- DFlash draft-block predicate: is_causal resolution and the dense
-                boolean mask (pinned: brute-force rule tables, closed forms).
+                boolean mask (pinned: brute-force rule tables, closed forms);
+                the inference geometry of one block after a KV cache (pinned:
+                worked example, the last block of a training sequence).
   blockmask  -- 128x128 tile classification into empty / partial / full and
                 the inverse expansion (pinned: round trip, per-head identity).
   topk       -- dynamic top-k keep mask over an additive bias (pinned: O(K^2)
@@ -54,6 +56,7 @@ from .dflash import (  # noqa: F401
     DFlashGeom,
     resolve_dflash_is_causal,
     dflash_dense_mask,
+    dflash_inference_geom,
 )
 from .blockmask import TILE, classify_tiles, expand_block_mask  # noqa: F401
 from .topk import finfo_min, topk_keep_mask, topk_rank_bruteforce  # noqa: F401

@@ -164,3 +164,20 @@ def dflash_dense_mask(g, rows=None):
         draft_keep &= (pos_q - pos_k) < W
 
     return ctx_keep | draft_keep
+
+
+def dflash_inference_geom(ctx_len, block_size, is_causal=None, layer_type="full",
+                          sliding_window=0):
+    """Mask geometry of one draft block drafted after ctx_len cached tokens.
+
+    [SF-905] Modifications and the maintainer reply (#935) give inference
+    (spec_generate) a default mask built by the same builders as training; the
+    pages show no inference shapes. Plainest reading: the block being drafted
+    is the last block of a training sequence whose context ends at the cache
+    end, so it sees every cached token (E = C), its own bs tokens under the
+    layer's in-block causality, and on sliding layers the left-bound window
+    with pos(draft i) = C + i. Keys: the C cached tokens, then the block.
+    """
+    return DFlashGeom(ctx_len, 1, block_size, ctx_per_block=ctx_len, is_causal=is_causal,
+                      layer_type=layer_type, sliding_window=sliding_window)
+

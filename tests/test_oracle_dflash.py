@@ -218,3 +218,41 @@ def test_blockmask_round_trip_random():
     np.testing.assert_array_equal(back, m)
     # a full tile is never listed when it straddles seqlen_k
     assert not (got[3] == Sk // 128).any()
+
+
+# ---------------------------------------------------------------------------
+# inference geometry: one draft block after a KV cache of C tokens
+
+
+def test_inference_worked_example():
+    """C = 5 cached tokens, a block of 3, causal sliding layer with W = 4: token
+    i sits at position 5 + i and sees cached keys c with 5 + i - c < 4 and its
+    own tokens i' <= i."""
+    from oracle import dflash_inference_geom
+    g = dflash_inference_geom(5, 3, is_causal=True, layer_type="sliding", sliding_window=4)
+    m = dflash_dense_mask(g)
+    assert m.shape == (3, 128) and not m[:, 8:].any()
+    want = [[0, 0, 1, 1, 1, 1, 0, 0],
+            [0, 0, 0, 1, 1, 1, 1, 0],
+            [0, 0, 0, 0, 1, 1, 1, 1]]
+    np.testing.assert_array_equal(m[:, :8], np.array(want, bool))
+    full = dflash_dense_mask(dflash_inference_geom(5, 3))
+    assert full[:, :8].all() and not full[:, 8:].any()
+
+
+@pytest.mark.parametrize("is_causal,layer,window", [
+    (None, "full", 0), (None, "sliding", 40), (True, "full", 0), (False, "sliding", 25),
+    (True, "sliding", 300),
+])
+def test_inference_is_last_training_block(is_causal, layer, window):
+    """The inference mask equals the last block of a training sequence with the
+    same context: its rows, on the context keys and that block's own keys."""
+    from oracle import dflash_inference_geom
+    C, NB, bs = 240, 6, 16
+    train = dflash_dense_mask(DFlashGeom(C, NB, bs, is_causal=is_causal, layer_type=layer,
+                                         sliding_window=window))
+    last = train[(NB - 1) * bs:NB * bs]
+    cols = np.r_[0:C, C + (NB - 1) * bs:C + NB * bs]
+    inf = dflash_dense_mask(dflash_inference_geom(C, bs, is_causal, layer, window))
+    np.testing.assert_array_equal(inf[:, :C + bs], last[:, cols])
+    assert not inf[:, C + bs:].any()
