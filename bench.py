@@ -242,6 +242,34 @@ def measure_components():
     out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
     del q, k, v, o
     out.update(measure_decode())
+    out.update(measure_dflash_infer())
+    return out
+
+
+def measure_dflash_infer():
+    """DFlash inference: one draft block of 16 after a 32K-token cache, B=8
+    requests, H=32, KVH=8, D=128, full and sliding (W=4096) layers. HBM-bound;
+    GB/s counts the K/V rows of the visited key tiles once per (b, KV head)
+    plus Q and O."""
+    out = {}
+    cfg = synth.CONFIGS["dflash_infer_bf16"]
+    B, H, KVH, D = (cfg[x] for x in ("B", "H", "KVH", "D"))
+    for lay in cfg["layers"]:
+        d = bsm.DFlash.inference(cfg["ctx_len"], cfg["block_size"], is_causal=lay["is_causal"],
+                                 layer_type=lay["layer_type"], sliding_window=lay["window"])
+        q, k, v = [t.cuda() for t in synth.qkv(B, d.Sq, d.Sk, H, KVH, D, "bf16", seed=0,
+                                               scale=cfg["qkv_scale"])]
+        geom = bsm.geometry_of(q, k)
+        bm = bsm.build_block_mask(geom, pred=d)
+        tiles = int(bm.kv_num_blocks.sum() + bm.full_kv_num_blocks.sum())
+        o = torch.empty_like(q)
+        ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, out=o),
+                      reps=10)
+        rows = min(tiles * 128, d.Sk)
+        nbytes = B * KVH * rows * 2 * D * 2 + 2 * q.numel() * 2
+        out[f"attn/dflash_infer_bf16/{lay['name']}_us"] = ms * 1e3
+        out[f"attn/dflash_infer_bf16/{lay['name']}_GB/s"] = nbytes / (ms * 1e-3) / 1e9
+        del q, k, v, o
     return out
 
 

@@ -188,6 +188,14 @@ class DFlash:
         return DFlashC(self.ctx_len, self.num_blocks, self.block_size, self.ctx_per_block,
                        self.ctx_end_offset, ic, lt, self.sliding_window)
 
+    @classmethod
+    def inference(cls, ctx_len, block_size, is_causal=None, layer_type="full", sliding_window=0):
+        """One draft block after ctx_len cached tokens (the default mask of
+        inference): the block sees every cached token, and keys are the cache
+        followed by the block's own block_size tokens."""
+        return cls(ctx_len, 1, block_size, ctx_per_block=ctx_len, is_causal=is_causal,
+                   layer_type=layer_type, sliding_window=sliding_window)
+
     @property
     def Sq(self):
         return self.num_blocks * self.block_size

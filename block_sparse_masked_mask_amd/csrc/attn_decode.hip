@@ -171,8 +171,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
   __shared__ __align__(1024) Tiles<D> buf0;
   __shared__ __align__(1024) Tiles<D> buf1;
 
-  const int h = blockIdx.x % p.H;
-  const int b = blockIdx.x / p.H;
+  // Workgroup i runs on XCD i % 8; give each XCD a contiguous range of (b, h)
+  // so the G heads of a KV group read their K/V through the same L2.
+  int id;
+  {
+    const int nwg = gridDim.x;
+    const int x = blockIdx.x % kXcds;
+    const int qx = nwg / kXcds, rx = nwg % kXcds;
+    id = (x < rx ? x * (qx + 1) : rx * (qx + 1) + (x - rx) * qx) + blockIdx.x / kXcds;
+  }
+  const int h = id % p.H;
+  const int b = id / p.H;
   const int kvh = h / p.G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -9,15 +9,16 @@
 // of G top-k sets: a small part of the key range.
 //
 // One workgroup per (bm, hm) streams the R mask rows once, 16 contiguous bytes
-// per thread per row and 4096 keys per pass, ORs the rows into per-key words,
-// and compacts the keys with a non-zero word by a workgroup prefix count.
+// per thread per row and 16384 keys per pass (a decode row of 16K keys is one
+// pass: one load round trip, one scan), ORs the rows into per-key words, and
+// compacts the keys with a non-zero word by a workgroup prefix count.
 #include "block_scan.h"
 #include "bsm_internal.h"
 
 namespace bsm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 16;                 // keys per thread per pass
 constexpr int kPass = kThreads * kPer;   // keys per pass
@@ -44,10 +45,18 @@ __global__ __launch_bounds__(kThreads) void k_key_list(KeyListParams p) {
     if (k0 < p.Sk) {
       // k0 is a multiple of 16 below Sk <= K (a multiple of 128): the 16
       // bytes lie inside the row
-      for (int r = 0; r < nrows; ++r) {
-        const uint4 v = *reinterpret_cast<const uint4*>(base + r * p.sq + k0);
+      // four rows' loads in flight at a time
+      for (int r0 = 0; r0 < nrows; r0 += 4) {
+        uint4 v[4];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) w[e] |= (byte_of(v, e) != 0u ? 1u : 0u) << r;
+        for (int i = 0; i < 4; ++i)
+          v[i] = r0 + i < nrows ? *reinterpret_cast<const uint4*>(base + (r0 + i) * p.sq + k0)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e)
+            w[e] |= (byte_of(v[i], e) != 0u ? 1u : 0u) << ((r0 + i) & 31);
       }
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {

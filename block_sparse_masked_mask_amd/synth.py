@@ -97,6 +97,13 @@ CONFIGS = {
         kind="topk", dtype="bf16", B=2, H=16, KVH=4, D=128, Sq=8000, Sk=8000,
         bias_heads="kvh", bias_q=1, pad_lo=0, pad_hi=1000, topk=2048, qkv_scale=1.0,
     ),
+    # inference: one draft block of 16 after a 32K-token cache per request
+    "dflash_infer_bf16": dict(
+        kind="dflash_infer", dtype="bf16", B=8, H=32, KVH=8, D=128,
+        ctx_len=32768, block_size=16, qkv_scale=0.5,
+        layers=[dict(name="full", is_causal=None, layer_type="full", window=0),
+                dict(name="sliding", is_causal=None, layer_type="sliding", window=4096)],
+    ),
     "decode_swap_bf16": dict(
         kind="topk", dtype="bf16", B=64, H=32, KVH=8, D=128, Sq=1, Sk=16384,
         bias_heads="h", bias_q=1, pad_lo=None, pad_hi=None, topk=1024, qkv_scale=1.0,

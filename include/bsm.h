@@ -99,7 +99,9 @@ typedef struct {
  * layer_type). On sliding layers a key is visible only if
  * pos_q - pos_k < sliding_window (left bound only), with pos(context c) = c and
  * pos(draft token i of block j) = E_j + i. The mask is the same for every batch
- * entry and head. */
+ * entry and head. Inference (the default mask of spec_generate, [SF-905]
+ * Modifications, #935): one block drafted after ctx_len cached tokens is
+ * num_blocks = 1 with ctx_per_block = ctx_len, so it sees the whole cache. */
 typedef struct {
   int64_t ctx_len, num_blocks, block_size, ctx_per_block, ctx_end_offset;
   int32_t is_causal;
