@@ -363,6 +363,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the DFlash training-shape backward and print it")
+    ap.add_argument("--only", choices=["decode", "infer", "components"],
+                    help="only time one group of the other workloads' kernels and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
@@ -374,6 +376,11 @@ def main():
         return
     if args.backward_only:
         print(json.dumps(measure_backward()), flush=True)
+        return
+    if args.only:
+        fn = {"decode": measure_decode, "infer": measure_dflash_infer,
+              "components": measure_components}[args.only]
+        print(json.dumps(fn()), flush=True)
         return
     step = Step()
     for _ in range(args.warmup):
