@@ -45,6 +45,9 @@ Modules:
                 attention (pinned: central finite differences of the forward
                 oracle, torch autograd in float64, broadcast dbias reductions).
   normalize  -- 2D/4D pre-mask normalisation and key-length rounding.
+  varlen     -- packed variable-length sequences: pad / unpad, per-sequence
+                DFlash geometry, packed attention and its block mask (pinned:
+                worked example, round trip, padded-batch equivalences).
   keylist    -- kept-key list of a dense mask over at most 32 query rows, with
                 a bit per row (pinned: hand-worked example, round trip,
                 top-k count invariant, attention over the gathered keys).
@@ -64,3 +67,5 @@ from .attention import attention_rows, attention_full  # noqa: F401
 from .attention_bwd import attention_bwd, group_grads, head_grads  # noqa: F401
 from .normalize import round_multiple, normalize_premask  # noqa: F401
 from .keylist import key_list, expand_key_list  # noqa: F401
+from .varlen import (attention_varlen, block_mask_varlen, dflash_varlen_geoms,  # noqa: F401
+                     pad, unpad)
