@@ -243,6 +243,44 @@ def measure_components():
     del q, k, v, o
     out.update(measure_decode())
     out.update(measure_dflash_infer())
+    out.update(measure_varlen())
+    return out
+
+
+VARLEN_LAYOUT = [(4096, 256), (2048, 128), (1024, 64), (3008, 47)]  # (context, blocks)
+
+
+def measure_varlen():
+    """Four DFlash sequences of different lengths packed together (H=32, KVH=8,
+    D=128, blocks of 16), both layer types of the training shape: per-sequence
+    block mask and packed attention, TFLOP/s counted on each sequence's kept
+    tiles."""
+    out = {}
+    cfg = synth.CONFIGS["dflash_train_bf16"]
+    H, KVH, D, bs = cfg["H"], cfg["KVH"], cfg["D"], cfg["block_size"]
+    sq = [nb * bs for _, nb in VARLEN_LAYOUT]
+    sk = [c + nb * bs for c, nb in VARLEN_LAYOUT]
+    cu_q = torch.tensor([0] + list(np.cumsum(sq)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(sk)), dtype=torch.int32)
+    q, k, v = [t[0].cuda() for t in synth.qkv(1, int(cu_q[-1]), int(cu_k[-1]), H, KVH, D, "bf16",
+                                               seed=0, scale=cfg["qkv_scale"])]
+    vl = bsm.Varlen(cu_q.cuda(), cu_k.cuda(), H, KVH, D)
+    for lay in cfg["layers"]:
+        pred = bsm.varlen_dflash(bs, is_causal=lay["is_causal"], layer_type=lay["layer_type"],
+                                 sliding_window=lay["window"])
+        bm = bsm.build_block_mask_varlen(vl, pred)
+        kvn, kvi, fn, fi = [t.cpu().numpy() for t in bm]
+        fl = 0
+        for b in range(len(sq)):
+            for qt in range((sq[b] + 127) // 128):
+                rows = min(128, sq[b] - 128 * qt)
+                for kt in list(kvi[b, 0, qt, :kvn[b, 0, qt]]) + list(fi[b, 0, qt, :fn[b, 0, qt]]):
+                    fl += 4 * D * H * rows * min(128, sk[b] - 128 * int(kt))
+        o = torch.empty_like(q)
+        ms = _time_ms(lambda: bsm.masked_attn_varlen_fwd(q, k, v, vl, pred=pred, block_mask=bm,
+                                                         out=o), reps=5)
+        out[f"attn_varlen/dflash_4seq_bf16/{lay['name']}_ms"] = ms
+        out[f"attn_varlen/dflash_4seq_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
     return out
 
 
@@ -363,7 +401,7 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the DFlash training-shape backward and print it")
-    ap.add_argument("--only", choices=["decode", "infer", "components"],
+    ap.add_argument("--only", choices=["decode", "infer", "varlen", "components"],
                     help="only time one group of the other workloads' kernels and print it")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -378,7 +416,7 @@ def main():
         print(json.dumps(measure_backward()), flush=True)
         return
     if args.only:
-        fn = {"decode": measure_decode, "infer": measure_dflash_infer,
+        fn = {"decode": measure_decode, "infer": measure_dflash_infer, "varlen": measure_varlen,
               "components": measure_components}[args.only]
         print(json.dumps(fn()), flush=True)
         return

@@ -28,7 +28,9 @@ BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
            "key_list_shape", "build_key_list", "dynamic_topk_mask", "dflash_dense_mask",
-           "masked_attn_fwd", "attn_bwd_workspace_size", "masked_attn_bwd", "bsm_last_error")
+           "masked_attn_fwd", "attn_bwd_workspace_size", "masked_attn_bwd",
+           "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
+           "unpad_index", "gather_rows", "scatter_rows", "bsm_last_error")
 
 
 class Tensor4(ctypes.Structure):
@@ -63,6 +65,13 @@ class AttnArgs(ctypes.Structure):
                 ("reserved", c_int32), ("pred", POINTER(DFlashC)), ("mask", POINTER(Tensor4)),
                 ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC)),
                 ("keys", POINTER(KeyListC))]
+
+
+class VarlenC(ctypes.Structure):
+    _fields_ = [("num_seqs", c_int64), ("H", c_int64), ("KVH", c_int64), ("D", c_int64),
+                ("total_q", c_int64), ("total_k", c_int64), ("cu_seqlens_q", c_void_p),
+                ("cu_seqlens_k", c_void_p), ("cu_seqlens_q_host", c_void_p),
+                ("cu_seqlens_k_host", c_void_p)]
 
 
 class AttnBwdArgs(ctypes.Structure):
@@ -103,6 +112,16 @@ def lib():
         L.attn_bwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs),
                                               POINTER(c_int64)]
         L.masked_attn_bwd.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs), c_void_p]
+        L.block_mask_varlen_shape.argtypes = [POINTER(VarlenC), POINTER(DFlashC),
+                                              POINTER(c_int64)]
+        L.build_block_mask_varlen.argtypes = [POINTER(VarlenC), POINTER(DFlashC),
+                                              POINTER(BlockMaskC), c_void_p]
+        L.masked_attn_varlen_fwd.argtypes = [POINTER(VarlenC), POINTER(AttnArgs), c_void_p]
+        L.unpad_index.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                                  c_void_p]
+        L.gather_rows.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+                                  c_int64, c_void_p]
+        L.scatter_rows.argtypes = L.gather_rows.argtypes
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = c_int32
         _lib = L
@@ -435,3 +454,131 @@ def masked_attn_bwd(q, k, v, out, dout, lse, pred=None, mask=None, bias=None, bl
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length sequences
+
+
+class Varlen:
+    """Packed sequences: cu_seqlens_q / cu_seqlens_k (int32, num_seqs + 1) on the
+    device, with host copies kept for the library's validation."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, H, KVH, D):
+        self.cu_q = cu_seqlens_q.to(torch.int32).contiguous()
+        self.cu_k = cu_seqlens_k.to(torch.int32).contiguous()
+        self.cu_q_host = self.cu_q.cpu().contiguous()
+        self.cu_k_host = self.cu_k.cpu().contiguous()
+        self.H, self.KVH, self.D = int(H), int(KVH), int(D)
+
+    @property
+    def num_seqs(self):
+        return self.cu_q_host.numel() - 1
+
+    def c(self):
+        return VarlenC(self.num_seqs, self.H, self.KVH, self.D, int(self.cu_q_host[-1]),
+                       int(self.cu_k_host[-1]), self.cu_q.data_ptr(), self.cu_k.data_ptr(),
+                       self.cu_q_host.data_ptr(), self.cu_k_host.data_ptr())
+
+
+def varlen_dflash(block_size, ctx_per_block=0, ctx_end_offset=0, is_causal=None,
+                  layer_type="full", sliding_window=0):
+    """DFlash predicate for packed sequences: each sequence's context and block
+    count come from its own lengths (ctx_len and num_blocks are 0)."""
+    return DFlash(0, 0, block_size, ctx_per_block, ctx_end_offset, is_causal, layer_type,
+                  sliding_window)
+
+
+def block_mask_varlen_shape(varlen, pred):
+    out = (c_int64 * 4)()
+    vc = varlen.c()
+    pc = pred.c()
+    _check(lib().block_mask_varlen_shape(ctypes.byref(vc), ctypes.byref(pc), out))
+    return tuple(int(x) for x in out)
+
+
+def build_block_mask_varlen(varlen, pred, stream=None):
+    """Per-sequence DFlash block mask (num_seqs, 1, nQmax, nKmax)."""
+    Bm, Hm, nQm, nK = block_mask_varlen_shape(varlen, pred)
+    dev = varlen.cu_q.device
+    bm = BlockMask(torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=dev),
+                   torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=dev),
+                   torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=dev),
+                   torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=dev))
+    vc, pc, bc = varlen.c(), pred.c(), bm.c()
+    _check(lib().build_block_mask_varlen(ctypes.byref(vc), ctypes.byref(pc), ctypes.byref(bc),
+                                         _stream(stream)))
+    return bm
+
+
+def masked_attn_varlen_fwd(q, k, v, varlen, pred=None, block_mask=None, softmax_scale=None,
+                           return_lse=False, out=None, stream=None):
+    """Attention over packed sequences: q (total_q, H, D), k / v (total_k, KVH, D);
+    returns O (total_q, H, D) and, if asked, LSE (H, total_q)."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v must be 3D (rows, heads, D)")
+    q4, k4, v4 = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    if out is None:
+        out = torch.empty_like(q)
+    o4 = out.unsqueeze(0)
+    lse = torch.empty((1, q.shape[1], q.shape[0]), dtype=torch.float32,
+                      device=q.device) if return_lse else None
+    a = AttnArgs()
+    a.q, a.k, a.v = tensor4(q4), tensor4(k4), tensor4(v4)
+    a.o = o4.data_ptr() if o4.numel() else None
+    for i in range(4):
+        a.o_stride[i] = o4.stride(i)
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.reserved = 0
+    keep = []
+    if pred is not None:
+        pc = pred.c()
+        keep.append(pc)
+        a.pred = ctypes.pointer(pc)
+    if block_mask is not None:
+        bmc = block_mask.c()
+        keep.append(bmc)
+        a.bm = ctypes.pointer(bmc)
+    vc = varlen.c()
+    _check(lib().masked_attn_varlen_fwd(ctypes.byref(vc), ctypes.byref(a), _stream(stream)))
+    return (out, lse[0]) if return_lse else out
+
+
+def unpad(x, valid, stream=None):
+    """Packed rows of a padded (B, S, ...) tensor: returns (packed, indices,
+    cu_seqlens, max_seqlen). The index pass runs on the device; the total is
+    read back to size the packed tensor."""
+    B, S = valid.shape
+    if tuple(x.shape[:2]) != (B, S):
+        raise ValueError("x and valid disagree on (batch, seqlen)")
+    if valid.dtype != torch.bool or valid.stride(1) != 1:
+        raise ValueError("valid must be a bool tensor with contiguous rows")
+    xc = x.contiguous()
+    cu = torch.empty(B + 1, dtype=torch.int32, device=x.device)
+    idx = torch.empty(max(B * S, 1), dtype=torch.int32, device=x.device)
+    _check(lib().unpad_index(valid.data_ptr() if valid.numel() else None, B, S,
+                             valid.stride(0), cu.data_ptr(), idx.data_ptr(), _stream(stream)))
+    cu_host = cu.cpu()
+    total = int(cu_host[-1])
+    lens = cu_host[1:] - cu_host[:-1]
+    row_shape = tuple(x.shape[2:])
+    row_bytes = xc[0, 0].numel() * xc.element_size() if B * S else 0
+    packed = torch.empty((total,) + row_shape, dtype=x.dtype, device=x.device)
+    if total:
+        _check(lib().gather_rows(xc.data_ptr(), row_bytes, packed.data_ptr(), row_bytes,
+                                 row_bytes, idx.data_ptr(), total, _stream(stream)))
+    return packed, idx[:total], cu, int(lens.max()) if B else 0
+
+
+def pad(packed, indices, B, S, stream=None):
+    """(B, S, ...) zeros with packed row i at flat position indices[i]."""
+    pc = packed.contiguous()
+    out = torch.zeros((B, S) + tuple(packed.shape[1:]), dtype=packed.dtype, device=packed.device)
+    n = pc.shape[0]
+    if n:
+        row_bytes = pc[0].numel() * pc.element_size()
+        _check(lib().scatter_rows(pc.data_ptr(), row_bytes, out.data_ptr(), row_bytes,
+                                  row_bytes, indices.data_ptr(), n, _stream(stream)))
+    return out
+

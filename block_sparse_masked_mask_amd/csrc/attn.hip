@@ -72,15 +72,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   const int w = tid >> 6;
   const int n = lane & 31;
   const int hh = lane >> 5;
+  const SeqView seq = seq_view(p, b);
+  if (qt >= seq.nQ) return;  // past a packed sequence's end (uniform)
   const int q = qt * kTile + w * 32 + n;
-  const bool qvalid = q < p.Sq;
+  const bool qvalid = q < seq.Sq;
   const int kvh = h / p.G;
 
   // Q fragment: lane holds row q, d = 16 s + 8 hh + [0, 8)
   bf16x8 qf[NS];
   {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
-                         (int64_t)q * p.q_sq + (int64_t)h * p.q_sh;
+                         (seq.q0 + q) * p.q_sq + (int64_t)h * p.q_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (qvalid)
@@ -90,16 +92,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
     }
   }
   RowIv iv{0, 0, 0, 0};
-  if (p.mask_kind == 1) iv = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+  if (p.mask_kind == 1) iv = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
   const uint8_t* mrow =
       (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
   const uint16_t* brow = (p.has_bias && qvalid)
       ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
 
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
-                        (int64_t)kvh * p.k_sh;
+                        seq.k0 * p.k_sk + (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
-                        (int64_t)kvh * p.v_sh;
+                        seq.k0 * p.v_sk + (int64_t)kvh * p.v_sh;
 
   f32x16 oacc[NDC];
 #pragma unroll
@@ -108,13 +110,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   float l_run = 0.f;
 
   TileList tl;
-  tl.init(p, b, h, qt);
+  tl.init(p, b, h, qt, seq.nK);
   const int ntiles = tl.count();
   for (int it = 0; it < ntiles; ++it) {
     bool is_full;
     const int kt = tl.tile(it, is_full);
     const int64_t k0 = (int64_t)kt * kTile;
-    const bool check_k = k0 + kTile > p.Sk;
+    const bool check_k = k0 + kTile > seq.Sk;
     const bool check_mask = !is_full && p.mask_kind != 0;
 
     __syncthreads();  // previous tile's LDS reads are done
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
       const int c8 = c % (D / 8);
       const int64_t key = k0 + r;
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < p.Sk) val = *reinterpret_cast<const uint4*>(kbase + key * p.k_sk + c8 * 8);
+      if (key < seq.Sk) val = *reinterpret_cast<const uint4*>(kbase + key * p.k_sk + c8 * 8);
       *reinterpret_cast<uint4*>(&sm.k[r * KP + c8 * 8]) = val;
     }
     // V tile -> LDS, transposed: item = 4 keys x 8 dims
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
       for (int j = 0; j < 4; ++j) {
         const int64_t key = k0 + 4 * kq + j;
         uint4 val = make_uint4(0, 0, 0, 0);
-        if (key < p.Sk) val = *reinterpret_cast<const uint4*>(vbase + key * p.v_sk + oct * 8);
+        if (key < seq.Sk) val = *reinterpret_cast<const uint4*>(vbase + key * p.v_sk + oct * 8);
         rw[j][0] = val.x;
         rw[j][1] = val.y;
         rw[j][2] = val.z;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
           if (check_k) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (kb + e >= p.Sk) mbits &= ~(1u << e);
+              if (kb + e >= seq.Sk) mbits &= ~(1u << e);
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   if (qvalid) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb +
-                   (int64_t)q * p.o_sq + (int64_t)h * p.o_sh;
+                   (seq.q0 + q) * p.o_sq + (int64_t)h * p.o_sh;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
     }
     if (p.lse && hh == 0) {
       const float lse = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (seq.q0 + q) * p.lse_sq] = lse;
     }
   }
 }
@@ -307,28 +309,30 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int part = tid & 3;
+  const SeqView seq = seq_view(p, b);
+  if (rt * kF32Rows >= seq.Sq) return;  // past a packed sequence's end (uniform)
   const int q = rt * kF32Rows + (tid >> 2);
-  const bool qvalid = q < p.Sq;
+  const bool qvalid = q < seq.Sq;
   const int kvh = h / p.G;
   const int qt = (rt * kF32Rows) / kTile;
 
   float qv[DS];
   {
     const float* qrow = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.q_sb +
-                        (int64_t)q * p.q_sq + (int64_t)h * p.q_sh + part * DS;
+                        (seq.q0 + q) * p.q_sq + (int64_t)h * p.q_sh + part * DS;
 #pragma unroll
     for (int i = 0; i < DS; ++i) qv[i] = qvalid ? qrow[i] : 0.f;
   }
   RowIv iv{0, 0, 0, 0};
-  if (p.mask_kind == 1) iv = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+  if (p.mask_kind == 1) iv = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
   const uint8_t* mrow =
       (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
   const float* brow = (p.has_bias && qvalid)
       ? reinterpret_cast<const float*>(aux_row(p.bias, 4, b, h, p.G, q)) : nullptr;
   const float* kbase = reinterpret_cast<const float*>(p.k) + (int64_t)b * p.k_sb +
-                       (int64_t)kvh * p.k_sh;
+                       seq.k0 * p.k_sk + (int64_t)kvh * p.k_sh;
   const float* vbase = reinterpret_cast<const float*>(p.v) + (int64_t)b * p.v_sb +
-                       (int64_t)kvh * p.v_sh;
+                       seq.k0 * p.v_sk + (int64_t)kvh * p.v_sh;
 
   float o[DS];
 #pragma unroll
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   TileList tl;
-  tl.init(p, b, h, qt);
+  tl.init(p, b, h, qt, seq.nK);
   const int ntiles = tl.count();
   for (int it = 0; it < ntiles; ++it) {
     bool is_full;
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         const int c4 = c % (D / 4);
         const int64_t key = k0 + r;
         float4 kv4 = make_float4(0, 0, 0, 0), vv4 = make_float4(0, 0, 0, 0);
-        if (key < p.Sk) {
+        if (key < seq.Sk) {
           kv4 = *reinterpret_cast<const float4*>(kbase + key * p.k_sk + c4 * 4);
           vv4 = *reinterpret_cast<const float4*>(vbase + key * p.v_sk + c4 * 4);
         }
@@ -370,8 +374,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         acc += __shfl_xor(acc, 2, 64);
         const int64_t key = k0 + j;
         float sc = acc * p.scale_log2;
-        if (brow && key < p.Sk) sc += brow[key] * kLog2e;
-        bool keep = qvalid && key < p.Sk;
+        if (brow && key < seq.Sk) sc += brow[key] * kLog2e;
+        bool keep = qvalid && key < seq.Sk;
         if (keep && check_mask) {
           if (p.mask_kind == 2)
             keep = mrow[key] != 0;
@@ -401,12 +405,12 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
   }
   if (qvalid) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* orow = reinterpret_cast<float*>(p.o) + (int64_t)b * p.o_sb + (int64_t)q * p.o_sq +
+    float* orow = reinterpret_cast<float*>(p.o) + (int64_t)b * p.o_sb + (seq.q0 + q) * p.o_sq +
                   (int64_t)h * p.o_sh + part * DS;
 #pragma unroll
     for (int i = 0; i < DS; ++i) orow[i] = o[i] * inv;
     if (p.lse && part == 0)
-      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] =
+      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (seq.q0 + q) * p.lse_sq] =
           l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }

@@ -24,6 +24,45 @@ __device__ inline const uint8_t* aux_row(const AuxView& a, int64_t elem, int b, 
   return reinterpret_cast<const uint8_t*>(a.data) + off * elem;
 }
 
+// One sequence of a launch. Padded batches: batch b's rows start at 0 and
+// every batch has the launch's Sq / Sk. Packed (varlen) launches: sequence b
+// owns query rows cu_q[b] .. cu_q[b+1] and key rows cu_k[b] .. cu_k[b+1] of
+// one packed batch (batch strides 0), and a DFlash rule is completed per
+// sequence: C_b = Sk_b - Sq_b context tokens, NB_b = Sq_b / bs blocks, and
+// S_b = C_b / NB_b unless the launch fixes it (rule.S > 0).
+struct SeqView {
+  int64_t q0, k0;  // first packed query row / key row
+  int Sq, Sk, nQ, nK;
+  DFlashRule rule;
+};
+
+__device__ inline SeqView seq_view(const AttnParams& p, int b) {
+  SeqView s;
+  s.rule = p.rule;
+  if (p.varlen) {
+    const int a = p.cu_q[b], e = p.cu_q[b + 1];
+    const int c = p.cu_k[b], d = p.cu_k[b + 1];
+    s.q0 = a;
+    s.k0 = c;
+    s.Sq = e - a;
+    s.Sk = d - c;
+    if (p.mask_kind == 1) {  // 32-bit arithmetic: packed sizes stay below 2^30
+      const int C = s.Sk - s.Sq;
+      const int nb = s.Sq / (int)p.rule.bs;
+      s.rule.C = C;
+      if (p.rule.S == 0) s.rule.S = nb > 0 ? C / nb : 0;
+    }
+  } else {
+    s.q0 = 0;
+    s.k0 = 0;
+    s.Sq = p.Sq;
+    s.Sk = p.Sk;
+  }
+  s.nQ = (s.Sq + kTile - 1) / kTile;
+  s.nK = (s.Sk + kTile - 1) / kTile;
+  return s;
+}
+
 // Key tiles visited by query tile qt of (b, h): first the full tiles, then the
 // partial ones. Without a block mask every key tile is visited, as partial when
 // a mask is present and as full otherwise.
@@ -32,7 +71,9 @@ struct TileList {
   const int32_t* part;
   int nfull, npart;
 
-  __device__ inline void init(const AttnParams& p, int b, int h, int qt) {
+  // nK: key tiles of the sequence when there is no block mask (-1: p.nK)
+  __device__ inline void init(const AttnParams& p, int b, int h, int qt, int nK = -1) {
+    if (nK < 0) nK = p.nK;
     if (p.has_bm) {
       const BlockMaskView& m = p.bm;
       const int64_t mb = m.Bm == 1 ? 0 : b;
@@ -46,11 +87,11 @@ struct TileList {
     } else {
       full = part = nullptr;
       if (p.mask_kind == 0) {
-        nfull = p.nK;
+        nfull = nK;
         npart = 0;
       } else {
         nfull = 0;
-        npart = p.nK;
+        npart = nK;
       }
     }
   }

@@ -478,7 +478,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
 
 bool attn_decode_applies(const AttnParams& p, int D) {
   if (D != 64 && D != 128) return false;
-  if (p.Sq > 32) return false;
+  if (p.Sq > 32 || p.varlen) return false;
   if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
   if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
   return true;

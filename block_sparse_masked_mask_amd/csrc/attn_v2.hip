@@ -84,12 +84,12 @@ struct LaneOffs {
 template <int D, int RB>
 __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
                                     bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
-                                    int lane) {
+                                    int lane, int Sk) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
   const int hh = lane >> 5;
   const int k0 = kt * kTile;
-  const bool check_k = k0 + kTile > p.Sk;
+  const bool check_k = k0 + kTile > Sk;
   const bool check_mask = !is_full && p.mask_kind != 0;
   const char* kbase = reinterpret_cast<const char*>(t.k);
   const char* vbase = reinterpret_cast<const char*>(t.v);
@@ -179,7 +179,7 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
               }
             }
             if (!R.qvalid) mbits = 0;
-            if (check_k) mbits &= range_bits(0, p.Sk, kb);
+            if (check_k) mbits &= range_bits(0, Sk, kb);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int u = 8 * sb + e;
@@ -262,7 +262,14 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   const int pairs = p.G / 2;
   const int ngrp = nWork / p.nQ;
   int qt, grp;
-  if (ngrp % kXcds == 0) {
+  if (p.varlen) {
+    // Packed sequences differ in cost: spread each sequence's groups over the
+    // XCDs (group g on XCD g % 8 when the group count is a multiple of 8) and
+    // run every group's heaviest (last) query tiles first; tiles past a
+    // sequence's end exit at once.
+    grp = L % ngrp;
+    qt = p.nQ - 1 - L / ngrp;
+  } else if (ngrp % kXcds == 0) {
     const int gx = ngrp / kXcds;
     const int li = L / kXcds;
     qt = p.nQ - 1 - li / gx;
@@ -278,6 +285,8 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   grp /= pairs;
   const int kvh = grp % p.KVH;
   const int b = grp / p.KVH;
+  const SeqView seq = seq_view(p, b);
+  if (qt >= seq.nQ) return;  // past a packed sequence's end (uniform)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,15 +300,15 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   for (int r = 0; r < RB; ++r) {
     RowBlock<D>& R = rbk[r];
     const int q = qt * kTile + ((w % WPH) * RB + r) * 32 + n;
-    R.qvalid = q < p.Sq;
+    R.qvalid = q < seq.Sq;
     const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
-                         (int64_t)q * p.q_sq + (int64_t)h * p.q_sh;
+                         (seq.q0 + q) * p.q_sq + (int64_t)h * p.q_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       R.qf[s] = R.qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
     R.iv = RowIv32{0, 0, 0, 0};
     if (p.mask_kind == 1) {
-      const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
+      const RowIv v = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
       R.iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
     }
     R.mrow = (p.mask_kind == 2 && R.qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
@@ -311,16 +320,16 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     R.l_run = 0.f;
   }
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
-                        (int64_t)kvh * p.k_sh;
+                        seq.k0 * p.k_sk + (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
-                        (int64_t)kvh * p.v_sh;
+                        seq.k0 * p.v_sk + (int64_t)kvh * p.v_sh;
   LaneOffs<D> off;
   off.init(lane);
   Loader<D, RB> ld;
-  ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+  ld.init(kbase, vbase, p.k_sk, p.v_sk, seq.Sk, w, lane);
 
   TileList tl;
-  tl.init(p, b, kvh * p.G + 2 * hp, qt);  // identical for both heads of the pair
+  tl.init(p, b, kvh * p.G + 2 * hp, qt, seq.nK);  // identical for both heads of the pair
   const int ntiles = tl.count();
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
-    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane);
+    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   }
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     if (R.qvalid) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb +
-                     (int64_t)q * p.o_sq + (int64_t)h * p.o_sh;
+                     (seq.q0 + q) * p.o_sq + (int64_t)h * p.o_sh;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
       if (p.lse && hh == 0) {
         const float lse =
             l_tot > 0.f ? (R.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-        p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] = lse;
+        p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (seq.q0 + q) * p.lse_sq] = lse;
       }
     }
   }

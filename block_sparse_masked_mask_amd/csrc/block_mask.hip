@@ -76,13 +76,16 @@ __device__ inline void compact_row(int nK, CodeFn code_of, int32_t* prow,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_block_mask_pred(
-    DFlashRule r, int64_t Sq, int nK, int32_t* kv_num, int32_t* kv_idx,
-    int32_t* full_num, int32_t* full_idx) {
+// Partial / full key tiles of query tile qt of one DFlash sequence of Sq
+// queries whose keys fill nKs tiles; the row holds nK entries (nK >= nKs, the
+// rest empty). A query tile past the sequence's end has no tiles.
+__device__ inline void pred_tile_row(const DFlashRule& r, int64_t Sq, int qt, int nKs, int nK,
+                                     int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
+                                     int32_t* full_idx) {
   __shared__ int64_t s_iv[kTile][4];
-  const int qt = blockIdx.x;
   const int64_t r0 = (int64_t)qt * kTile;
-  const int rows = (int)(Sq - r0 < kTile ? Sq - r0 : kTile);
+  const int64_t left = Sq - r0;
+  const int rows = (int)(left < 0 ? 0 : (left < kTile ? left : kTile));
   for (int t = threadIdx.x; t < rows; t += kThreads) {
     const RowIv v = dflash_row(r, r0 + t);
     s_iv[t][0] = v.lo1;
@@ -92,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mask_pred(
   }
   __syncthreads();
   auto code_of = [&](int kt) {
+    if (kt >= nKs) return 0;
     const int64_t k0 = (int64_t)kt * kTile;
     int64_t cnt = 0;
     for (int t = 0; t < rows; ++t)
@@ -99,8 +103,35 @@ __global__ __launch_bounds__(kThreads) void k_block_mask_pred(
              iv_overlap(s_iv[t][2], s_iv[t][3], k0, kTile);
     return cnt == 0 ? 0 : (cnt == (int64_t)rows * kTile ? 2 : 1);
   };
-  compact_row(nK, code_of, kv_idx + (int64_t)qt * nK,
-              full_idx + (int64_t)qt * nK, kv_num + qt, full_num + qt);
+  compact_row(nK, code_of, kv_idx, full_idx, kv_num, full_num);
+}
+
+__global__ __launch_bounds__(kThreads) void k_block_mask_pred(
+    DFlashRule r, int64_t Sq, int nK, int32_t* kv_num, int32_t* kv_idx,
+    int32_t* full_num, int32_t* full_idx) {
+  const int qt = blockIdx.x;
+  pred_tile_row(r, Sq, qt, nK, nK, kv_num + qt, kv_idx + (int64_t)qt * nK, full_num + qt,
+                full_idx + (int64_t)qt * nK);
+}
+
+// Packed sequences: workgroup (qt, b) builds row (b, qt) from sequence b's own
+// geometry (C_b = Sk_b - Sq_b, S_b = C_b / NB_b unless fixed).
+__global__ __launch_bounds__(kThreads) void k_block_mask_pred_varlen(
+    DFlashRule r, const int32_t* cu_q, const int32_t* cu_k, int nQ, int nK,
+    int32_t* kv_num, int32_t* kv_idx, int32_t* full_num, int32_t* full_idx) {
+  const int qt = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t Sq = cu_q[b + 1] - cu_q[b];
+  const int64_t Sk = cu_k[b + 1] - cu_k[b];
+  DFlashRule sr = r;
+  sr.C = Sk - Sq;
+  if (r.S == 0) {
+    const int64_t nb = Sq / r.bs;
+    sr.S = nb > 0 ? sr.C / nb : 0;
+  }
+  const int64_t row = (int64_t)b * nQ + qt;
+  pred_tile_row(sr, Sq, qt, (int)((Sk + kTile - 1) / kTile), nK, kv_num + row,
+                kv_idx + row * nK, full_num + row, full_idx + row * nK);
 }
 
 __global__ __launch_bounds__(kThreads) void k_dflash_dense(DFlashRule r, int64_t Sq,
@@ -242,6 +273,16 @@ hipError_t launch_block_mask_pred(const DFlashRule& r, int64_t Sq, int64_t Sk,
   if (nQ == 0) return hipSuccess;
   hipLaunchKernelGGL(k_block_mask_pred, dim3((unsigned)nQ), dim3(kThreads), 0, s, r,
                      Sq, (int)nK, kv_num, kv_idx, full_num, full_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mask_pred_varlen(const DFlashRule& r, const int32_t* cu_q,
+                                         const int32_t* cu_k, int64_t B, int64_t nQ,
+                                         int64_t nK, int32_t* kv_num, int32_t* kv_idx,
+                                         int32_t* full_num, int32_t* full_idx, hipStream_t s) {
+  if (B == 0 || nQ == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_mask_pred_varlen, dim3((unsigned)nQ, (unsigned)B), dim3(kThreads),
+                     0, s, r, cu_q, cu_k, (int)nQ, (int)nK, kv_num, kv_idx, full_num, full_idx);
   return hipGetLastError();
 }
 

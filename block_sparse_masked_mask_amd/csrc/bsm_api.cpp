@@ -749,3 +749,256 @@ int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_
 }
 
 }  // extern "C"
+
+// ---- packed variable-length sequences
+
+namespace {
+
+struct VarlenInfo {
+  int64_t B, maxSq, maxSk, nQ, nK;
+};
+
+int check_varlen(const bsm_varlen* vl, VarlenInfo& vi) {
+  if (!vl) return fail(BSM_E_ARG, "varlen is NULL");
+  if (vl->num_seqs < 0 || vl->H < 1 || vl->KVH < 1 || vl->D < 1 || vl->total_q < 0 ||
+      vl->total_k < 0)
+    return fail(BSM_E_SHAPE, "bad varlen sizes");
+  if (vl->H % vl->KVH)
+    return fail(BSM_E_SHAPE, "H=%lld is not a multiple of KVH=%lld", (long long)vl->H,
+                (long long)vl->KVH);
+  if (vl->num_seqs > 65535 || vl->H > 65535 || vl->total_q > INT32_MAX / 2 ||
+      vl->total_k > INT32_MAX / 2)
+    return fail(BSM_E_UNSUPPORTED, "varlen sizes beyond this build's limits");
+  const int64_t B = vl->num_seqs;
+  if (!vl->cu_seqlens_q_host || !vl->cu_seqlens_k_host || !vl->cu_seqlens_q ||
+      !vl->cu_seqlens_k)
+    return fail(BSM_E_ARG, "cu_seqlens arrays (device and host) are required");
+  const int32_t* cq = vl->cu_seqlens_q_host;
+  const int32_t* ck = vl->cu_seqlens_k_host;
+  if (cq[0] != 0 || ck[0] != 0) return fail(BSM_E_ARG, "cu_seqlens must start at 0");
+  vi.B = B;
+  vi.maxSq = vi.maxSk = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t sq = (int64_t)cq[b + 1] - cq[b];
+    const int64_t sk = (int64_t)ck[b + 1] - ck[b];
+    if (sq < 0 || sk < 0) return fail(BSM_E_ARG, "cu_seqlens must be nondecreasing");
+    vi.maxSq = sq > vi.maxSq ? sq : vi.maxSq;
+    vi.maxSk = sk > vi.maxSk ? sk : vi.maxSk;
+  }
+  if (cq[B] != vl->total_q || ck[B] != vl->total_k)
+    return fail(BSM_E_SHAPE, "cu_seqlens end at %d / %d, total_q / total_k are %lld / %lld",
+                cq[B], ck[B], (long long)vl->total_q, (long long)vl->total_k);
+  vi.nQ = (vi.maxSq + kTile - 1) / kTile;
+  vi.nK = (vi.maxSk + kTile - 1) / kTile;
+  return BSM_OK;
+}
+
+// Per-sequence DFlash rule: the shared fields, C and (when 0) S left to the
+// kernels; every sequence must have a DFlash layout.
+int check_dflash_varlen(const bsm_dflash* d, const bsm_varlen* vl, DFlashRule& r) {
+  if (d->ctx_len != 0 || d->num_blocks != 0)
+    return fail(BSM_E_ARG, "varlen DFlash: ctx_len and num_blocks must be 0 (per sequence)");
+  if (d->block_size < 1 || d->ctx_per_block < 0)
+    return fail(BSM_E_ARG, "bad DFlash block_size / ctx_per_block");
+  const int c = resolve_causal(d->is_causal, d->layer_type);
+  if (c < 0)
+    return fail(BSM_E_ARG, "bad is_causal=%d / layer_type=%d", d->is_causal, d->layer_type);
+  if (d->layer_type == 1 && d->sliding_window < 1)
+    return fail(BSM_E_ARG, "sliding layer needs sliding_window >= 1");
+  const int32_t* cq = vl->cu_seqlens_q_host;
+  const int32_t* ck = vl->cu_seqlens_k_host;
+  for (int64_t b = 0; b < vl->num_seqs; ++b) {
+    const int64_t sq = (int64_t)cq[b + 1] - cq[b];
+    const int64_t sk = (int64_t)ck[b + 1] - ck[b];
+    if (sq % d->block_size || sk < sq)
+      return fail(BSM_E_SHAPE, "sequence %lld (%lld queries, %lld keys) is not a DFlash layout "
+                  "with blocks of %lld", (long long)b, (long long)sq, (long long)sk,
+                  (long long)d->block_size);
+    const int64_t nb = sq / d->block_size;
+    if (d->ctx_per_block == 0 && nb > 0 && (sk - sq) % nb)
+      return fail(BSM_E_SHAPE, "sequence %lld: ctx_per_block=0 needs its context (%lld) to be a "
+                  "multiple of its %lld blocks", (long long)b, (long long)(sk - sq),
+                  (long long)nb);
+  }
+  r.C = 0;
+  r.bs = d->block_size;
+  r.S = d->ctx_per_block;
+  r.e0 = d->ctx_end_offset;
+  r.W = d->layer_type == 1 ? d->sliding_window : 0;
+  r.causal = c;
+  r.pad = 0;
+  return BSM_OK;
+}
+
+int check_copy(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+               int64_t row_bytes, const int32_t* idx, int64_t n) {
+  if (n < 0 || row_bytes < 0) return fail(BSM_E_ARG, "negative row count or size");
+  if (n == 0 || row_bytes == 0) return BSM_OK;
+  if (!src || !dst || !idx) return fail(BSM_E_ARG, "src, dst or indices is NULL");
+  if (row_bytes % 16 || src_stride % 16 || dst_stride % 16 || (uintptr_t)src % 16 ||
+      (uintptr_t)dst % 16)
+    return fail(BSM_E_STRIDE, "rows, strides and pointers must be multiples of 16 bytes");
+  if (src_stride < row_bytes || dst_stride < row_bytes)
+    return fail(BSM_E_STRIDE, "row stride smaller than the row");
+  return BSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int block_mask_varlen_shape(const bsm_varlen* vl, const bsm_dflash* pred, int64_t out_shape[4]) {
+  VarlenInfo vi;
+  int e = check_varlen(vl, vi);
+  if (e) return e;
+  if (!pred || !out_shape) return fail(BSM_E_ARG, "pred or out_shape is NULL");
+  DFlashRule r;
+  if ((e = check_dflash_varlen(pred, vl, r))) return e;
+  if (vi.nK > 65536) return fail(BSM_E_UNSUPPORTED, "more than 65536 key tiles");
+  out_shape[0] = vi.B;
+  out_shape[1] = 1;
+  out_shape[2] = vi.nQ;
+  out_shape[3] = vi.nK;
+  return BSM_OK;
+}
+
+int build_block_mask_varlen(const bsm_varlen* vl, const bsm_dflash* pred,
+                            const bsm_block_mask* out, hipStream_t stream) {
+  int64_t shp[4];
+  int e = block_mask_varlen_shape(vl, pred, shp);
+  if (e) return e;
+  if (!out) return fail(BSM_E_ARG, "out is NULL");
+  if (out->Bm != shp[0] || out->Hm != shp[1] || out->nQm != shp[2] || out->nK != shp[3])
+    return fail(BSM_E_SHAPE, "block mask dims (%lld,%lld,%lld,%lld) expected (%lld,%lld,%lld,%lld)",
+                (long long)out->Bm, (long long)out->Hm, (long long)out->nQm, (long long)out->nK,
+                (long long)shp[0], (long long)shp[1], (long long)shp[2], (long long)shp[3]);
+  if (shp[0] * shp[2] > 0 && (!out->kv_num_blocks || !out->full_kv_num_blocks ||
+                              (shp[3] > 0 && (!out->kv_indices || !out->full_kv_indices))))
+    return fail(BSM_E_ARG, "block mask buffer is NULL");
+  DFlashRule r;
+  check_dflash_varlen(pred, vl, r);
+  return hip_status(launch_block_mask_pred_varlen(r, vl->cu_seqlens_q, vl->cu_seqlens_k, shp[0],
+                                                  shp[2], shp[3], out->kv_num_blocks,
+                                                  out->kv_indices, out->full_kv_num_blocks,
+                                                  out->full_kv_indices, stream),
+                    "build_block_mask_varlen");
+}
+
+int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* a, hipStream_t stream) {
+  VarlenInfo vi;
+  int e = check_varlen(vl, vi);
+  if (e) return e;
+  if (!a) return fail(BSM_E_ARG, "args is NULL");
+  if (a->reserved != 0) return fail(BSM_E_ARG, "args.reserved must be 0");
+  if (vl->D != 64 && vl->D != 128)
+    return fail(BSM_E_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)vl->D);
+  if (a->mask || a->bias || a->keys)
+    return fail(BSM_E_UNSUPPORTED, "varlen attention takes a DFlash predicate or no mask");
+  const int32_t dt = a->q.dtype;
+  if (dt != BSM_BF16 && dt != BSM_F32) return fail(BSM_E_DTYPE, "q must be bf16 or f32");
+  if ((e = check_tensor_qkv(&a->q, "q", 1, vl->total_q, vl->H, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->k, "k", 1, vl->total_k, vl->KVH, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->v, "v", 1, vl->total_k, vl->KVH, vl->D, dt))) return e;
+  {
+    bsm_tensor4 o{};
+    o.data = a->o;
+    o.dtype = dt;
+    o.size[0] = 1;
+    o.size[1] = vl->total_q;
+    o.size[2] = vl->H;
+    o.size[3] = vl->D;
+    for (int i = 0; i < 4; ++i) o.stride[i] = a->o_stride[i];
+    if ((e = check_tensor_qkv(&o, "o", 1, vl->total_q, vl->H, vl->D, dt))) return e;
+  }
+  if (std::isnan(a->softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
+  AttnInputs in;
+  if (a->pred && (e = check_dflash_varlen(a->pred, vl, in.rule))) return e;
+  if (a->bm) {
+    if (!a->pred) return fail(BSM_E_ARG, "a block mask needs pred");
+    const bsm_block_mask* bm = a->bm;
+    if (bm->Bm != vi.B || bm->Hm != 1 || bm->nQm != vi.nQ || bm->nK != vi.nK)
+      return fail(BSM_E_SHAPE, "block mask dims do not match these sequences");
+    if (vi.B * vi.nQ > 0 && (!bm->kv_num_blocks || !bm->full_kv_num_blocks ||
+                             (vi.nK > 0 && (!bm->kv_indices || !bm->full_kv_indices))))
+      return fail(BSM_E_ARG, "block mask buffer is NULL");
+    in.bmv.kv_num = bm->kv_num_blocks;
+    in.bmv.kv_idx = bm->kv_indices;
+    in.bmv.full_num = bm->full_kv_num_blocks;
+    in.bmv.full_idx = bm->full_kv_indices;
+    in.bmv.Bm = bm->Bm;
+    in.bmv.Hm = 1;
+    in.bmv.nQm = bm->nQm;
+    in.bmv.nK = bm->nK;
+    in.bmv.h_mode = 0;
+  }
+  if (vi.B == 0 || vl->total_q == 0) return BSM_OK;
+
+  // Geometry of the launch: one "batch" per sequence, the longest sequence's
+  // tile counts, and the packed tensors' row strides with batch strides 0.
+  Geo g{};
+  g.B = vi.B;
+  g.H = vl->H;
+  g.KVH = vl->KVH;
+  g.Sq = vl->total_q;
+  g.Sk = vl->total_k;
+  g.D = vl->D;
+  g.G = vl->H / vl->KVH;
+  g.swap = false;
+  AttnParams p;
+  fill_params(g, a->q, a->k, a->v, a->o, a->o_stride, a->lse, a->softmax_scale, a->pred,
+              false, false, a->bm, in, p);
+  p.q_sb = p.k_sb = p.v_sb = p.o_sb = 0;
+  p.lse_sb = 0;
+  p.lse_sh = vl->total_q;
+  p.lse_sq = 1;
+  p.Sq = (int32_t)vi.maxSq;
+  p.nQ = (int32_t)vi.nQ;
+  p.Sk = (int32_t)vl->total_k;  // bounds the 32-bit offset checks
+  p.nK = (int32_t)vi.nK;
+  p.varlen = 1;
+  p.cu_q = vl->cu_seqlens_q;
+  p.cu_k = vl->cu_seqlens_k;
+  hipError_t he;
+  if (dt == BSM_BF16) {
+    if (attn_v2_applies(p, (int)g.D))
+      he = launch_attn_bf16_v2(p, (int)g.D, stream);
+    else
+      he = launch_attn_bf16(p, (int)g.D, stream);
+  } else {
+    he = launch_attn_f32(p, (int)g.D, stream);
+  }
+  return hip_status(he, "masked_attn_varlen_fwd");
+}
+
+int unpad_index(const uint8_t* valid, int64_t batch, int64_t seqlen, int64_t row_stride,
+                int32_t* cu_seqlens, int32_t* indices, hipStream_t stream) {
+  if (batch < 0 || seqlen < 0) return fail(BSM_E_ARG, "negative batch or seqlen");
+  if (batch > 65535 || batch * seqlen >= ((int64_t)1 << 31))
+    return fail(BSM_E_UNSUPPORTED, "batch * seqlen must stay below 2^31");
+  if (!cu_seqlens) return fail(BSM_E_ARG, "cu_seqlens is NULL");
+  if (batch * seqlen > 0 && (!valid || !indices)) return fail(BSM_E_ARG, "valid or indices is NULL");
+  if (batch > 1 && row_stride < seqlen) return fail(BSM_E_STRIDE, "row_stride below seqlen");
+  return hip_status(launch_unpad_index(valid, batch, seqlen, row_stride, cu_seqlens, indices,
+                                       stream),
+                    "unpad_index");
+}
+
+int gather_rows(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+                int64_t row_bytes, const int32_t* indices, int64_t n, hipStream_t stream) {
+  int e = check_copy(src, src_stride, dst, dst_stride, row_bytes, indices, n);
+  if (e) return e;
+  return hip_status(launch_copy_rows(src, src_stride, dst, dst_stride, row_bytes, indices, n,
+                                     false, stream),
+                    "gather_rows");
+}
+
+int scatter_rows(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+                 int64_t row_bytes, const int32_t* indices, int64_t n, hipStream_t stream) {
+  int e = check_copy(src, src_stride, dst, dst_stride, row_bytes, indices, n);
+  if (e) return e;
+  return hip_status(launch_copy_rows(src, src_stride, dst, dst_stride, row_bytes, indices, n,
+                                     true, stream),
+                    "scatter_rows");
+}
+
+}  // extern "C"

@@ -76,8 +76,10 @@ struct AttnParams {
   int32_t has_bm;
   BlockMaskView bm;
   int32_t gather;   // visit the keys of `keys` instead of key tiles
-  int32_t pad2;
+  int32_t varlen;   // packed sequences: cu_q / cu_k give each one's rows
   KeyListView keys;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
 };
 
 // Backward: the forward's view plus the incoming gradient, the gradient
@@ -146,6 +148,19 @@ hipError_t launch_block_mask_pred(const DFlashRule& r, int64_t Sq, int64_t Sk,
                                   int64_t nQ, int64_t nK, int32_t* kv_num,
                                   int32_t* kv_idx, int32_t* full_num,
                                   int32_t* full_idx, hipStream_t s);
+// one block-mask row per (sequence, query tile); rule.C is completed per
+// sequence from cu_q / cu_k, and rule.S too when it is 0
+hipError_t launch_block_mask_pred_varlen(const DFlashRule& r, const int32_t* cu_q,
+                                         const int32_t* cu_k, int64_t B, int64_t nQ,
+                                         int64_t nK, int32_t* kv_num, int32_t* kv_idx,
+                                         int32_t* full_num, int32_t* full_idx, hipStream_t s);
+// packing helpers: cu_seqlens / indices of a (batch, seqlen) validity mask,
+// and 16-byte row copies through an index list (scatter: dst[idx[i]] = src[i])
+hipError_t launch_unpad_index(const uint8_t* valid, int64_t batch, int64_t seqlen,
+                              int64_t row_stride, int32_t* cu, int32_t* idx, hipStream_t s);
+hipError_t launch_copy_rows(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+                            int64_t row_bytes, const int32_t* idx, int64_t n, bool scatter,
+                            hipStream_t s);
 hipError_t launch_dflash_dense(const DFlashRule& r, int64_t Sq, int64_t Sk,
                                int64_t K, uint8_t* out, hipStream_t s);
 hipError_t launch_block_mask_dense(const DenseMaskView& m, int32_t* kv_num,

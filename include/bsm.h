@@ -277,6 +277,70 @@ int attn_bwd_workspace_size(const bsm_geom* geom, const bsm_attn_bwd_args* args,
 int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* args,
                     hipStream_t stream);
 
+/* ---- Packed variable-length sequences ([FSA-197] Changes: the integration's
+ * varlen attention entry point and its pad / unpad helpers; [SF-452] traceback:
+ * a block mask with one entry per batch element, Bm = B). */
+
+/* Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of a packed
+ * Q / O of sizes (1, total_q, H, D) and key rows [cu_seqlens_k[b],
+ * cu_seqlens_k[b+1]) of a packed K / V of sizes (1, total_k, KVH, D), and
+ * attends to its own keys only. The cu arrays (num_seqs + 1 int32, starting at
+ * 0, nondecreasing, ending at total_q / total_k) are given twice: on the
+ * device for the kernels and on the host for validation and launch sizing;
+ * both copies must hold the same values. */
+typedef struct {
+  int64_t num_seqs, H, KVH, D;
+  int64_t total_q, total_k;
+  const int32_t* cu_seqlens_q;       /* device */
+  const int32_t* cu_seqlens_k;       /* device */
+  const int32_t* cu_seqlens_q_host;  /* host */
+  const int32_t* cu_seqlens_k_host;  /* host */
+} bsm_varlen;
+
+/* Per-sequence DFlash geometry: pred.ctx_len and pred.num_blocks must be 0;
+ * sequence b is NB_b = Sq_b / block_size draft blocks after C_b = Sk_b - Sq_b
+ * context tokens (Sq_b a multiple of block_size, Sk_b >= Sq_b), with
+ * S_b = ctx_per_block, or C_b / NB_b when ctx_per_block is 0 (then NB_b must
+ * divide C_b); is_causal, layer_type, sliding_window and ctx_end_offset are
+ * shared. Block mask dims: (num_seqs, 1, max_b ceil(Sq_b / 128),
+ * max_b ceil(Sk_b / 128)); row b lists sequence b's own tiles, its query
+ * tiles past ceil(Sq_b / 128) are empty. Host only. */
+int block_mask_varlen_shape(const bsm_varlen* vl, const bsm_dflash* pred, int64_t out_shape[4]);
+
+/* Build that block mask on the device (never materialising a mask). */
+int build_block_mask_varlen(const bsm_varlen* vl, const bsm_dflash* pred,
+                            const bsm_block_mask* out, hipStream_t stream);
+
+/* Masked attention forward over packed sequences: as masked_attn_fwd applied
+ * to each sequence alone. args.q / o are (1, total_q, H, D), args.k / v
+ * (1, total_k, KVH, D), args.lse (if not NULL) float (1, H, total_q)
+ * contiguous. Mask source: args.pred with the per-sequence geometry above, or
+ * none; args.bm NULL or built by build_block_mask_varlen for the same
+ * sequences; args.mask, args.bias and args.keys must be NULL
+ * (BSM_E_UNSUPPORTED). No head-group swap is applied. */
+int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* args, hipStream_t stream);
+
+/* Packing index of a padded batch: valid is a device bool array (batch,
+ * seqlen) with row b at valid + b * row_stride (bytes). Writes cu_seqlens
+ * (batch + 1 int32: cu_seqlens[b] = valid positions in rows 0 .. b-1) and
+ * indices[i] = b * seqlen + s of the i-th valid position in row-major order
+ * (int32, room for batch * seqlen entries; entries past the total are left
+ * unspecified). The unpad of [FSA-197] Changes; batch * seqlen < 2^31. */
+int unpad_index(const uint8_t* valid, int64_t batch, int64_t seqlen, int64_t row_stride,
+                int32_t* cu_seqlens, int32_t* indices, hipStream_t stream);
+
+/* dst row i = src row indices[i] for i < n (unpad). Rows of row_bytes bytes at
+ * src + r * src_stride and dst + i * dst_stride; pointers, strides and
+ * row_bytes multiples of 16; indices in [0, src rows) are the caller's
+ * promise. */
+int gather_rows(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+                int64_t row_bytes, const int32_t* indices, int64_t n, hipStream_t stream);
+
+/* dst row indices[i] = src row i for i < n (pad; rows not listed are left as
+ * they are, so a zero-filled dst gives the padded batch). Same layout rules. */
+int scatter_rows(const void* src, int64_t src_stride, void* dst, int64_t dst_stride,
+                 int64_t row_bytes, const int32_t* indices, int64_t n, hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call into the library on this thread. */
 const char* bsm_last_error(void);

@@ -56,7 +56,7 @@ def test_struct_layouts_match_c_compiler(tmp_path):
     """sizeof and field offsets as the C compiler lays out include/bsm.h."""
     structs = {"bsm_tensor4": bsm.Tensor4, "bsm_dflash": bsm.DFlashC,
                "bsm_block_mask": bsm.BlockMaskC, "bsm_geom": bsm.Geom,
-               "bsm_key_list": bsm.KeyListC,
+               "bsm_key_list": bsm.KeyListC, "bsm_varlen": bsm.VarlenC,
                "bsm_attn_args": bsm.AttnArgs, "bsm_attn_bwd_args": bsm.AttnBwdArgs}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "bsm.h"', "int main(void) {"]
     for cname, py in structs.items():
@@ -326,3 +326,55 @@ def test_attention_bwd_validation(L):
     wrong = _t4((2, 4, 1, 384), bsm.BSM_F32)           # dbias dtype != bias dtype
     a.dbias = ctypes.pointer(wrong)
     assert _bwd(L, geom, a)[0] == bsm.BSM_E_DTYPE
+
+
+def _varlen(cu_q, cu_k, H=8, KVH=2, D=128, dev_q=1 << 22, dev_k=1 << 23):
+    hq = (ctypes.c_int32 * len(cu_q))(*cu_q)
+    hk = (ctypes.c_int32 * len(cu_k))(*cu_k)
+    vl = bsm.VarlenC(len(cu_q) - 1, H, KVH, D, cu_q[-1], cu_k[-1], dev_q, dev_k,
+                     ctypes.addressof(hq), ctypes.addressof(hk))
+    return vl, (hq, hk)
+
+
+def _vl_shape(L, vl, pred):
+    out = (ctypes.c_int64 * 4)()
+    return L.block_mask_varlen_shape(ctypes.byref(vl), ctypes.byref(pred), out), tuple(out)
+
+
+def test_varlen_shapes_and_validation(L):
+    pred = bsm.varlen_dflash(16).c()
+    # three sequences: 2 blocks after 100 tokens, none, 10 blocks after 300
+    vl, keep = _varlen([0, 32, 32, 192], [0, 132, 132, 592])
+    assert _vl_shape(L, vl, pred) == (0, (3, 1, 2, 4))
+    bad, keep2 = _varlen([0, 30, 62], [0, 130, 262])          # 30 queries, blocks of 16
+    assert _vl_shape(L, bad, pred)[0] == bsm.BSM_E_SHAPE
+    dec, keep3 = _varlen([0, 32, 16], [0, 132, 300])          # decreasing
+    assert _vl_shape(L, dec, pred)[0] == bsm.BSM_E_ARG
+    odd, keep4 = _varlen([0, 32], [0, 133])                   # 101 context tokens, 2 blocks
+    assert _vl_shape(L, odd, pred)[0] == bsm.BSM_E_SHAPE
+    fixed = bsm.varlen_dflash(16, ctx_per_block=50).c()       # a fixed S needs no divisibility
+    assert _vl_shape(L, odd, fixed)[0] == 0
+    whole = bsm.DFlash(100, 2, 16).c()                        # ctx_len / num_blocks given
+    assert _vl_shape(L, vl, whole)[0] == bsm.BSM_E_ARG
+    total, keep5 = _varlen([0, 32, 32, 192], [0, 132, 132, 592])
+    total.total_q = 191
+    assert _vl_shape(L, total, pred)[0] == bsm.BSM_E_SHAPE
+    # attention: packed tensors are (1, total, heads, D); masks and biases are refused
+    a = _attn_args((1, 8, 2, 192, 592, 128))
+    m = _t4((1, 1, 192, 640))
+    a.mask = ctypes.pointer(m)
+    assert L.masked_attn_varlen_fwd(ctypes.byref(vl), ctypes.byref(a), None) == \
+        bsm.BSM_E_UNSUPPORTED
+    a = _attn_args((2, 8, 2, 96, 296, 128))                   # a padded (B=2) q
+    assert L.masked_attn_varlen_fwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_SHAPE
+
+
+def test_row_copy_validation(L):
+    assert L.gather_rows(1 << 20, 48, 1 << 21, 48, 40, 1 << 22, 5, None) == bsm.BSM_E_STRIDE
+    assert L.gather_rows(1 << 20, 32, 1 << 21, 64, 64, 1 << 22, 5, None) == bsm.BSM_E_STRIDE
+    assert L.scatter_rows(None, 64, 1 << 21, 64, 64, 1 << 22, 5, None) == bsm.BSM_E_ARG
+    assert L.gather_rows(None, 64, None, 64, 64, None, 0, None) == 0   # nothing to copy
+    assert L.unpad_index(1 << 20, 70000, 10, 10, 1 << 21, 1 << 22, None) == \
+        bsm.BSM_E_UNSUPPORTED
+    assert L.unpad_index(1 << 20, 4, 100, 50, 1 << 21, 1 << 22, None) == bsm.BSM_E_STRIDE
+
