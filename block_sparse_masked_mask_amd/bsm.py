@@ -28,7 +28,8 @@ BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
            "key_list_shape", "build_key_list", "dynamic_topk_mask", "dflash_dense_mask",
-           "masked_attn_fwd", "attn_bwd_workspace_size", "masked_attn_bwd",
+           "masked_attn_fwd", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
+           "masked_attn_bwd",
            "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
            "unpad_index", "gather_rows", "scatter_rows", "bsm_last_error")
 
@@ -64,7 +65,8 @@ class AttnArgs(ctypes.Structure):
                 ("o_stride", c_int64 * 4), ("lse", c_void_p), ("softmax_scale", c_float),
                 ("reserved", c_int32), ("pred", POINTER(DFlashC)), ("mask", POINTER(Tensor4)),
                 ("bias", POINTER(Tensor4)), ("bm", POINTER(BlockMaskC)),
-                ("keys", POINTER(KeyListC))]
+                ("keys", POINTER(KeyListC)), ("workspace", c_void_p),
+                ("workspace_bytes", c_int64)]
 
 
 class VarlenC(ctypes.Structure):
@@ -109,6 +111,7 @@ def lib():
                                         c_void_p, c_void_p]
         L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
         L.masked_attn_fwd.argtypes = [POINTER(Geom), POINTER(AttnArgs), c_void_p]
+        L.attn_fwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnArgs), POINTER(c_int64)]
         L.attn_bwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs),
                                               POINTER(c_int64)]
         L.masked_attn_bwd.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs), c_void_p]
@@ -363,8 +366,11 @@ def dflash_dense_mask(geom, pred, out=None, stream=None):
 
 def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
                     softmax_scale=None, return_lse=False, out=None, lse=None, stream=None,
-                    keys=None):
-    """Masked attention forward; returns O (and LSE if return_lse)."""
+                    keys=None, split=True, workspace=None):
+    """Masked attention forward; returns O (and LSE if return_lse).
+
+    split: let short query blocks split their keys over several workgroups
+    (a workspace of attn_fwd_workspace_size bytes is allocated unless given)."""
     geom = geometry_of(q, k)
     if out is None:
         out = torch.empty_like(q)
@@ -399,7 +405,18 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
         kc = keys.c()
         keep.append(kc)
         a.keys = ctypes.pointer(kc)
-    _check(lib().masked_attn_fwd(ctypes.byref(geom.c()), ctypes.byref(a), _stream(stream)))
+    gc = geom.c()
+    if split:
+        if workspace is None:
+            need = c_int64(0)
+            _check(lib().attn_fwd_workspace_size(ctypes.byref(gc), ctypes.byref(a),
+                                                 ctypes.byref(need)))
+            if need.value > 0:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().masked_attn_fwd(ctypes.byref(gc), ctypes.byref(a), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

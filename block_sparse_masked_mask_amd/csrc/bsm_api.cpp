@@ -574,10 +574,39 @@ int64_t bwd_workspace_bytes(const Geo& g, const bsm_tensor4* bias, const bsm_ten
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t stream) {
-  Geo g;
+// Short query blocks on the packed / split kernel: the G heads of a KV group
+// share a workgroup when their rows fit (G * Sq <= 64) and their block-mask
+// row is shared; a launch with fewer than 384 workgroups splits each tile list
+// into up to 32 parts of at least ~4 tiles, given a workspace for the partials.
+struct GroupPlan {
+  int pack, splits;
+  int64_t ws_o_bytes, ws_bytes;
+};
+
+GroupPlan group_plan(const AttnParams& p, int D) {
+  GroupPlan g{1, 1, 0, 0};
+  if (p.G > 1 && (int64_t)p.Sq * p.G <= 64 && !(p.has_bm && p.bm.h_mode == 1)) g.pack = p.G;
+  const int64_t base = (int64_t)p.B * (p.H / g.pack);
+  if (base > 0 && base < 384) {
+    int64_t S = (512 + base - 1) / base;
+    const int64_t cap = p.nK / 4 > 1 ? p.nK / 4 : 1;
+    S = S < cap ? S : cap;
+    g.splits = (int)(S < 32 ? S : 32);
+  }
+  if (g.splits > 1) {
+    const int64_t rows = (int64_t)g.splits * p.B * p.H * p.Sq;
+    g.ws_o_bytes = round_multiple(rows * D * 4, 256);
+    g.ws_bytes = g.ws_o_bytes + round_multiple(rows * 2 * 4, 256);
+  }
+  return g;
+}
+
+// Validation and parameters shared by masked_attn_fwd and its workspace query.
+// Sets `empty` when there is nothing to compute.
+int prepare_fwd(const bsm_geom* geom, const bsm_attn_args* a, Geo& g, AttnParams& p,
+                bool& empty) {
   int e = check_geom(geom, g);
   if (e) return e;
   if (!a) return fail(BSM_E_ARG, "args is NULL");
@@ -612,9 +641,11 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
     if ((e = key_list_dims(g, a->mask, ka, klist))) return e;
     if ((e = check_key_list(a->keys, klist))) return e;
   }
-  if (g.B == 0 || g.Sq == 0) return BSM_OK;
-
-  AttnParams p;
+  if (a->workspace_bytes < 0) return fail(BSM_E_ARG, "workspace_bytes < 0");
+  if (a->workspace_bytes > 0 && (!a->workspace || (uintptr_t)a->workspace % 256))
+    return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
+  empty = g.B == 0 || g.Sq == 0;
+  if (empty) return BSM_OK;
   fill_params(g, a->q, a->k, a->v, a->o, a->o_stride, a->lse, a->softmax_scale, a->pred,
               a->mask, a->bias, a->bm, in, p);
   if (a->keys) {
@@ -628,19 +659,60 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
     p.keys.h_mode = bm_head_mode(g, klist[1]);
     if (!attn_decode_applies(p, (int)g.D))
       return fail(BSM_E_UNSUPPORTED, "key-gather attention: K/V too large for 32-bit offsets");
-    return hip_status(launch_attn_decode(p, (int)g.D, stream), "masked_attn_fwd");
   }
+  return BSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_workspace_size(const bsm_geom* geom, const bsm_attn_args* a, int64_t* bytes) {
+  if (!bytes) return fail(BSM_E_ARG, "bytes is NULL");
+  Geo g;
+  AttnParams p{};
+  bool empty = false;
+  int e = prepare_fwd(geom, a, g, p, empty);
+  if (e) return e;
+  *bytes = 0;
+  if (empty || p.gather || a->q.dtype != BSM_BF16 || !attn_decode_applies(p, (int)g.D))
+    return BSM_OK;
+  *bytes = group_plan(p, (int)g.D).ws_bytes;
+  return BSM_OK;
+}
+
+int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t stream) {
+  Geo g;
+  AttnParams p{};
+  bool empty = false;
+  int e = prepare_fwd(geom, a, g, p, empty);
+  if (e) return e;
+  if (empty) return BSM_OK;
+  const int D = (int)g.D;
+  if (p.gather) return hip_status(launch_attn_decode(p, D, stream), "masked_attn_fwd");
   hipError_t he;
-  if (dt == BSM_BF16) {
-    if (attn_decode_applies(p, (int)g.D))
-      he = launch_attn_decode(p, (int)g.D, stream);
-    else if (attn_v2_applies(p, (int)g.D))
-      he = launch_attn_bf16_v2(p, (int)g.D, stream);
-    else
-      he = launch_attn_bf16(p, (int)g.D, stream);
+  if (a->q.dtype == BSM_BF16) {
+    if (attn_decode_applies(p, D)) {
+      const GroupPlan gp = group_plan(p, D);
+      p.pack = gp.pack;
+      p.splits = gp.splits > 1 && a->workspace_bytes >= gp.ws_bytes ? gp.splits : 1;
+      if (p.splits > 1) {
+        char* ws = static_cast<char*>(a->workspace);
+        p.ws_o = reinterpret_cast<float*>(ws);
+        p.ws_ml = reinterpret_cast<float*>(ws + gp.ws_o_bytes);
+      }
+      if (p.pack == 1 && p.splits == 1)
+        he = launch_attn_decode(p, D, stream);
+      else
+        he = launch_attn_group(p, D, stream);
+    } else if (attn_v2_applies(p, D)) {
+      he = launch_attn_bf16_v2(p, D, stream);
+    } else {
+      he = launch_attn_bf16(p, D, stream);
+    }
+  } else {
+    he = launch_attn_f32(p, D, stream);
   }
-  else
-    he = launch_attn_f32(p, (int)g.D, stream);
   return hip_status(he, "masked_attn_fwd");
 }
 

@@ -80,6 +80,12 @@ struct AttnParams {
   KeyListView keys;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  // short query blocks (k_attn_group): heads packed per workgroup (1 or G),
+  // key-tile splits per (b, head group), and the float partials of the splits
+  int32_t pack;
+  int32_t splits;
+  float* ws_o;   // (splits, B, H, Sq, D)
+  float* ws_ml;  // (splits, B, H, Sq, 2): running max (log2 units), row sum
 };
 
 // Backward: the forward's view plus the incoming gradient, the gradient
@@ -183,6 +189,9 @@ hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
 // bf16 kernel for at most 32 query rows per (b, h), split along the keys; with
 // p.gather it visits the kept keys of p.keys in tiles of 128 list positions
 bool attn_decode_applies(const AttnParams& p, int D);
+// packed / split short-query kernel (p.pack, p.splits set), plus the merge of
+// the splits' partial states when p.splits > 1
+hipError_t launch_attn_group(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s);
 
 }  // namespace bsm

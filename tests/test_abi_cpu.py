@@ -48,7 +48,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(bsm.DFlashC) == 56
     assert ctypes.sizeof(bsm.BlockMaskC) == 64
     assert ctypes.sizeof(bsm.KeyListC) == 3 * 8 + 4 * 8
-    assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 5 * 8
+    assert ctypes.sizeof(bsm.AttnArgs) == 3 * 80 + 8 + 32 + 8 + 8 + 7 * 8
     assert ctypes.sizeof(bsm.AttnBwdArgs) == 8 * 80 + 8 + 8 + 5 * 8 + 8 + 8
 
 
@@ -377,4 +377,26 @@ def test_row_copy_validation(L):
     assert L.unpad_index(1 << 20, 70000, 10, 10, 1 << 21, 1 << 22, None) == \
         bsm.BSM_E_UNSUPPORTED
     assert L.unpad_index(1 << 20, 4, 100, 50, 1 << 21, 1 << 22, None) == bsm.BSM_E_STRIDE
+
+
+def test_forward_workspace_sizes(L):
+    """Short query blocks with few (b, head) pairs ask for a split workspace."""
+    def need(geom, **kw):
+        a = _attn_args(geom, **kw)
+        n = ctypes.c_int64(-1)
+        st = L.attn_fwd_workspace_size(ctypes.byref(bsm.Geom(*geom)), ctypes.byref(a),
+                                       ctypes.byref(n))
+        return st, n.value
+    # inference: 8 requests x 8 KV groups of 4 heads x 16 rows packed, 257 key
+    # tiles -> 8 splits of (8, 32, 16) rows x (128 + 2) floats
+    geom = (8, 32, 8, 16, 32784, 128)
+    assert need(geom) == (0, 8 * 8 * 32 * 16 * 128 * 4 + 8 * 8 * 32 * 16 * 2 * 4)
+    # a long prefill (tiled kernels) and a wide decode batch need none
+    assert need((2, 32, 8, 4096, 8192, 128)) == (0, 0)
+    assert need((64, 32, 8, 1, 16384, 128)) == (0, 0)
+    assert need((8, 32, 8, 16, 32784, 128), dtype=bsm.BSM_F32) == (0, 0)
+    a = _attn_args(geom)
+    a.workspace, a.workspace_bytes = (1 << 24) + 8, 1 << 20
+    assert L.masked_attn_fwd(ctypes.byref(bsm.Geom(*geom)), ctypes.byref(a), None) == \
+        bsm.BSM_E_ARG  # misaligned workspace
 
