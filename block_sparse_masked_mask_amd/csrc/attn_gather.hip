@@ -1,31 +1,26 @@
-// Masked attention forward, bf16, for short query blocks: at most 32 query rows
-// per (b, h) -- the seqlen_q == 1 head-group swap gives G rows per KV head
-// (flash-sparse-attention PR #190, Design: swapped path), and short prefill
-// chunks.
+// Masked attention forward, bf16, key-gather mode for short query blocks: at
+// most 32 query rows per (b, h) -- under the seqlen_q == 1 head-group swap the
+// G heads of a KV group (flash-sparse-attention PR #190, Design: swapped path)
+// -- whose mask is given as a kept-key list (key_list.hip): the keys any row
+// keeps, with a word of row bits per key. With a dynamic top-k mask (PR #197,
+// Design) the list is a small part of the keys, and only those K / V rows
+// cross HBM.
 //
-// Such a launch streams K and V once and does little arithmetic on them, so
-// the work is split along the keys inside the workgroup instead of along the
-// queries: 4 waves share each 128-key K/V tile (LDS-DMA double buffering as in
-// attn_v2.hip), wave w takes keys 32w .. 32w+31 of every tile for all the rows,
-// keeps its own online-softmax state, and the four partial (max, sum, O) states
-// are merged through LDS at the end. The mask bytes and bias values a wave needs
-// for the next tile are loaded into registers together with that tile's DMA,
-// so the wait for one covers the other.
-//
-// Key-gather mode: with a kept-key list (key_list.hip) a "tile" is 128
-// consecutive list positions instead of 128 consecutive keys. Each DMA chunk
-// is fetched from the K / V row of its position's key (positions past the
-// list's end, or keys outside [0, Sk), fall outside the buffer resource and
+// The work is split along the list as in attn_group.hip: 4 waves share each
+// "tile" of 128 consecutive list positions (LDS-DMA double buffered), wave w
+// takes positions 32w .. 32w+31 for all the rows with its own online-softmax
+// state, and the four partial states are merged through LDS at the end. Each
+// DMA chunk is fetched from the K / V row of its position's key (positions past
+// the list's end, or keys outside [0, Sk), fall outside the buffer resource and
 // load as zeros), the mask bit of a (row, position) pair is bit `row` of the
 // position's row word, and the bias is gathered per key. The key indices a
 // tile's DMA needs are loaded two tiles ahead, so no load waits on another
-// inside the loop. Only the kept keys' K / V rows cross HBM.
+// inside the loop.
 #include <math.h>
 
 #include "attn_common.h"
 #include "attn_pipe.h"
 #include "bsm_internal.h"
-#include "dflash_rows.h"
 
 namespace bsm {
 namespace {
@@ -33,24 +28,7 @@ namespace {
 using namespace pipe;
 
 constexpr int kDecWaves = 4;
-constexpr int kDecRB = 512 / (64 * kDecWaves);  // Loader layout for 256 threads
-
-// Mask / bias words of one lane for one tile: keys kb .. kb+7 for sb = 0, 1
-// with kb = k0 + 32 w + 16 sb + 8 hh.
-struct AuxRegs {
-  uint4 bias[2];
-  uint2 mask[2];
-};
-
-__device__ inline void load_aux(const AttnParams& p, int kt, int w, int hh, const uint8_t* mrow,
-                                const uint16_t* brow, AuxRegs& a) {
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int kb = kt * kTile + 32 * w + 16 * sb + 8 * hh;
-    a.bias[sb] = brow ? *reinterpret_cast<const uint4*>(brow + kb) : make_uint4(0, 0, 0, 0);
-    a.mask[sb] = mrow ? *reinterpret_cast<const uint2*>(mrow + kb) : make_uint2(0, 0);
-  }
-}
+constexpr int kDecRB = 512 / (64 * kDecWaves);  // V2Ctx layout for 256 threads
 
 // LDS-DMA loader of gathered rows: load j of this thread moves 16-byte chunk
 // c_j of tile row r_j (the Loader layout); its source row is the key at list
@@ -164,15 +142,14 @@ __device__ inline void load_gather_aux(const uint32_t* lbits, const uint16_t* br
   }
 }
 
-template <int D, bool GATHER>
-__global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p) {
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_gather(AttnParams p) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
   __shared__ __align__(1024) Tiles<D> buf0;
   __shared__ __align__(1024) Tiles<D> buf1;
 
-  // Workgroup i runs on XCD i % 8; give each XCD a contiguous range of (b, h)
-  // so the G heads of a KV group read their K/V through the same L2.
+  // Workgroup i runs on XCD i % 8; each XCD takes a contiguous range of (b, h).
   int id;
   {
     const int nwg = gridDim.x;
@@ -199,25 +176,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
     for (int s = 0; s < NS; ++s)
       qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
   }
-  RowIv32 iv{0, 0, 0, 0};
-  if (p.mask_kind == 1) {
-    const RowIv v = dflash_row(p.rule, p.pred_row0 ? 0 : q);
-    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
-  }
-  const uint8_t* mrow =
-      (p.mask_kind == 2 && qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
   const uint16_t* brow = (p.has_bias && qvalid)
       ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb +
                         (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         (int64_t)kvh * p.v_sh;
-  Loader<D, kDecRB> ld;
   GatherLoader<D> gl;
-  if constexpr (GATHER)
-    gl.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
-  else
-    ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
+  gl.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
 
   f32x16 oacc[NDC];
 #pragma unroll
@@ -229,69 +195,41 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
   const int g4 = lane & 3;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  TileList tl;
-  int ntiles;
-  const int32_t* lidx = nullptr;
-  const uint32_t* lbits = nullptr;
-  int nlist = 0;
-  if constexpr (GATHER) {
-    const KeyListView& kl = p.keys;
-    const int64_t li = (kl.Bm == 1 ? 0 : (int64_t)b) * kl.Hm + head_index(kl.h_mode, h, p.G);
-    nlist = kl.num[li];
-    nlist = __builtin_amdgcn_readfirstlane(nlist < 0 ? 0 : (nlist > kl.K ? (int)kl.K : nlist));
-    lidx = kl.idx + li * kl.K;
-    lbits = kl.bits + li * kl.K;
-    ntiles = (nlist + kTile - 1) / kTile;
-  } else {
-    tl.init(p, b, h, 0);
-    ntiles = tl.count();
-  }
-  bool full_cur = false;
-  int kt_cur = 0;
-  AuxRegs aux_cur, aux_nxt;
+  const KeyListView& kl = p.keys;
+  const int64_t li = (kl.Bm == 1 ? 0 : (int64_t)b) * kl.Hm + head_index(kl.h_mode, h, p.G);
+  int nlist = kl.num[li];
+  nlist = __builtin_amdgcn_readfirstlane(nlist < 0 ? 0 : (nlist > kl.K ? (int)kl.K : nlist));
+  const int32_t* lidx = kl.idx + li * kl.K;
+  const uint32_t* lbits = kl.bits + li * kl.K;
+  const int ntiles = (nlist + kTile - 1) / kTile;
   GatherAux ga_cur, ga_nxt;
   int dkey[V2Ctx<D, kDecRB>::LOADS];  // DMA keys of the next tile to issue
   GatherKeys gk;                      // lane keys of the next tile's aux loads
   if (ntiles > 0) {
-    if constexpr (GATHER) {
-      gl.keys(lidx, 0, nlist, dkey);
-      gl.issue(buf0, dkey, w);
-      load_gather_keys(lidx, 0, w, hh, gk);
-      load_gather_aux(lbits, brow, p.Sk, 0, w, hh, gk, ga_cur);
-      if (ntiles > 1) {
-        gl.keys(lidx, 1, nlist, dkey);
-        load_gather_keys(lidx, 1, w, hh, gk);
-      }
-    } else {
-      kt_cur = tl.tile(0, full_cur);
-      ld.issue(buf0, kt_cur, w);
-      load_aux(p, kt_cur, w, hh, mrow, brow, aux_cur);
+    gl.keys(lidx, 0, nlist, dkey);
+    gl.issue(buf0, dkey, w);
+    load_gather_keys(lidx, 0, w, hh, gk);
+    load_gather_aux(lbits, brow, p.Sk, 0, w, hh, gk, ga_cur);
+    if (ntiles > 1) {
+      gl.keys(lidx, 1, nlist, dkey);
+      load_gather_keys(lidx, 1, w, hh, gk);
     }
   }
   for (int it = 0; it < ntiles; ++it) {
     const Tiles<D>& t = (it & 1) ? buf1 : buf0;
     Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
-    bool full_nxt = false;
-    int kt_nxt = 0;
-    if constexpr (!GATHER) kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) {
-      if constexpr (GATHER) {
-        gl.issue(nxt, dkey, w);
-        load_gather_aux(lbits, brow, p.Sk, it + 1, w, hh, gk, ga_nxt);
-        if (it + 2 < ntiles) {
-          gl.keys(lidx, it + 2, nlist, dkey);
-          load_gather_keys(lidx, it + 2, w, hh, gk);
-        }
-      } else {
-        ld.issue(nxt, kt_nxt, w);
-        load_aux(p, kt_nxt, w, hh, mrow, brow, aux_nxt);
+      gl.issue(nxt, dkey, w);
+      load_gather_aux(lbits, brow, p.Sk, it + 1, w, hh, gk, ga_nxt);
+      if (it + 2 < ntiles) {
+        gl.keys(lidx, it + 2, nlist, dkey);
+        load_gather_keys(lidx, it + 2, w, hh, gk);
       }
     }
 
-    // S^T for this wave's 32 keys (list positions in gather mode)
-    const int k0 = kt_cur * kTile;
+    // S^T for this wave's 32 list positions
     const int row = w * 32 + perm_row(n);
     f32x16 sc{};
 #pragma unroll
@@ -302,65 +240,29 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
     }
     // scale, bias, mask
     float mloc = -INFINITY;
-    if constexpr (GATHER) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int pb = it * kTile + 32 * w + 16 * sb + 8 * hh;
-        uint32_t mbits = 0;
+    for (int sb = 0; sb < 2; ++sb) {
+      const int pb = it * kTile + 32 * w + 16 * sb + 8 * hh;
+      uint32_t mbits = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint4 wq = ga_cur.bits[sb][e >> 2];
-          const uint32_t word =
-              (e & 3) == 0 ? wq.x : ((e & 3) == 1 ? wq.y : ((e & 3) == 2 ? wq.z : wq.w));
-          const int key = key_at(ga_cur.key, 8 * sb + e);
-          const bool keep = ((word >> q) & 1u) && (uint32_t)key < (uint32_t)p.Sk;
-          mbits |= (keep ? 1u : 0u) << e;
-        }
-        mbits &= range_bits(0, nlist, pb);
-        if (!qvalid) mbits = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int u = 8 * sb + e;
-          const float bv = bf16_to_f32(ga_cur.bias[u]) * kLog2e;
-          float sv = fmaf(sc[u], p.scale_log2, bv);
-          sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
-          sc[u] = sv;
-          mloc = fmaxf(mloc, sv);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const uint4 wq = ga_cur.bits[sb][e >> 2];
+        const uint32_t word =
+            (e & 3) == 0 ? wq.x : ((e & 3) == 1 ? wq.y : ((e & 3) == 2 ? wq.z : wq.w));
+        const int key = key_at(ga_cur.key, 8 * sb + e);
+        const bool keep = ((word >> q) & 1u) && (uint32_t)key < (uint32_t)p.Sk;
+        mbits |= (keep ? 1u : 0u) << e;
       }
-    } else {
-      const bool check_k = k0 + kTile > p.Sk;
-      const bool check_mask = !full_cur && p.mask_kind != 0;
+      mbits &= range_bits(0, nlist, pb);
+      if (!qvalid) mbits = 0;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int kb = k0 + 32 * w + 16 * sb + 8 * hh;
-        uint32_t mbits = 0xFFu;
-        if (check_mask) {
-          if (p.mask_kind == 2) {
-            const uint2 mb = aux_cur.mask[sb];
-            mbits = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
-              mbits |= (byte != 0u ? 1u : 0u) << e;
-            }
-          } else {
-            mbits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
-          }
-        }
-        if (!qvalid) mbits = 0;
-        if (check_k) mbits &= range_bits(0, p.Sk, kb);
-        const uint32_t wv[4] = {aux_cur.bias[sb].x, aux_cur.bias[sb].y, aux_cur.bias[sb].z,
-                                aux_cur.bias[sb].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int u = 8 * sb + e;
-          const float bv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
-          float sv = fmaf(sc[u], p.scale_log2, bv);
-          sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
-          sc[u] = sv;
-          mloc = fmaxf(mloc, sv);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int u = 8 * sb + e;
+        const float bv = bf16_to_f32(ga_cur.bias[u]) * kLog2e;
+        float sv = fmaf(sc[u], p.scale_log2, bv);
+        sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+        sc[u] = sv;
+        mloc = fmaxf(mloc, sv);
       }
     }
     mloc = max_pair(mloc);
@@ -407,13 +309,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
         oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[sb], oacc[dc], 0, 0, 0);
       }
     }
-    if constexpr (GATHER) {
-      ga_cur = ga_nxt;
-    } else {
-      aux_cur = aux_nxt;
-      kt_cur = kt_nxt;
-      full_cur = full_nxt;
-    }
+    ga_cur = ga_nxt;
   }
 
   // merge the four waves' partial states through LDS (tiles are free now)
@@ -476,29 +372,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_decode(AttnParams p)
 
 }  // namespace
 
-bool attn_decode_applies(const AttnParams& p, int D) {
-  if (D != 64 && D != 128) return false;
-  if (p.Sq > 32 || p.varlen) return false;
-  if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
-  if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
-  return true;
-}
-
-hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s) {
+hipError_t launch_attn_gather(const AttnParams& p, int D, hipStream_t s) {
   const int nwg = p.B * p.H;
   if (nwg == 0) return hipSuccess;
   const dim3 blk(64 * kDecWaves);
-  if (D == 128) {
-    if (p.gather)
-      hipLaunchKernelGGL((k_attn_decode<128, true>), dim3(nwg), blk, 0, s, p);
-    else
-      hipLaunchKernelGGL((k_attn_decode<128, false>), dim3(nwg), blk, 0, s, p);
-  } else {
-    if (p.gather)
-      hipLaunchKernelGGL((k_attn_decode<64, true>), dim3(nwg), blk, 0, s, p);
-    else
-      hipLaunchKernelGGL((k_attn_decode<64, false>), dim3(nwg), blk, 0, s, p);
-  }
+  if (D == 128)
+    hipLaunchKernelGGL(k_attn_gather<128>, dim3(nwg), blk, 0, s, p);
+  else
+    hipLaunchKernelGGL(k_attn_gather<64>, dim3(nwg), blk, 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,12 +1,16 @@
-// Masked attention forward, bf16, for short query blocks with few workgroups:
-// the query rows of several heads of one KV group packed into one workgroup,
-// and the visited key tiles split over several workgroups.
+// Masked attention forward, bf16, for short query blocks: at most 32 query rows
+// per (b, h) -- the seqlen_q == 1 head-group swap gives G rows per KV head
+// (flash-sparse-attention PR #190, Design: swapped path), prefill chunks of a
+// few tokens, a draft block against a long KV cache.
 //
-// A launch with at most 32 query rows per (b, h) reads K and V once per
-// workgroup and does little arithmetic on them. When the G heads of a KV group
-// each get a workgroup (prefill chunks of a few tokens, a draft block against a
-// long KV cache), the K/V tiles cross from L2 into LDS G times, and a batch of
-// a few sequences fills only B * H of the 256 CUs. Here:
+// Such a launch streams K and V and does little arithmetic on them, so the
+// work inside a workgroup is split along the keys instead of the queries: 4
+// waves share each 128-key K/V tile (LDS-DMA double buffering as in
+// attn_v2.hip), wave w takes keys 32w .. 32w+31 of every tile for all the rows,
+// keeps its own online-softmax state, and the four partial (max, sum, O) states
+// are merged through LDS at the end. The mask bytes and bias values a wave
+// needs for the next tile are loaded together with that tile's DMA, so the wait
+// for one covers the other. Across workgroups:
 //  * the heads of a KV group whose block-mask row is shared (a head-shared or
 //    per-KV-head block mask, or none) are packed: row r of the workgroup is
 //    query r % Sq of head h0 + r / Sq, up to 64 rows in two 32-row blocks, so
@@ -15,9 +19,7 @@
 //    workgroup; each part's unnormalised O, running max and row sum go to a
 //    float workspace and k_split_merge combines them (the online-softmax merge
 //    of partial results: weights 2^(m_s - m*)).
-// Inside a workgroup the work is split along the keys as in attn_decode.hip:
-// 4 waves share each LDS-DMA double-buffered 128-key tile, wave w takes keys
-// 32w .. 32w+31 for all rows, and the waves' partial states merge through LDS.
+// Without packing or splitting (pack = 1, S = 1) a workgroup is one (b, h).
 // The heads of the mask / bias / DFlash row follow each row's own head and
 // query (flash-sparse-attention PR #190, Design: broadcast rules; SpecForge
 // issue #452: head-shared block masks).
@@ -383,6 +385,15 @@ __global__ __launch_bounds__(256) void k_split_merge(AttnParams p) {
 }
 
 }  // namespace
+
+bool short_query_applies(const AttnParams& p, int D) {
+  if (D != 64 && D != 128) return false;
+  if (p.Sq > 32 || p.varlen) return false;
+  // 32-bit buffer offsets within one (b, kv head)
+  if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
+  if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
+  return true;
+}
 
 hipError_t launch_attn_group(const AttnParams& p, int D, hipStream_t s) {
   const int64_t nwg = (int64_t)p.B * (p.H / p.pack) * p.splits;

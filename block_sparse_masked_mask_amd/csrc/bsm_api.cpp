@@ -657,7 +657,7 @@ int prepare_fwd(const bsm_geom* geom, const bsm_attn_args* a, Geo& g, AttnParams
     p.keys.Hm = klist[1];
     p.keys.K = klist[3];
     p.keys.h_mode = bm_head_mode(g, klist[1]);
-    if (!attn_decode_applies(p, (int)g.D))
+    if (!short_query_applies(p, (int)g.D))
       return fail(BSM_E_UNSUPPORTED, "key-gather attention: K/V too large for 32-bit offsets");
   }
   return BSM_OK;
@@ -675,7 +675,7 @@ int attn_fwd_workspace_size(const bsm_geom* geom, const bsm_attn_args* a, int64_
   int e = prepare_fwd(geom, a, g, p, empty);
   if (e) return e;
   *bytes = 0;
-  if (empty || p.gather || a->q.dtype != BSM_BF16 || !attn_decode_applies(p, (int)g.D))
+  if (empty || p.gather || a->q.dtype != BSM_BF16 || !short_query_applies(p, (int)g.D))
     return BSM_OK;
   *bytes = group_plan(p, (int)g.D).ws_bytes;
   return BSM_OK;
@@ -689,10 +689,10 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
   if (e) return e;
   if (empty) return BSM_OK;
   const int D = (int)g.D;
-  if (p.gather) return hip_status(launch_attn_decode(p, D, stream), "masked_attn_fwd");
+  if (p.gather) return hip_status(launch_attn_gather(p, D, stream), "masked_attn_fwd");
   hipError_t he;
   if (a->q.dtype == BSM_BF16) {
-    if (attn_decode_applies(p, D)) {
+    if (short_query_applies(p, D)) {
       const GroupPlan gp = group_plan(p, D);
       p.pack = gp.pack;
       p.splits = gp.splits > 1 && a->workspace_bytes >= gp.ws_bytes ? gp.splits : 1;
@@ -701,10 +701,7 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
         p.ws_o = reinterpret_cast<float*>(ws);
         p.ws_ml = reinterpret_cast<float*>(ws + gp.ws_o_bytes);
       }
-      if (p.pack == 1 && p.splits == 1)
-        he = launch_attn_decode(p, D, stream);
-      else
-        he = launch_attn_group(p, D, stream);
+      he = launch_attn_group(p, D, stream);
     } else if (attn_v2_applies(p, D)) {
       he = launch_attn_bf16_v2(p, D, stream);
     } else {

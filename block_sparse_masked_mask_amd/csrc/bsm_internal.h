@@ -186,12 +186,11 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D);
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s);
 hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
-// bf16 kernel for at most 32 query rows per (b, h), split along the keys; with
-// p.gather it visits the kept keys of p.keys in tiles of 128 list positions
-bool attn_decode_applies(const AttnParams& p, int D);
-// packed / split short-query kernel (p.pack, p.splits set), plus the merge of
-// the splits' partial states when p.splits > 1
+// bf16 short query blocks (at most 32 query rows per (b, h)): the packed /
+// split kernel (p.pack, p.splits set; the merge of the splits' partial states
+// follows when p.splits > 1), and the key-gather kernel for a kept-key list
+bool short_query_applies(const AttnParams& p, int D);
 hipError_t launch_attn_group(const AttnParams& p, int D, hipStream_t s);
-hipError_t launch_attn_decode(const AttnParams& p, int D, hipStream_t s);
+hipError_t launch_attn_gather(const AttnParams& p, int D, hipStream_t s);
 
 }  // namespace bsm
