@@ -222,25 +222,7 @@ def measure_components():
     out["attn/long_dflash_bf16_ms"] = ms
     out["attn/long_dflash_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
     del q, k, v, o
-    # dynamic top-k attention: top-k, dense builder, attention
-    cfg = synth.CONFIGS["dynamic_topk_bf16"]
-    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
-    q, k, v = [t.cuda() for t in synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0)]
-    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
-    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
-    geom = bsm.geometry_of(q, k)
-    bm = bsm.build_block_mask(geom, mask=mask)
-    fl = counted_flops(bm, geom)
-    o = torch.empty_like(q)
-    out["topk/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
-        lambda: bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"], ))
-    out["block_mask_dense/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
-        lambda: bsm.build_block_mask(geom, mask=mask))
-    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
-                                              out=o), reps=5)
-    out["attn/dynamic_topk_bf16_ms"] = ms
-    out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
-    del q, k, v, o
+    out.update(measure_dynamic())
     out.update(measure_decode())
     out.update(measure_dflash_infer())
     out.update(measure_varlen())
@@ -311,6 +293,35 @@ def measure_dflash_infer():
     return out
 
 
+def measure_dynamic():
+    """The dynamic-mask workload (B=2, H=16, KVH=4, Sq=Sk=8000, bias (2,4,1,8064),
+    2D right padding, top-2048): top-k, dense builder, the fused top-k + block
+    mask, and the attention."""
+    out = {}
+    cfg = synth.CONFIGS["dynamic_topk_bf16"]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = [t.cuda() for t in synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0)]
+    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    fl = counted_flops(bm, geom)
+    o = torch.empty_like(q)
+    out["topk/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"], ))
+    out["block_mask_dense/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.build_block_mask(geom, mask=mask))
+    pm4 = pad2d.as_strided((B, 1, 1, Sk), (pad2d.stride(0), 0, 0, pad2d.stride(1)))
+    out["topk_fused_bm/dynamic_topk_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.dynamic_topk_fused(geom, bias, pm4, cfg["topk"]))
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o), reps=5)
+    out["attn/dynamic_topk_bf16_ms"] = ms
+    out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+    del q, k, v, o
+    return out
+
+
 def measure_decode():
     """Decode with the head-group swap (B=64, H=32, KVH=8, Sk=16384, per-head
     bias, top-1024): top-k, then either the dense block-mask builder and the
@@ -344,6 +355,12 @@ def measure_decode():
     out["key_list/decode_swap_bf16_us"] = kb
     out["key_list/decode_swap_bf16_listed_frac"] = listed / (B * KVH * Sk)
     out["key_list/decode_swap_bf16_GB/s"] = (mask.numel() + listed * 8) / (kb * 1e-6) / 1e9
+    # top-k fused with the key list (and the block mask), one pass over the bias
+    out["topk_fused_keys/decode_swap_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.dynamic_topk_fused(geom, bias, None, cfg["topk"], want_mask=False,
+                                       want_block_mask=False, want_keys=True))
+    out["topk_fused_all/decode_swap_bf16_us"] = 1e3 * _time_ms(
+        lambda: bsm.dynamic_topk_fused(geom, bias, None, cfg["topk"], want_keys=True))
     mg = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, keys=keys, out=o),
                   reps=5)
     g_bytes = row_bytes * listed + listed * 8 + bias.numel() * 2 + 2 * q.numel() * 2
@@ -401,7 +418,7 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the DFlash training-shape backward and print it")
-    ap.add_argument("--only", choices=["decode", "infer", "varlen", "components"],
+    ap.add_argument("--only", choices=["decode", "dynamic", "infer", "varlen", "components"],
                     help="only time one group of the other workloads' kernels and print it")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -416,7 +433,8 @@ def main():
         print(json.dumps(measure_backward()), flush=True)
         return
     if args.only:
-        fn = {"decode": measure_decode, "infer": measure_dflash_infer, "varlen": measure_varlen,
+        fn = {"decode": measure_decode, "dynamic": measure_dynamic,
+              "infer": measure_dflash_infer, "varlen": measure_varlen,
               "components": measure_components}[args.only]
         print(json.dumps(fn()), flush=True)
         return

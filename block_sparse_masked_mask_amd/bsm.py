@@ -27,7 +27,8 @@ BSM_OK, BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE, BSM_E_UNSUPPORTED, BS
 BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
-           "key_list_shape", "build_key_list", "dynamic_topk_mask", "dflash_dense_mask",
+           "key_list_shape", "build_key_list", "dynamic_topk_mask", "dynamic_topk_fused",
+           "dflash_dense_mask",
            "masked_attn_fwd", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
            "masked_attn_bwd",
            "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
@@ -109,6 +110,9 @@ def lib():
                                      c_void_p]
         L.dynamic_topk_mask.argtypes = [POINTER(Tensor4), POINTER(Tensor4), c_int64, c_int64,
                                         c_void_p, c_void_p]
+        L.dynamic_topk_fused.argtypes = [POINTER(Geom), POINTER(Tensor4), POINTER(Tensor4),
+                                         c_int64, c_void_p, POINTER(BlockMaskC),
+                                         POINTER(KeyListC), c_void_p]
         L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
         L.masked_attn_fwd.argtypes = [POINTER(Geom), POINTER(AttnArgs), c_void_p]
         L.attn_fwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnArgs), POINTER(c_int64)]
@@ -326,6 +330,66 @@ def dynamic_topk_mask(bias, premask, seqlen_k, k, out=None, stream=None):
                                    int(seqlen_k), int(k),
                                    out.data_ptr() if out.numel() else None, _stream(stream)))
     return out
+
+
+def dynamic_topk_fused(geom, bias, premask, k, want_mask=True, want_block_mask=True,
+                       want_keys=False, stream=None):
+    """Top-k over `bias` (seqlen_k = geom Sk) and, from the same pass, the block
+    mask and / or the kept-key list of its mask. Returns (mask, block_mask, keys)
+    with None for what was not asked."""
+    g = Geometry(*geom)
+    dev = bias.device
+    mask = torch.empty(bias.shape, dtype=torch.bool, device=dev) if want_mask else None
+    bm = keys = None
+    if want_block_mask:
+        Bm, Hm, nQm, nK = _mask_bm_shape(g, bias.shape)
+        bm = BlockMask(torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=dev),
+                       torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=dev),
+                       torch.empty((Bm, Hm, nQm), dtype=torch.int32, device=dev),
+                       torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=dev))
+    if want_keys:
+        Bm, Hm, R, K = _mask_kl_shape(g, bias.shape)
+        keys = KeyList(torch.empty((Bm, Hm), dtype=torch.int32, device=dev),
+                       torch.empty((Bm, Hm, K), dtype=torch.int32, device=dev),
+                       torch.empty((Bm, Hm, K), dtype=torch.int32, device=dev), R)
+    bc = tensor4(bias)
+    pc = tensor4(premask) if premask is not None else None
+    bmc = bm.c() if bm is not None else None
+    kc = keys.c() if keys is not None else None
+    _check(lib().dynamic_topk_fused(ctypes.byref(g.c()), ctypes.byref(bc),
+                                    ctypes.byref(pc) if pc else None, int(k),
+                                    mask.data_ptr() if mask is not None and mask.numel() else None,
+                                    ctypes.byref(bmc) if bmc else None,
+                                    ctypes.byref(kc) if kc else None, _stream(stream)))
+    return mask, bm, keys
+
+
+def _contig_mask4(shape):
+    """Tensor4 of a contiguous bool mask of this shape (sizes and strides only)."""
+    x = Tensor4()
+    x.data = 256
+    x.dtype = BSM_BOOL
+    x.reserved = 0
+    st = 1
+    for i in (3, 2, 1, 0):
+        x.size[i] = shape[i]
+        x.stride[i] = st
+        st *= shape[i]
+    return x
+
+
+def _mask_bm_shape(g, shape):
+    out = (c_int64 * 4)()
+    mc = _contig_mask4(shape)
+    _check(lib().block_mask_shape(ctypes.byref(g.c()), None, ctypes.byref(mc), out))
+    return tuple(int(x) for x in out)
+
+
+def _mask_kl_shape(g, shape):
+    out = (c_int64 * 4)()
+    mc = _contig_mask4(shape)
+    _check(lib().key_list_shape(ctypes.byref(g.c()), ctypes.byref(mc), out))
+    return tuple(int(x) for x in out)
 
 
 def create_mask(attention_bias, attention_mask, batch_size, query_len, key_len, window_size,

@@ -344,8 +344,14 @@ int build_block_mask(const bsm_geom* geom, const bsm_dflash* pred, const bsm_ten
                     "block_mask_dense");
 }
 
-int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64_t seqlen_k,
-                      int64_t k, uint8_t* out_mask, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and parameters of a top-k over `bias` (shared by the plain and the
+// fused entry points); p.out is left null.
+int fill_topk(const bsm_tensor4* bias, const bsm_tensor4* premask, int64_t seqlen_k, int64_t k,
+              TopkParams& p) {
   if (!bias) return fail(BSM_E_ARG, "bias is NULL");
   if (k < 0) return fail(BSM_E_ARG, "k must be >= 0 (got %lld)", (long long)k);
   if (seqlen_k < 0) return fail(BSM_E_ARG, "seqlen_k must be >= 0");
@@ -358,10 +364,10 @@ int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64
     return fail(BSM_E_SHAPE, "bias last dim %lld must be round_multiple(seqlen_k,128)=%lld",
                 (long long)bias->size[3], (long long)Kr);
   const int64_t n = numel(bias);
-  if (n > 0 && (!bias->data || !out_mask)) return fail(BSM_E_ARG, "bias or out_mask is NULL");
+  if (n > 0 && !bias->data) return fail(BSM_E_ARG, "bias data is NULL");
   if (bias->size[0] * bias->size[1] * bias->size[2] > INT32_MAX)
     return fail(BSM_E_UNSUPPORTED, "too many rows");
-  TopkParams p{};
+  p = TopkParams{};
   p.bias = bias->data;
   p.b_sb = bias->size[0] == 1 ? 0 : bias->stride[0];
   p.b_sh = bias->size[1] == 1 ? 0 : bias->stride[1];
@@ -372,7 +378,6 @@ int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64
   p.K = Kr;
   p.Sk = seqlen_k;
   p.k = k;
-  p.out = out_mask;
   p.is_bf16 = bias->dtype == BSM_BF16;
   p.pm = nullptr;
   if (premask) {
@@ -397,8 +402,85 @@ int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64
     p.p_sq = premask->size[2] == 1 ? 0 : premask->stride[2];
     p.pK = premask->size[3];
   }
+  return BSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dynamic_topk_mask(const bsm_tensor4* bias, const bsm_tensor4* premask, int64_t seqlen_k,
+                      int64_t k, uint8_t* out_mask, hipStream_t stream) {
+  TopkParams p;
+  int e = fill_topk(bias, premask, seqlen_k, k, p);
+  if (e) return e;
+  const int64_t n = numel(bias);
+  if (n > 0 && !out_mask) return fail(BSM_E_ARG, "out_mask is NULL");
+  p.out = out_mask;
   if (n == 0) return BSM_OK;
   return hip_status(launch_topk(p, stream), "dynamic_topk_mask");
+}
+
+int dynamic_topk_fused(const bsm_geom* geom, const bsm_tensor4* bias, const bsm_tensor4* premask,
+                       int64_t k, uint8_t* out_mask, const bsm_block_mask* out_bm,
+                       const bsm_key_list* out_keys, hipStream_t stream) {
+  Geo g;
+  int e = check_geom(geom, g);
+  if (e) return e;
+  if (!out_mask && !out_bm && !out_keys) return fail(BSM_E_ARG, "no output requested");
+  TopkFusedParams fp{};
+  if ((e = fill_topk(bias, premask, g.Sk, k, fp.t))) return e;
+  if (!topk_fused_applies(fp.t))
+    return fail(BSM_E_UNSUPPORTED, "fused top-k handles rows of up to 16384 bf16 / 8192 f32 keys");
+  // the mask this top-k writes: contiguous, the bias's sizes, seen in the
+  // attention's iteration space
+  bsm_tensor4 mt{};
+  mt.data = out_mask ? out_mask : reinterpret_cast<const void*>((uintptr_t)256);
+  mt.dtype = BSM_BOOL;
+  for (int i = 0; i < 4; ++i) mt.size[i] = bias->size[i];
+  mt.stride[3] = 1;
+  mt.stride[2] = mt.size[3];
+  mt.stride[1] = mt.size[2] * mt.stride[2];
+  mt.stride[0] = mt.size[1] * mt.stride[1];
+  Aux a;
+  if ((e = check_aux(&mt, "top-k mask", g, BSM_BOOL, a))) return e;
+  if (a.Qm > 32)
+    return fail(BSM_E_UNSUPPORTED, "fused top-k needs at most 32 distinct mask rows per (b, h)");
+  if (out_mask && (uintptr_t)out_mask % 16) return fail(BSM_E_STRIDE, "out_mask not 16-byte aligned");
+  fp.t.out = out_mask;
+  fp.m_sb = a.view.sb;
+  fp.m_sh = a.view.sh;
+  fp.m_sq = a.view.q_bcast ? 0 : a.view.sq;
+  fp.Bm = a.Bm;
+  fp.Hm = a.Hm;
+  fp.Qm = (int32_t)a.Qm;
+  fp.R = (int32_t)iter_rows(g);
+  if (out_bm) {
+    int64_t shp[4];
+    expected_bm(g, nullptr, &a, shp);
+    if (out_bm->Bm != shp[0] || out_bm->Hm != shp[1] || out_bm->nQm != shp[2] ||
+        out_bm->nK != shp[3])
+      return fail(BSM_E_SHAPE, "block mask dims do not match the top-k mask");
+    if (shp[0] * shp[1] > 0 && (!out_bm->kv_num_blocks || !out_bm->full_kv_num_blocks ||
+                                (shp[3] > 0 && (!out_bm->kv_indices || !out_bm->full_kv_indices))))
+      return fail(BSM_E_ARG, "block mask buffer is NULL");
+    fp.kv_num = out_bm->kv_num_blocks;
+    fp.kv_idx = out_bm->kv_indices;
+    fp.full_num = out_bm->full_kv_num_blocks;
+    fp.full_idx = out_bm->full_kv_indices;
+    fp.nK = shp[3];
+  }
+  if (out_keys) {
+    int64_t shp[4];
+    Aux ka;
+    if ((e = key_list_dims(g, &mt, ka, shp))) return e;
+    if ((e = check_key_list(out_keys, shp))) return e;
+    fp.l_num = out_keys->num_keys;
+    fp.l_idx = out_keys->key_indices;
+    fp.l_bits = out_keys->row_bits;
+  }
+  if (fp.Qm == 0) return BSM_OK;  // no rows
+  return hip_status(launch_topk_fused(fp, stream), "dynamic_topk_fused");
 }
 
 int key_list_shape(const bsm_geom* geom, const bsm_tensor4* mask, int64_t out_shape[4]) {

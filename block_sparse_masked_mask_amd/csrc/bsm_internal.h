@@ -173,6 +173,27 @@ hipError_t launch_block_mask_dense(const DenseMaskView& m, int32_t* kv_num,
                                    int32_t* kv_idx, int32_t* full_num,
                                    int32_t* full_idx, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+
+// Top-k fused with the block mask and / or the kept-key list of its mask
+// (t.out nullable). The mask is contiguous with the bias's sizes; (m_sb, m_sh,
+// m_sq) are its element strides in the attention's iteration space (m_sq = 0
+// when Qm == 1), Bm x Hm lists of Qm <= 32 distinct rows, R iteration rows.
+struct TopkFusedParams {
+  TopkParams t;
+  int64_t m_sb, m_sh, m_sq;
+  int64_t Bm, Hm;
+  int32_t Qm, R;
+  int32_t* kv_num;   // block mask (Bm, Hm, 1, nK), or null
+  int32_t* kv_idx;
+  int32_t* full_num;
+  int32_t* full_idx;
+  int64_t nK;
+  int32_t* l_num;    // key list (Bm, Hm, K), or null
+  int32_t* l_idx;
+  uint32_t* l_bits;
+};
+bool topk_fused_applies(const TopkParams& p);  // rows short enough for registers
+hipError_t launch_topk_fused(const TopkFusedParams& fp, hipStream_t s);
 hipError_t launch_key_list(const KeyListParams& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);

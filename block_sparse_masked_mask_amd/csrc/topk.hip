@@ -225,33 +225,38 @@ __global__ __launch_bounds__(kThreads) void k_topk(TopkParams p) {
 
 constexpr size_t kCacheMax = 64 * 1024;
 
-// Register-resident variant for rows of up to NSEG * 256 * (16 / sizeof(KeyT))
+// Register-resident selection for rows of up to NSEG * 256 * (16 / sizeof(KeyT))
 // keys: each thread keeps its keys in registers throughout; the threshold
-// comes from a wide-digit radix select (below). Segment s
-// of a row is the 4 KiB (bf16) / 4 KiB (f32) block [s * SEG, (s + 1) * SEG);
-// thread t owns the 16 contiguous bytes at t * EPL of every segment, so each
-// load and each store of a segment is one coalesced wave-wide access. The
-// index-order prefix count of keys equal to the threshold is one workgroup
-// scan of NSEG counters per thread (segment-major, then thread order).
+// comes from a wide-digit radix select (below). Segment s of a row is the 4 KiB
+// block [s * SEG, (s + 1) * SEG); thread t owns the 16 contiguous bytes at
+// t * EPL of every segment, so each load and each store of a segment is one
+// coalesced wave-wide access. The index-order prefix count of keys equal to the
+// threshold is one workgroup scan of NSEG counters per thread (segment-major,
+// then thread order). t is the thread's index in its group of 256 threads
+// (sm belongs to the group); on return bit i of sel[s] says whether key
+// s * SEG + t * EPL + i is kept (selected and valid). Every thread of the
+// workgroup must call it: its barriers are workgroup-wide, so groups that
+// share a workgroup run it together, each on its own row and LDS.
+template <int NSEG>
+struct SelectSmem {
+  uint32_t hist[4096];
+  uint32_t scan[kWaves];
+  uint32_t sel[2];
+  int wsum[NSEG][kWaves];
+};
+
 template <typename KeyT, int NSEG, bool HAS_PM>
-__global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
+__device__ inline void select_row(const TopkParams& p, const KeyT* brow, const uint8_t* prow,
+                                  int t, SelectSmem<NSEG>& sm, uint32_t (&sel)[NSEG]) {
   using Tr = KeyTraits<KeyT>;
   constexpr int EPL = 16 / sizeof(KeyT);  // keys per 16-byte load
   constexpr int SEG = kThreads * EPL;
-  __shared__ uint32_t s_hist[4096];
-  __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_sel[2];
-  __shared__ int s_wsum[NSEG][kWaves];
+  uint32_t* s_hist = sm.hist;
+  uint32_t* s_scan = sm.scan;
+  uint32_t* s_sel = sm.sel;
+  auto& s_wsum = sm.wsum;
 
-  const int64_t row = blockIdx.x;
-  const int64_t qb = row % p.Qb;
-  const int64_t hb = (row / p.Qb) % p.Hb;
-  const int64_t bb = row / (p.Qb * p.Hb);
-  const KeyT* brow = reinterpret_cast<const KeyT*>(p.bias) + bb * p.b_sb + hb * p.b_sh + qb * p.b_sq;
-  const uint8_t* prow = p.pm ? p.pm + bb * p.p_sb + hb * p.p_sh + qb * p.p_sq : nullptr;
-  uint8_t* orow = p.out + row * p.K;
   const int K = (int)p.K;
-  const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
   const KeyT sent = Tr::sentinel();
@@ -392,18 +397,33 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
     const int k0 = s * SEG + t * EPL;
-    if (k0 >= K) continue;
     uint32_t bits = 0;  // one bit per key
-    int r = excl[s];
+    if (k0 < K) {
+      int r = excl[s];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const uint32_t key = (uint32_t)kk[s][i];
-      const bool eq = key == T;
-      bool sel = key > T || (eq && r < need);
-      r += eq ? 1 : 0;
-      sel = keff >= K ? true : (keff == 0 ? false : sel);
-      bits |= (uint32_t)(sel && valid(k0 + i)) << i;
+      for (int i = 0; i < EPL; ++i) {
+        const uint32_t key = (uint32_t)kk[s][i];
+        const bool eq = key == T;
+        bool pick = key > T || (eq && r < need);
+        r += eq ? 1 : 0;
+        pick = keff >= K ? true : (keff == 0 ? false : pick);
+        bits |= (uint32_t)(pick && valid(k0 + i)) << i;
+      }
     }
+    sel[s] = bits;
+  }
+}
+
+// Writes the keep bytes of one row from select_row's bits.
+template <typename KeyT, int NSEG>
+__device__ inline void write_row(uint8_t* orow, int K, int t, const uint32_t (&sel)[NSEG]) {
+  constexpr int EPL = 16 / sizeof(KeyT);
+  constexpr int SEG = kThreads * EPL;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    const int k0 = s * SEG + t * EPL;
+    if (k0 >= K) continue;
+    const uint32_t bits = sel[s];
     if (EPL == 8) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -418,6 +438,149 @@ __global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
       for (int i = 0; i < 4; ++i) v |= ((bits >> i) & 1u) << (8 * i);
       *reinterpret_cast<uint32_t*>(orow + k0) = v;
     }
+  }
+}
+
+template <typename KeyT, int NSEG, bool HAS_PM>
+__global__ __launch_bounds__(kThreads) void k_topk_reg(TopkParams p) {
+  const int64_t row = blockIdx.x;
+  const int64_t qb = row % p.Qb;
+  const int64_t hb = (row / p.Qb) % p.Hb;
+  const int64_t bb = row / (p.Qb * p.Hb);
+  const KeyT* brow = reinterpret_cast<const KeyT*>(p.bias) + bb * p.b_sb + hb * p.b_sh + qb * p.b_sq;
+  const uint8_t* prow = p.pm ? p.pm + bb * p.p_sb + hb * p.p_sh + qb * p.p_sq : nullptr;
+  __shared__ SelectSmem<NSEG> sm;
+  uint32_t sel[NSEG];
+  select_row<KeyT, NSEG, HAS_PM>(p, brow, prow, (int)threadIdx.x, sm, sel);
+  write_row<KeyT, NSEG>(p.out + row * p.K, (int)p.K, (int)threadIdx.x, sel);
+}
+
+// Top-k fused with what is built from its mask. One workgroup per (bm, hm) of
+// the mask in the attention's iteration space selects its Qm (<= 32) distinct
+// mask rows in turn (small workgroups: the selection is latency-bound and
+// gains from many resident workgroups), writes them if asked, and keeps per
+// owned key a word of the rows that keep it (thread t owns the same keys in
+// every row). Then, without reading the mask back:
+//  * block mask: the kept pairs of each 128-key tile (popcounts of its words)
+//    classify it empty / partial / full over the Qm rows, and the two lists
+//    are compacted in ascending order;
+//  * key list: the keys with a non-zero word, ascending, with the word (all R
+//    rows when the mask broadcasts over queries), by a prefix count per
+//    segment.
+template <typename KeyT, int NSEG, bool HAS_PM>
+__global__ __launch_bounds__(kThreads) void k_topk_fused(TopkFusedParams fp) {
+  constexpr int EPL = 16 / sizeof(KeyT);
+  constexpr int SEG = kThreads * EPL;
+  constexpr int KMAX = NSEG * SEG;
+  __shared__ SelectSmem<NSEG> sm;
+  __shared__ int s_codes[KMAX / kTile];
+  __shared__ int s_wave[2][kWaves];
+  const TopkParams& p = fp.t;
+  const int64_t lb = blockIdx.x / fp.Hm;
+  const int64_t lh = blockIdx.x % fp.Hm;
+  const int K = (int)p.K;
+  const int t = threadIdx.x;
+  // per owned key (thread t owns the same keys in every row): bit r = row r keeps it
+  uint32_t rw[NSEG][EPL];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) rw[s][i] = 0;
+  for (int r = 0; r < fp.Qm; ++r) {
+    // mask row of (lb, lh, r) in the contiguous (Bb, Hb, Qb, K) mask, and the
+    // bias / pre-mask rows it comes from
+    const int64_t mrow = (lb * fp.m_sb + lh * fp.m_sh + (int64_t)r * fp.m_sq) / p.K;
+    const int64_t qb = mrow % p.Qb;
+    const int64_t hb = (mrow / p.Qb) % p.Hb;
+    const int64_t bb = mrow / (p.Qb * p.Hb);
+    const KeyT* brow =
+        reinterpret_cast<const KeyT*>(p.bias) + bb * p.b_sb + hb * p.b_sh + qb * p.b_sq;
+    const uint8_t* prow = p.pm ? p.pm + bb * p.p_sb + hb * p.p_sh + qb * p.p_sq : nullptr;
+    uint32_t sel[NSEG];
+    select_row<KeyT, NSEG, HAS_PM>(p, brow, prow, t, sm, sel);
+    if (p.out) write_row<KeyT, NSEG>(p.out + mrow * p.K, K, t, sel);
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) rw[s][i] |= ((sel[s] >> i) & 1u) << r;
+  }
+
+  const int64_t li = blockIdx.x;  // list / block-mask row (lb, lh), query tile 0
+  if (fp.kv_num) {
+    const int nK = (int)fp.nK;
+    constexpr int TPT = kTile / EPL;  // threads owning one 128-key tile
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) c += __popc(rw[s][i]);
+#pragma unroll
+      for (int o = TPT / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+      const int kt = (s * SEG + t * EPL) / kTile;
+      if (t % TPT == 0 && kt < nK) s_codes[kt] = c == 0 ? 0 : (c == fp.Qm * kTile ? 2 : 1);
+    }
+    __syncthreads();
+    int np = 0, nf = 0;
+    int32_t* prow_o = fp.kv_idx + li * nK;
+    int32_t* frow_o = fp.full_idx + li * nK;
+    for (int base = 0; base < nK; base += kThreads) {
+      const int kk = base + t;
+      const int cc = kk < nK ? s_codes[kk] : 0;
+      int tp, tf;
+      const int op = block_excl_sum<kWaves>(cc == 1, s_wave[0], tp);
+      const int of = block_excl_sum<kWaves>(cc == 2, s_wave[1], tf);
+      if (cc == 1) prow_o[np + op] = kk;
+      if (cc == 2) frow_o[nf + of] = kk;
+      np += tp;
+      nf += tf;
+    }
+    for (int kk = np + t; kk < nK; kk += kThreads) prow_o[kk] = -1;
+    for (int kk = nf + t; kk < nK; kk += kThreads) frow_o[kk] = -1;
+    if (t == 0) {
+      fp.kv_num[li] = np;
+      fp.full_num[li] = nf;
+    }
+  }
+  if (fp.l_num) {
+    // segment-major, then thread order = ascending key order
+    const uint32_t all_rows = fp.R >= 32 ? 0xFFFFFFFFu : ((1u << fp.R) - 1u);
+    int taken = 0;
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      const int k0 = s * SEG + t * EPL;
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) cnt += rw[s][i] != 0u;
+      int tot;
+      int pos = taken + block_excl_sum<kWaves>(cnt, s_wave[0], tot);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const uint32_t wd = fp.Qm == 1 ? all_rows : rw[s][i];
+        if (rw[s][i]) {
+          fp.l_idx[li * p.K + pos] = k0 + i;
+          fp.l_bits[li * p.K + pos] = wd;
+          ++pos;
+        }
+      }
+      taken += tot;
+    }
+    if (t == 0) fp.l_num[li] = taken;
+  }
+}
+
+template <typename KeyT, bool HAS_PM>
+bool launch_fused2(const TopkFusedParams& fp, hipStream_t s) {
+  constexpr int SEG = kThreads * (16 / sizeof(KeyT));
+  const int nseg = (int)((fp.t.K + SEG - 1) / SEG);
+  const dim3 grid((unsigned)(fp.Bm * fp.Hm)), block(kThreads);
+  switch (nseg) {
+    case 1: hipLaunchKernelGGL((k_topk_fused<KeyT, 1, HAS_PM>), grid, block, 0, s, fp); return true;
+    case 2: hipLaunchKernelGGL((k_topk_fused<KeyT, 2, HAS_PM>), grid, block, 0, s, fp); return true;
+    case 3:
+    case 4: hipLaunchKernelGGL((k_topk_fused<KeyT, 4, HAS_PM>), grid, block, 0, s, fp); return true;
+    case 5: case 6: case 7:
+    case 8: hipLaunchKernelGGL((k_topk_fused<KeyT, 8, HAS_PM>), grid, block, 0, s, fp); return true;
+    default: return false;
   }
 }
 
@@ -443,6 +606,21 @@ bool launch_reg(const TopkParams& p, unsigned rows, hipStream_t s) {
 }
 
 }  // namespace
+
+bool topk_fused_applies(const TopkParams& p) {
+  const int64_t maxk = p.is_bf16 ? 8 * kThreads * 8 : 8 * kThreads * 4;
+  return p.K <= maxk;
+}
+
+hipError_t launch_topk_fused(const TopkFusedParams& fp, hipStream_t s) {
+  if (fp.Bm * fp.Hm == 0 || fp.t.K == 0) return hipSuccess;
+  bool ok;
+  if (fp.t.is_bf16)
+    ok = fp.t.pm ? launch_fused2<uint16_t, true>(fp, s) : launch_fused2<uint16_t, false>(fp, s);
+  else
+    ok = fp.t.pm ? launch_fused2<uint32_t, true>(fp, s) : launch_fused2<uint32_t, false>(fp, s);
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   const int64_t rows = p.Bb * p.Hb * p.Qb;

@@ -212,6 +212,24 @@ int key_list_shape(const bsm_geom* geom, const bsm_tensor4* mask, int64_t out_sh
 int build_key_list(const bsm_geom* geom, const bsm_tensor4* mask, const bsm_key_list* out,
                    hipStream_t stream);
 
+/* Dynamic top-k fused with what the attention needs from its mask: the same
+ * selection as dynamic_topk_mask (seqlen_k = geom->Sk) over `bias`, whose mask
+ * -- contiguous, the bias's sizes -- must be a valid mask for geom, and from it,
+ * without a second pass over the mask:
+ *   out_mask: the mask itself (nullable: not written);
+ *   out_bm:   its block mask, as build_block_mask would build it (nullable);
+ *   out_keys: its kept-key list, as build_key_list would build it (nullable).
+ * At least one output; the mask must have at most 32 distinct rows per (b, h)
+ * in the attention's iteration space (a query-broadcast mask, or the
+ * seqlen_q == 1 head-group swap), and rows of at most 16384 bf16 / 8192 f32
+ * keys (else BSM_E_UNSUPPORTED). The per-tile kept counts of the block mask
+ * are taken while the selection is still in registers, which saves the
+ * builder's read of the mask ([FSA-197] Design: the top-k mask; [SF-452]
+ * traceback: the block-mask reduction). */
+int dynamic_topk_fused(const bsm_geom* geom, const bsm_tensor4* bias, const bsm_tensor4* premask,
+                       int64_t k, uint8_t* out_mask, const bsm_block_mask* out_bm,
+                       const bsm_key_list* out_keys, hipStream_t stream);
+
 /* Dense DFlash mask, materialised: out_mask is a device, contiguous bool array
  * (Sq, K_round) (the [B,1,Q_LEN,KV_LEN] mask of [SF-474] Suggestion 2 with the
  * batch dim dropped, keys rounded to 128, tail False). For consumers that need

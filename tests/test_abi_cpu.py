@@ -400,3 +400,34 @@ def test_forward_workspace_sizes(L):
     assert L.masked_attn_fwd(ctypes.byref(bsm.Geom(*geom)), ctypes.byref(a), None) == \
         bsm.BSM_E_ARG  # misaligned workspace
 
+
+def test_topk_fused_validation(L):
+    geom = bsm.Geom(2, 16, 4, 8000, 8000, 128)
+    bias = _t4((2, 4, 1, 8064), bsm.BSM_BF16)
+    bm = bsm.BlockMaskC(1 << 22, 1 << 22, 1 << 22, 1 << 22, 2, 4, 1, 63)
+    # nothing to produce
+    assert L.dynamic_topk_fused(ctypes.byref(geom), ctypes.byref(bias), None, 10, None, None,
+                                None, None) == bsm.BSM_E_ARG
+    # block mask of the wrong shape
+    bad = bsm.BlockMaskC(1 << 22, 1 << 22, 1 << 22, 1 << 22, 2, 1, 1, 63)
+    assert L.dynamic_topk_fused(ctypes.byref(geom), ctypes.byref(bias), None, 10, None,
+                                ctypes.byref(bad), None, None) == bsm.BSM_E_SHAPE
+    # a key list needs at most 32 rows per (b, h): 8000 query rows here
+    kl = bsm.KeyListC(1 << 22, 1 << 23, 1 << 24, 2, 4, 8000, 8064)
+    assert L.dynamic_topk_fused(ctypes.byref(geom), ctypes.byref(bias), None, 10, None, None,
+                                ctypes.byref(kl), None) == bsm.BSM_E_UNSUPPORTED
+    # per-query bias rows: 8000 distinct mask rows per (b, h)
+    per_q = _t4((2, 4, 8000, 8064), bsm.BSM_BF16)
+    assert L.dynamic_topk_fused(ctypes.byref(geom), ctypes.byref(per_q), None, 10, 1 << 21,
+                                None, None, None) == bsm.BSM_E_UNSUPPORTED
+    # rows longer than the register-resident selection
+    g2 = bsm.Geom(1, 8, 8, 1, 20000, 128)
+    long_bias = _t4((1, 8, 1, 20096), bsm.BSM_BF16)
+    assert L.dynamic_topk_fused(ctypes.byref(g2), ctypes.byref(long_bias), None, 10, 1 << 21,
+                                None, None, None) == bsm.BSM_E_UNSUPPORTED
+    # a bias whose mask does not fit the geometry (head dim 3)
+    odd = _t4((2, 3, 1, 8064), bsm.BSM_BF16)
+    assert L.dynamic_topk_fused(ctypes.byref(geom), ctypes.byref(odd), None, 10, 1 << 21,
+                                None, None, None) == bsm.BSM_E_SHAPE
+    assert bm.Bm == 2
+
