@@ -50,8 +50,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "60e64eeee1ac99d4",
-                "fetch_kib": 86514.2, "write_kib": 65536.0,
+                "sha256_16": "6157ea219d28fe6b",
+                "fetch_kib": 86514.4, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -140,6 +140,28 @@ def measure_mask_build(reps=5):
     return {"workload": "long_dflash_dense_mask", "shape": [1, 1, d.Sq, 65536],
             "bytes": int(nbytes), "ms": ms, "GB/s": nbytes / ms / 1e6,
             "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def device_info(mib=1024, reps=5):
+    """Name, CU count and peak clock of cuda:0, and the GB/s of a plain device
+    copy of mib MiB (read + write bytes over the copy time): the measured
+    counterpart of the 8 TB/s HBM peak used as the denominator."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    clock_khz = ctypes.c_int(0)
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        # hipDeviceAttributeClockRate: 5 in hip_runtime_api.h's enum (kHz)
+        hip.hipDeviceGetAttribute(ctypes.byref(clock_khz), 5, 0)
+    except OSError:
+        pass
+    n = mib << 20
+    src = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src), reps=reps)
+    del src, dst
+    return {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "clock_mhz": clock_khz.value / 1000.0, "copy_GB/s": 2 * n / (ms * 1e-3) / 1e9}
 
 
 def copy_probe(mib=1024, reps=3):
@@ -482,6 +504,7 @@ def main():
                      "avg_launch_ms": float(np.mean(attn_ms)),
                      "flops_per_launch": float(np.mean(attn_flops))},
         "per_layer": per_layer,
+        "device": device_info(),
     }
     if not args.no_mask_build:
         line["mask_build"] = measure_mask_build()
