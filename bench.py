@@ -340,6 +340,11 @@ def measure_dynamic():
                                               out=o), reps=5)
     out["attn/dynamic_topk_bf16_ms"] = ms
     out["attn/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+    # the same call without a workspace: mask and bias read per key tile
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o, split=False), reps=5)
+    out["attn_unstaged/dynamic_topk_bf16_ms"] = ms
+    out["attn_unstaged/dynamic_topk_bf16_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
     del q, k, v, o
     return out
 

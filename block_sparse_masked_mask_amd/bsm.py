@@ -433,8 +433,10 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
                     keys=None, split=True, workspace=None):
     """Masked attention forward; returns O (and LSE if return_lse).
 
-    split: let short query blocks split their keys over several workgroups
-    (a workspace of attn_fwd_workspace_size bytes is allocated unless given)."""
+    split: allocate (unless given) the workspace attn_fwd_workspace_size asks
+    for, which lets short query blocks split their keys over several
+    workgroups and folds a query-broadcast mask / bias into staged rows;
+    split=False runs without either."""
     geom = geometry_of(q, k)
     if out is None:
         out = torch.empty_like(q)

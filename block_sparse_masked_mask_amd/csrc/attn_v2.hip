@@ -84,7 +84,7 @@ struct LaneOffs {
 template <int D, int RB>
 __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
                                     bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
-                                    int lane, int Sk) {
+                                    int lane, int Sk, const float* cbrow) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
   const int hh = lane >> 5;
@@ -136,9 +136,31 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       RowBlock<D>& R = rbk[r];
-      const bool plain = !check_k && !check_mask && R.brow == nullptr && R.qvalid;
+      const bool plain =
+          !p.staged && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
       float mloc = -INFINITY;
-      if (plain) {
+      if (p.staged) {
+        // the tile's slice of the folded mask / bias row: -inf drops a key
+        // (masked or past Sk); rows past Sq compute values nobody stores
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int kc = 2 * half + c;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const float4 c0 = *reinterpret_cast<const float4*>(cbrow + kc * 32 + 16 * sb + 8 * hh);
+            const float4 c1 =
+                *reinterpret_cast<const float4*>(cbrow + kc * 32 + 16 * sb + 8 * hh + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int u = 8 * sb + e;
+              const float sv = fmaf(sacc[r][c][u], p.scale_log2, cv[e]);
+              sacc[r][c][u] = sv;
+              mloc = fmaxf(mloc, sv);
+            }
+          }
+        }
+      } else if (plain) {
         // raw scores: the scale is folded into the exponent below
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -251,6 +273,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   constexpr int WPH = C::NW / 2;  // waves per head
   __shared__ __align__(1024) Tiles<D> buf0;
   __shared__ __align__(1024) Tiles<D> buf1;
+  __shared__ __align__(16) float s_cb[2][2][kTile];  // staged rows: buffer, head of the pair
 
   // Work items: (head-pair group, query tile). Workgroup L runs on XCD L % 8.
   // When the groups split evenly over the XCDs, XCD x takes groups
@@ -311,8 +334,9 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
       const RowIv v = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
       R.iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
     }
-    R.mrow = (p.mask_kind == 2 && R.qvalid) ? aux_row(p.mask, 1, b, h, p.G, q) : nullptr;
-    R.brow = (p.has_bias && R.qvalid)
+    R.mrow = (p.mask_kind == 2 && R.qvalid && !p.staged) ? aux_row(p.mask, 1, b, h, p.G, q)
+                                                          : nullptr;
+    R.brow = (p.has_bias && R.qvalid && !p.staged)
         ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
 #pragma unroll
     for (int i = 0; i < NDC; ++i) R.oacc[i] = f32x16{};
@@ -328,12 +352,39 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   Loader<D, RB> ld;
   ld.init(kbase, vbase, p.k_sk, p.v_sk, seq.Sk, w, lane);
 
+  // Staged rows: wave 0 loads the tile's 128-key slice of both heads' rows
+  // (lanes 0-31 head h, 32-63 head h + 1, 16 bytes each) with the K/V tile.
+  const __amdgpu_buffer_rsrc_t cbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.staged ? p.cb + (int64_t)b * p.cb_sb : nullptr), 0,
+      p.staged ? (int)(p.cb_sb * 4) : 0, 0x00020000);
+  uint32_t cboff = 0;
+  if (p.staged) {
+    const int hs = kvh * p.G + 2 * hp + (lane >> 5);
+    const int64_t hc = p.cb_hmode == 1 ? hs : (p.cb_hmode == 2 ? hs / p.G : 0);
+    cboff = (uint32_t)(hc * p.cb_sh * 4 + (lane & 31) * 16);
+  }
+  auto issue_cb = [&](int slot, int kt) {
+    if (p.staged && w == 0) {
+      const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)(&s_cb[slot][0][0]);
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(cboff + (uint32_t)kt * (kTile * 4)),
+            "s"(cbr)
+          : "memory");
+    }
+  };
+
   TileList tl;
   tl.init(p, b, kvh * p.G + 2 * hp, qt, seq.nK);  // identical for both heads of the pair
   const int ntiles = tl.count();
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
-  if (ntiles > 0) ld.issue(buf0, kt_cur, w);
+  if (ntiles > 0) {
+    ld.issue(buf0, kt_cur, w);
+    issue_cb(0, kt_cur);
+  }
   // One barrier per tile: it publishes tile i (every wave has awaited its own
   // loads of it) and frees the other buffer (every wave has finished tile
   // i - 1), so the loads of tile i + 1 go out right after it and overlap the
@@ -345,8 +396,12 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
     wait_vmcnt<0>();
     barrier();
-    if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
-    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk);
+    if (it + 1 < ntiles) {
+      ld.issue(nxt, kt_nxt, w);
+      issue_cb((it + 1) & 1, kt_nxt);
+    }
+    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
+                        &s_cb[it & 1][w / WPH][0]);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   }
@@ -379,7 +434,78 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   }
 }
 
+// Folded mask / bias rows: cb[b][hc][k] = bias * log2(e) (0 without a bias)
+// where the mask keeps key k < Sk, -inf elsewhere. Four keys per thread.
+__global__ __launch_bounds__(256) void k_aux_combine(AttnParams p, float* cb, int Hc) {
+  const int K4 = p.nK * (kTile / 4);
+  const int64_t n = (int64_t)p.B * Hc * K4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int k0 = (int)(i % K4) * 4;
+    const int64_t r = i / K4;
+    const int hc = (int)(r % Hc);
+    const int b = (int)(r / Hc);
+    // an iteration-space head whose row this is
+    const int h = p.cb_hmode == 1 ? hc : (p.cb_hmode == 2 ? hc * p.G : 0);
+    const uint8_t* mrow = p.mask_kind == 2 ? aux_row(p.mask, 1, b, h, p.G, 0) : nullptr;
+    const uint16_t* brow =
+        p.has_bias ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, 0)) : nullptr;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + e;
+      const bool keep = k < p.Sk && (mrow == nullptr || mrow[k] != 0);
+      o[e] = keep ? (brow ? bf16_to_f32(brow[k]) * kLog2e : 0.f) : -INFINITY;
+    }
+    *reinterpret_cast<float4*>(cb + r * ((int64_t)p.nK * kTile) + k0) =
+        make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 }  // namespace
+
+namespace {
+// head rule and head count of the folded rows
+void staged_heads(const AttnParams& p, int& hmode, int& Hc) {
+  const int mm = p.mask_kind == 2 ? p.mask.h_mode : 0;
+  const int bm = p.has_bias ? p.bias.h_mode : 0;
+  hmode = (mm == 1 || bm == 1) ? 1 : ((mm == 2 || bm == 2) ? 2 : 0);
+  Hc = hmode == 1 ? p.H : (hmode == 2 ? p.KVH : 1);
+}
+}  // namespace
+
+bool staged_aux_applies(const AttnParams& p) {
+  if (p.varlen || p.gather || p.mask_kind == 1) return false;
+  if (p.mask_kind != 2 && !p.has_bias) return false;
+  if (p.mask_kind == 2 && !p.mask.q_bcast) return false;
+  if (p.has_bias && !p.bias.q_bcast) return false;
+  int hmode, Hc;
+  staged_heads(p, hmode, Hc);
+  return (int64_t)Hc * p.nK * kTile * 4 < ((int64_t)1 << 31);  // 32-bit buffer offsets
+}
+
+int64_t staged_aux_bytes(const AttnParams& p) {
+  int hmode, Hc;
+  staged_heads(p, hmode, Hc);
+  const int64_t n = (int64_t)p.B * Hc * p.nK * kTile * 4;
+  return (n + 255) / 256 * 256;
+}
+
+hipError_t launch_aux_combine(AttnParams& p, void* ws, hipStream_t s) {
+  int hmode, Hc;
+  staged_heads(p, hmode, Hc);
+  p.staged = 1;
+  p.cb_hmode = hmode;
+  p.cb = static_cast<const float*>(ws);
+  p.cb_sh = (int64_t)p.nK * kTile;
+  p.cb_sb = Hc * p.cb_sh;
+  const int64_t n = (int64_t)p.B * Hc * p.nK * (kTile / 4);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_aux_combine, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256),
+                     0, s, p, static_cast<float*>(ws), Hc);
+  return hipGetLastError();
+}
 
 bool attn_v2_applies(const AttnParams& p, int D) {
   if (D != 64 && D != 128) return false;

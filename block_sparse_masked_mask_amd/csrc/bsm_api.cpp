@@ -757,9 +757,11 @@ int attn_fwd_workspace_size(const bsm_geom* geom, const bsm_attn_args* a, int64_
   int e = prepare_fwd(geom, a, g, p, empty);
   if (e) return e;
   *bytes = 0;
-  if (empty || p.gather || a->q.dtype != BSM_BF16 || !short_query_applies(p, (int)g.D))
-    return BSM_OK;
-  *bytes = group_plan(p, (int)g.D).ws_bytes;
+  if (empty || p.gather || a->q.dtype != BSM_BF16) return BSM_OK;
+  if (short_query_applies(p, (int)g.D))
+    *bytes = group_plan(p, (int)g.D).ws_bytes;
+  else if (attn_v2_applies(p, (int)g.D) && staged_aux_applies(p))
+    *bytes = staged_aux_bytes(p);
   return BSM_OK;
 }
 
@@ -785,7 +787,10 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
       }
       he = launch_attn_group(p, D, stream);
     } else if (attn_v2_applies(p, D)) {
-      he = launch_attn_bf16_v2(p, D, stream);
+      he = hipSuccess;
+      if (staged_aux_applies(p) && a->workspace_bytes >= staged_aux_bytes(p))
+        he = launch_aux_combine(p, a->workspace, stream);
+      if (he == hipSuccess) he = launch_attn_bf16_v2(p, D, stream);
     } else {
       he = launch_attn_bf16(p, D, stream);
     }

@@ -86,6 +86,14 @@ struct AttnParams {
   int32_t splits;
   float* ws_o;   // (splits, B, H, Sq, D)
   float* ws_ml;  // (splits, B, H, Sq, 2): running max (log2 units), row sum
+  // Staged mask and bias (bf16 long-query kernel): when both broadcast over
+  // the query dim, they are folded into one float row per (b, head) -- the
+  // bias in log2 units where the mask keeps a key below Sk, -inf elsewhere --
+  // whose 128-key slices travel to LDS with each K/V tile.
+  int32_t staged;
+  int32_t cb_hmode;     // head rule of the rows: 0 one row, 1 per head, 2 per KV head
+  const float* cb;      // (B, Hc, nK * 128) floats, contiguous
+  int64_t cb_sb, cb_sh; // element strides of b and of the row's head
 };
 
 // Backward: the forward's view plus the incoming gradient, the gradient
@@ -199,6 +207,11 @@ hipError_t launch_attn_bf16(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int D, hipStream_t s);
 // pipelined bf16 kernel: two heads of a KV group per workgroup
 bool attn_v2_applies(const AttnParams& p, int D);
+// Staged mask / bias rows for the pipelined kernel: whether they apply, the
+// workspace they take, and the pass that writes them (sets p.staged, p.cb...).
+bool staged_aux_applies(const AttnParams& p);
+int64_t staged_aux_bytes(const AttnParams& p);
+hipError_t launch_aux_combine(AttnParams& p, void* ws, hipStream_t s);
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
 // backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
 hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);

@@ -158,7 +158,8 @@ typedef struct {
   const bsm_key_list* keys;  /* nullable; key-gather visit: needs mask, no bm, bf16,
                                 and the list build_key_list made from that mask */
   void* workspace;           /* nullable; device scratch, 256-byte aligned, of at least */
-  int64_t workspace_bytes;   /*   attn_fwd_workspace_size's bytes to enable key splits */
+  int64_t workspace_bytes;   /*   attn_fwd_workspace_size's bytes (key splits, staged
+                                mask / bias rows) */
 } bsm_attn_args;
 
 /* In-block causality of a DFlash layer ([SF-905] Motivation; #934):
@@ -254,14 +255,21 @@ int dflash_dense_mask(const bsm_geom* geom, const bsm_dflash* pred,
 int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* args,
                     hipStream_t stream);
 
-/* Bytes of optional device workspace that lets masked_attn_fwd split the keys
- * of short query blocks (at most 32 query rows per (b, h) after the swap, bf16,
- * no key list) over several workgroups when the launch has few (b, head)
- * pairs -- a few sequences decoding against a long KV cache. 0 when no split
- * would be used. With a smaller or NULL workspace the same call runs unsplit;
- * the result is the same up to float rounding order. The split parts' float
- * partial states (O, running max, row sum) are merged as in the online
- * softmax ([FSA-190] Design: the swapped decode path of few rows). */
+/* Bytes of optional device workspace masked_attn_fwd can use for these
+ * arguments; 0 when it would use none. Two uses (bf16, no key list):
+ *  - short query blocks (at most 32 query rows per (b, h) after the swap):
+ *    the keys are split over several workgroups when the launch has few
+ *    (b, head) pairs -- a few sequences decoding against a long KV cache. The
+ *    split parts' float partial states (O, running max, row sum) are merged as
+ *    in the online softmax ([FSA-190] Design: the swapped decode path of few
+ *    rows);
+ *  - longer queries with a dense mask and/or a bias that broadcast over the
+ *    query dim (the dynamic top-k layout, [FSA-190] Changes): both are folded
+ *    first into one float row per (b, head) and key -- the bias in log2 units
+ *    where the mask keeps the key, -inf elsewhere -- which the attention reads
+ *    tile by tile with K and V.
+ * With a smaller or NULL workspace the same call runs without them; the result
+ * is the same up to float rounding order. */
 int attn_fwd_workspace_size(const bsm_geom* geom, const bsm_attn_args* args, int64_t* bytes);
 
 /* Arguments of masked_attn_bwd: the forward's inputs, its output O and LSE,

@@ -252,3 +252,64 @@ def test_dflash_bf16_d128_block_mask_or_not(case, with_bm):
     q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 4, 2, 128, "bf16", seed=30))
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d) if with_bm else None
     _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what=f"dflash bm={with_bm} {case}")
+
+
+def _fwd_ws_bytes(q, k, v, mask=None, bias=None, bm=None):
+    """Workspace bytes the library asks for (0: none would be used)."""
+    import ctypes
+    a = bsm.AttnArgs()
+    a.q, a.k, a.v = bsm.tensor4(q), bsm.tensor4(k), bsm.tensor4(v)
+    a.o = q.data_ptr()
+    for i in range(4):
+        a.o_stride[i] = q.stride(i)
+    keep = []
+    for name, t in (("mask", mask), ("bias", bias)):
+        if t is not None:
+            c = bsm.tensor4(t)
+            keep.append(c)
+            setattr(a, name, ctypes.pointer(c))
+    if bm is not None:
+        bc = bm.c()
+        keep.append(bc)
+        a.bm = ctypes.pointer(bc)
+    n = ctypes.c_int64(0)
+    bsm._check(bsm.lib().attn_fwd_workspace_size(ctypes.byref(bsm.geometry_of(q, k).c()),
+                                                 ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mshape,bshape", [
+    ((2, 2, 1, 768), (2, 4, 1, 768)),   # per-KV-head mask, per-head bias
+    ((1, 1, 1, 768), None),             # one mask row for everything
+    (None, (2, 1, 1, 768)),             # bias only, one row per batch
+    ((2, 4, 1, 768), (1, 2, 1, 768)),   # per-head mask, per-KV-head bias
+])
+def test_staged_mask_bias_rows(D, mshape, bshape):
+    """Query-broadcast mask / bias folded into staged rows: against the oracle
+    on every row, and against the same call without the workspace (the rows
+    then come from the mask / bias tensors directly)."""
+    B, Sq, Sk, H, KVH = 2, 260, 700, 4, 2
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=5))
+    mask = bias = None
+    if mshape is not None:
+        m = synth.random_bool(mshape, 0.4, 5, synth.TID_MASK)
+        m[..., 128:256] = False                      # an empty key tile
+        m[0, 0, 0, 3] = True
+        mask = torch.from_numpy(m).cuda()
+    if bshape is not None:
+        bias = synth.normal_tensor(bshape, 5, synth.TID_BIAS, "bf16").cuda()
+    # a per-head block mask goes to the one-head kernel, which stages nothing
+    bm = (bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+          if mask is not None and mshape[1] != H else None)
+    assert _fwd_ws_bytes(q, k, v, mask=mask, bias=bias, bm=bm) > 0
+    o, lse = _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, scale=0.09,
+                            what=f"staged m={mshape} b={bshape} D={D}")
+    o1, lse1 = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                   softmax_scale=0.09, return_lse=True, split=False)
+    torch.cuda.synchronize()
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
+    fin = torch.isfinite(lse1)
+    assert torch.equal(torch.isfinite(lse), fin)
+    if fin.any():
+        assert (lse[fin] - lse1[fin]).abs().max().item() <= 1e-3
