@@ -81,7 +81,7 @@ struct LaneOffs {
   }
 };
 
-template <int D, int RB>
+template <int D, int RB, bool ST>
 __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
                                     bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
                                     int lane, int Sk, const float* cbrow) {
@@ -136,10 +136,9 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       RowBlock<D>& R = rbk[r];
-      const bool plain =
-          !p.staged && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
+      const bool plain = !ST && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
       float mloc = -INFINITY;
-      if (p.staged) {
+      if (ST) {
         // the tile's slice of the folded mask / bias row: -inf drops a key
         // (masked or past Sk); rows past Sq compute values nobody stores
 #pragma unroll
@@ -265,7 +264,8 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
   }
 }
 
-template <int D, int RB>
+// ST: the mask / bias come as staged rows (p.staged)
+template <int D, int RB, bool ST>
 __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
   using C = V2Ctx<D, RB>;
   constexpr int NS = C::NS;
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
       const RowIv v = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
       R.iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
     }
-    R.mrow = (p.mask_kind == 2 && R.qvalid && !p.staged) ? aux_row(p.mask, 1, b, h, p.G, q)
-                                                          : nullptr;
-    R.brow = (p.has_bias && R.qvalid && !p.staged)
+    R.mrow = (p.mask_kind == 2 && R.qvalid && !ST) ? aux_row(p.mask, 1, b, h, p.G, q)
+                                                    : nullptr;
+    R.brow = (p.has_bias && R.qvalid && !ST)
         ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
 #pragma unroll
     for (int i = 0; i < NDC; ++i) R.oacc[i] = f32x16{};
@@ -355,16 +355,16 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   // Staged rows: wave 0 loads the tile's 128-key slice of both heads' rows
   // (lanes 0-31 head h, 32-63 head h + 1, 16 bytes each) with the K/V tile.
   const __amdgpu_buffer_rsrc_t cbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(p.staged ? p.cb + (int64_t)b * p.cb_sb : nullptr), 0,
-      p.staged ? (int)(p.cb_sb * 4) : 0, 0x00020000);
+      const_cast<float*>(ST ? p.cb + (int64_t)b * p.cb_sb : nullptr), 0,
+      ST ? (int)(p.cb_sb * 4) : 0, 0x00020000);
   uint32_t cboff = 0;
-  if (p.staged) {
+  if (ST) {
     const int hs = kvh * p.G + 2 * hp + (lane >> 5);
     const int64_t hc = p.cb_hmode == 1 ? hs : (p.cb_hmode == 2 ? hs / p.G : 0);
     cboff = (uint32_t)(hc * p.cb_sh * 4 + (lane & 31) * 16);
   }
   auto issue_cb = [&](int slot, int kt) {
-    if (p.staged && w == 0) {
+    if (ST && w == 0) {
       const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)(&s_cb[slot][0][0]);
       asm volatile(
           "s_mov_b32 m0, %0\n\t"
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
       ld.issue(nxt, kt_nxt, w);
       issue_cb((it + 1) & 1, kt_nxt);
     }
-    compute_tile<D, RB>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
+    compute_tile<D, RB, ST>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
                         &s_cb[it & 1][w / WPH][0]);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
@@ -524,12 +524,22 @@ hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
 #define BSM_V2_RB 1
 #endif
   constexpr int RB = BSM_V2_RB;
-  if (D == 128)
-    hipLaunchKernelGGL((k_attn_bf16_v2<128, RB>), dim3(nWork), dim3(V2Ctx<128, RB>::NT), 0, s,
-                       p, nWork);
-  else
-    hipLaunchKernelGGL((k_attn_bf16_v2<64, RB>), dim3(nWork), dim3(V2Ctx<64, RB>::NT), 0, s,
-                       p, nWork);
+  const dim3 grid(nWork);
+  if (D == 128) {
+    if (p.staged)
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, true>), grid, dim3(V2Ctx<128, RB>::NT), 0, s,
+                         p, nWork);
+    else
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, false>), grid, dim3(V2Ctx<128, RB>::NT), 0, s,
+                         p, nWork);
+  } else {
+    if (p.staged)
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, true>), grid, dim3(V2Ctx<64, RB>::NT), 0, s, p,
+                         nWork);
+    else
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, false>), grid, dim3(V2Ctx<64, RB>::NT), 0, s,
+                         p, nWork);
+  }
   return hipGetLastError();
 }
 
