@@ -233,6 +233,208 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
   }
 }
 
+// ------------------------------------------------- dQ, two heads per workgroup
+//
+// The layout of the pipelined forward (attn_v2.hip): 512 threads, waves 0-3
+// take 128 query rows of head h and waves 4-7 the same rows of head h + 1 of
+// the same KV group (their block-mask row is shared), K and V tiles reach LDS
+// by LDS-DMA, double buffered, V with its transposed-read swizzle. Per 32-key
+// chunk: S^T = K Q^T, dP^T = V dO^T, dS, then dQ^T += K^T dS^T.
+
+// Per-lane LDS byte offsets of the operand reads, computed once. A 32-key chunk
+// adds 32 rows, a 16-key step 16 rows: neither changes a swizzle.
+struct DqOffs {
+  uint32_t krow[kNS];   // K rows (A of S^T): row perm_row(n), chunk 2 s + hh
+  uint32_t vrow[kNS];   // V rows (A of dP^T), V swizzle
+  uint32_t kc0[kNDC];   // K^T (A of dQ^T): first and second transposed reads
+  uint32_t kc1[kNDC];   //   of d chunk dc at key 0
+  __device__ inline void init(int lane) {
+    const int hh = lane >> 5;
+    const int row = perm_row(lane & 31);
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      krow[s] = (uint32_t)(row * kRowB + (((2 * s + hh) ^ swz_k<kD>(row)) * 16));
+      vrow[s] = (uint32_t)(row * kRowB + (((2 * s + hh) ^ swz_v<kD>(row)) * 16));
+    }
+    const int blk = lane >> 4;
+    const int e4 = (lane >> 2) & 3;
+    const int g4 = lane & 3;
+    const int row0 = 8 * (blk >> 1) + e4;
+    const int row1 = row0 + 4;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc) {
+      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+      kc0[dc] = (uint32_t)(row0 * kRowB + ((chunk ^ swz_k<kD>(row0)) * 16) + (g4 & 1) * 8);
+      kc1[dc] = (uint32_t)(row1 * kRowB + ((chunk ^ swz_k<kD>(row1)) * 16) + (g4 & 1) * 8);
+    }
+  }
+};
+
+__global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWork) {
+  const AttnParams& f = P.f;
+  __shared__ __align__(1024) Tiles<kD> buf0;
+  __shared__ __align__(1024) Tiles<kD> buf1;
+
+  // work items (b, KV-group head pair, query tile) as in the pipelined forward
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds;
+  const int pairs = f.G / 2;
+  const int ngrp = nWork / f.nQ;
+  int qt, grp;
+  if (ngrp % kXcds == 0) {
+    const int gx = ngrp / kXcds;
+    const int li = L / kXcds;
+    qt = f.nQ - 1 - li / gx;
+    grp = xcd * gx + li % gx;
+  } else {
+    const int per = nWork / kXcds;
+    const int rem = nWork % kXcds;
+    const int wi = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
+    qt = f.nQ - 1 - wi % f.nQ;
+    grp = wi / f.nQ;
+  }
+  const int hp = grp % pairs;
+  grp /= pairs;
+  const int kvh = grp % f.KVH;
+  const int b = grp / f.KVH;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int h0 = kvh * f.G + 2 * hp;
+  const int h = h0 + (w >> 2);
+  const int q = qt * kTile + 32 * (w & 3) + n;
+  const bool qvalid = q < f.Sq;
+
+  bf16x8 qf[kNS], df[kNS];
+  {
+    const __bf16* qr = reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb +
+                       (int64_t)q * f.q_sq + (int64_t)h * f.q_sh;
+    const __bf16* dr = reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb +
+                       (int64_t)q * P.do_sq + (int64_t)h * P.do_sh;
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hh) : bf16x8{};
+      df[s] = qvalid ? *reinterpret_cast<const bf16x8*>(dr + 16 * s + 8 * hh) : bf16x8{};
+    }
+  }
+  const float lse2 =
+      qvalid ? f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
+                   kLog2e
+             : -INFINITY;
+  const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
+  const bool live = lse2 != -INFINITY;
+  RowIv32 iv{0, 0, 0, 0};
+  if (f.mask_kind == 1) {
+    const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+    iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
+  }
+  f32x16 dq[kNDC];
+#pragma unroll
+  for (int i = 0; i < kNDC; ++i) dq[i] = f32x16{};
+
+  DqOffs off;
+  off.init(lane);
+  Loader<kD, 1> ld;
+  ld.init(reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb + (int64_t)kvh * f.k_sh,
+          reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb + (int64_t)kvh * f.v_sh,
+          f.k_sk, f.v_sk, f.Sk, w, lane);
+  TileList tl;
+  tl.init(f, b, h0, qt);  // identical for both heads of the pair
+  const int ntiles = tl.count();
+  bool full_cur = false;
+  int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
+  // Q, dO, LSE and Delta have arrived before the first DMA goes out, so no
+  // wait for them inside the loop also waits for a tile
+  wait_vmcnt<0>();
+  if (ntiles > 0) ld.issue(buf0, kt_cur, w);
+  for (int it = 0; it < ntiles; ++it) {
+    const Tiles<kD>& cur = (it & 1) ? buf1 : buf0;
+    Tiles<kD>& nxt = (it & 1) ? buf0 : buf1;
+    bool full_nxt = false;
+    const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
+    wait_vmcnt<0>();
+    barrier();
+    if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
+
+    const int k0 = kt_cur * kTile;
+    const bool test = !full_cur || k0 + kTile > f.Sk || !qvalid;
+    const char* kb = reinterpret_cast<const char*>(cur.k);
+    const char* vb = reinterpret_cast<const char*>(cur.v);
+#pragma unroll
+    for (int c = 0; c < kTile / 32; ++c) {
+      f32x16 st = f32x16{}, dpt = f32x16{};
+      bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + off.krow[0] + c * 32 * kRowB);
+      bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + off.vrow[0] + c * 32 * kRowB);
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) {
+        const bf16x8 a = ka, v = va;
+        if (s + 1 < kNS) {
+          ka = *reinterpret_cast<const bf16x8*>(kb + off.krow[s + 1] + c * 32 * kRowB);
+          va = *reinterpret_cast<const bf16x8*>(vb + off.vrow[s + 1] + c * 32 * kRowB);
+        }
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, df[s], dpt, 0, 0, 0);
+      }
+      // lane: row q, keys k0 + 32 c + 16 sb + 8 hh + e for value 8 sb + e
+      float ds[16];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kbk = k0 + 32 * c + 16 * sb + 8 * hh;
+        uint32_t bits = 0xFFu;
+        if (test) {
+          if (!full_cur && f.mask_kind == 1)
+            bits = range_bits(iv.lo1, iv.hi1, kbk) | range_bits(iv.lo2, iv.hi2, kbk);
+          bits &= range_bits(0, f.Sk, kbk);
+          if (!qvalid) bits = 0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 8 * sb + e;
+          const float pr = (live && ((bits >> e) & 1u))
+                               ? __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, -lse2))
+                               : 0.f;
+          ds[u] = pr * (dpt[u] - delta);
+        }
+      }
+      const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+#pragma unroll
+      for (int dc = 0; dc < kNDC; ++dc) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int rows = (32 * c + 16 * j) * kRowB;
+          const i16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc0[dc] + rows));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc1[dc] + rows));
+          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                   __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
+                                                   4, 5, 6, 7);
+          dq[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j ? d1 : d0, dq[dc], 0, 0, 0);
+        }
+      }
+    }
+    kt_cur = kt_nxt;
+    full_cur = full_nxt;
+  }
+  if (qvalid) {
+    __bf16* out = reinterpret_cast<__bf16*>(P.dq) + (int64_t)b * P.dq_sb + (int64_t)q * P.dq_sq +
+                  (int64_t)h * P.dq_sh;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dq[dc][4 * g + e] * P.scale);
+        *reinterpret_cast<bf16x4*>(out + dc * 32 + 8 * g + 4 * hh) = v4;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dK / dV
 
 __device__ inline int tile_class_of(const AttnParams& f, int b, int h, int qt, int kt) {
@@ -454,7 +656,19 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
   const AttnParams& f = p.f;
   const int64_t nq = (int64_t)f.B * f.H * f.nQ;
   const int64_t nk = (int64_t)f.B * f.KVH * f.nK;
-  if (nq > 0) hipLaunchKernelGGL(k_bwd_dq_mfma, dim3(nq), dim3(kThreads), 0, s, p);
+  // the two-head pipelined dQ kernel needs head pairs that share their block
+  // mask row and K / V offsets within 32 bits
+  const bool pair = f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1) && !f.varlen &&
+                    (int64_t)f.Sk * f.k_sk * 2 < ((int64_t)1 << 31) &&
+                    (int64_t)f.Sk * f.v_sk * 2 < ((int64_t)1 << 31);
+  if (nq > 0) {
+    if (pair) {
+      const int nWork = (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
+      hipLaunchKernelGGL(k_bwd_dq_pair, dim3(nWork), dim3(512), 0, s, p, nWork);
+    } else {
+      hipLaunchKernelGGL(k_bwd_dq_mfma, dim3(nq), dim3(kThreads), 0, s, p);
+    }
+  }
   if (nk > 0) hipLaunchKernelGGL(k_bwd_dkdv_mfma, dim3(nk), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
