@@ -25,6 +25,7 @@
 
 #include "attn_common.h"
 #include "attn_pipe.h"
+#include "block_scan.h"
 #include "bsm_internal.h"
 #include "dflash_rows.h"
 
@@ -38,6 +39,7 @@ constexpr int kNS = kD / 16;    // 16-wide d steps
 constexpr int kNDC = kD / 32;   // 32-wide d chunks
 constexpr int kRowB = kD * 2;   // bytes per bf16 row
 constexpr int kThreads = 256;
+constexpr int kMaxVisits = 4096;  // (head, query tile) positions listed in LDS by dK / dV
 
 // 128 x 128 bf16 tile in LDS, rows swizzled in 16-byte chunks like the forward's
 // K tiles (conflict-free row reads).
@@ -459,6 +461,38 @@ __device__ inline int tile_class_of(const AttnParams& f, int b, int h, int qt, i
   return 0;
 }
 
+// Per-lane LDS byte offsets of the dK / dV kernel's operand reads, computed
+// once: Q rows (K swizzle) and dO rows (V swizzle) as A operands of S and dP,
+// and the transposed reads of dO (V swizzle: the second read is 4 rows down)
+// and of Q (K swizzle: its own offset). A 32-row block or a 16-row step adds
+// rows without changing a swizzle.
+struct DkdvOffs {
+  uint32_t qrow[kNS], drow[kNS];
+  uint32_t dc0[kNDC];
+  uint32_t qc0[kNDC], qc1[kNDC];
+  __device__ inline void init(int lane) {
+    const int hh = lane >> 5;
+    const int row = perm_row(lane & 31);
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) {
+      qrow[s] = (uint32_t)(row * kRowB + (((2 * s + hh) ^ swz_k<kD>(row)) * 16));
+      drow[s] = (uint32_t)(row * kRowB + (((2 * s + hh) ^ swz_v<kD>(row)) * 16));
+    }
+    const int blk = lane >> 4;
+    const int e4 = (lane >> 2) & 3;
+    const int g4 = lane & 3;
+    const int row0 = 8 * (blk >> 1) + e4;
+    const int row1 = row0 + 4;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc) {
+      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+      dc0[dc] = (uint32_t)(row0 * kRowB + ((chunk ^ swz_v<kD>(row0)) * 16) + (g4 & 1) * 8);
+      qc0[dc] = (uint32_t)(row0 * kRowB + ((chunk ^ swz_k<kD>(row0)) * 16) + (g4 & 1) * 8);
+      qc1[dc] = (uint32_t)(row1 * kRowB + ((chunk ^ swz_k<kD>(row1)) * 16) + (g4 & 1) * 8);
+    }
+  }
+};
+
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) {
   const AttnParams& f = P.f;
   // two slots: Q tile (.k) and dO tile (.v) of a visited (head, query tile), with
@@ -500,9 +534,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   f32x16 dk[kNDC], dv[kNDC];
 #pragma unroll
   for (int i = 0; i < kNDC; ++i) dk[i] = dv[i] = f32x16{};
+  DkdvOffs off;
+  off.init(lane);
 
   // visits: positions pos = g * nQ + qt whose tile (qt, kt) of head g is not empty
   const int end = f.G * f.nQ;
+  // Up to kMaxVisits positions, the workgroup classifies them all first, one
+  // thread per position (the block-mask lookups run side by side, not one
+  // dependent search per visit), and keeps the non-empty ones in order in LDS.
+  __shared__ uint16_t s_vis[kMaxVisits];  // pos << 2 | class
+  __shared__ int s_scan[kThreads / 64];
+  const bool listed = end <= kMaxVisits;
+  int nvis = 0;
+  if (listed) {
+    for (int base = 0; base < end; base += kThreads) {
+      const int ps = base + tid;
+      const int c = ps < end ? tile_class_of(f, b, kvh * f.G + ps / f.nQ, ps % f.nQ, kt) : 0;
+      int tot;
+      const int o = block_excl_sum<kThreads / 64>(c != 0 ? 1 : 0, s_scan, tot);
+      if (c != 0) s_vis[nvis + o] = (uint16_t)((ps << 2) | c);
+      nvis += tot;
+    }
+    __syncthreads();
+  }
+  auto listed_visit = [&](int i, int& cls) {
+    const int v = __builtin_amdgcn_readfirstlane((int)s_vis[i]);
+    cls = v & 3;
+    return v >> 2;
+  };
   auto next_visit = [&](int pos, int& cls) {
     for (; pos < end; ++pos) {
       cls = __builtin_amdgcn_readfirstlane(
@@ -556,29 +615,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     ld.issue(buf[sl], pos % f.nQ, w);
   };
 
+  // the visit after visit `it` (at position pos), or end
+  auto following = [&](int it, int pos, int& cls) {
+    if (listed) return it + 1 < nvis ? listed_visit(it + 1, cls) : end;
+    return next_visit(pos + 1, cls);
+  };
   int cls = 0;
-  int pos = next_visit(0, cls);
+  int pos = listed ? (nvis > 0 ? listed_visit(0, cls) : end) : next_visit(0, cls);
   if (pos < end) prepare(0, pos, cls);
   for (int it = 0; pos < end; ++it) {
     const int sl = it & 1;
     wait_vmcnt<0>();   // this visit's tiles (this thread's share)
     __syncthreads();   // everyone's share, and the row data; slot sl ^ 1 is free
     int ncls = 0;
-    const int npos = next_visit(pos + 1, ncls);
+    const int npos = following(it, pos, ncls);
     if (npos < end) prepare(sl ^ 1, npos, ncls);
     const bool test = cls == 1 || test_k;
-    const __bf16* tq = buf[sl].k;
-    const __bf16* tdo = buf[sl].v;
+    const char* tq = reinterpret_cast<const char*>(buf[sl].k);
+    const char* tdo = reinterpret_cast<const char*>(buf[sl].v);
+    auto ld8 = [](const char* a) { return *reinterpret_cast<const bf16x8*>(a); };
+    auto tr8 = [](const char* a0, const char* a1) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+      return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                     __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 #pragma unroll
     for (int rb = 0; rb < kTile / 32; ++rb) {
+      const int rbo = rb * 32 * kRowB;
       f32x16 s = f32x16{}, dp = f32x16{};
+      // row operands one d-step ahead
+      bf16x8 qa = ld8(tq + off.qrow[0] + rbo), da = ld8(tdo + off.drow[0] + rbo);
 #pragma unroll
       for (int ds_ = 0; ds_ < kNS; ++ds_) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<false>(tq, rb, ds_, lane), kf[ds_], s,
-                                                    0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<true>(tdo, rb, ds_, lane), vf[ds_],
-                                                     dp, 0, 0, 0);
+        const bf16x8 a = qa, d = da;
+        if (ds_ + 1 < kNS) {
+          qa = ld8(tq + off.qrow[ds_ + 1] + rbo);
+          da = ld8(tdo + off.drow[ds_ + 1] + rbo);
+        }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ds_], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d, vf[ds_], dp, 0, 0, 0);
       }
+      // the first transposed operands load while P and dS are computed
+      bf16x8 dca = tr8(tdo + off.dc0[0] + rbo, tdo + off.dc0[0] + rbo + 4 * kRowB);
+      bf16x8 qca = tr8(tq + off.qc0[0] + rbo, tq + off.qc1[0] + rbo);
       // lane: key, rows rb*32 + 16 st + 8 hh + e for value u = 8 st + e
       float pv[16], dsv[16];
 #pragma unroll
@@ -586,10 +666,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
         const int r0 = rb * 32 + 16 * st + 8 * hh;
         const float4 la = *reinterpret_cast<const float4*>(&s_lse2[sl][r0]);
         const float4 lb = *reinterpret_cast<const float4*>(&s_lse2[sl][r0 + 4]);
-        const float4 da = *reinterpret_cast<const float4*>(&s_delta[sl][r0]);
-        const float4 db = *reinterpret_cast<const float4*>(&s_delta[sl][r0 + 4]);
+        const float4 da4 = *reinterpret_cast<const float4*>(&s_delta[sl][r0]);
+        const float4 db4 = *reinterpret_cast<const float4*>(&s_delta[sl][r0 + 4]);
         const float l2[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float dl[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+        const float dl[8] = {da4.x, da4.y, da4.z, da4.w, db4.x, db4.y, db4.z, db4.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * st + e;
@@ -598,23 +678,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
             const int kk = 32 * w + n;  // key within the tile
             keep = keep && ((s_keep[sl][r0 + e][kk >> 6] >> (kk & 63)) & 1u);
           }
-          const float pr = keep ? __builtin_amdgcn_exp2f(s[u] * f.scale_log2 - l2[e]) : 0.f;
+          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, -l2[e])) : 0.f;
           pv[u] = pr;
           dsv[u] = pr * (dp[u] - dl[e]);
         }
       }
       const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
       const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+      // dV^T += dO^T P and dK^T += Q^T dS: operand i = (dc, half j), one ahead
 #pragma unroll
-      for (int dc = 0; dc < kNDC; ++dc) {
-        dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<true>(tdo, dc, rb * 32, lane), p0,
-                                                         dv[dc], 0, 0, 0);
-        dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<true>(tdo, dc, rb * 32 + 16, lane),
-                                                         p1, dv[dc], 0, 0, 0);
-        dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<false>(tq, dc, rb * 32, lane), s0,
-                                                         dk[dc], 0, 0, 0);
-        dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op<false>(tq, dc, rb * 32 + 16, lane),
-                                                         s1, dk[dc], 0, 0, 0);
+      for (int i = 0; i < 2 * kNDC; ++i) {
+        const int dc = i / 2, j = i % 2;
+        const bf16x8 a = dca, qb = qca;
+        if (i + 1 < 2 * kNDC) {
+          const int dn = (i + 1) / 2, jn = (i + 1) % 2;
+          const int o = rbo + 16 * jn * kRowB;
+          dca = tr8(tdo + off.dc0[dn] + o, tdo + off.dc0[dn] + o + 4 * kRowB);
+          qca = tr8(tq + off.qc0[dn] + o, tq + off.qc1[dn] + o);
+        }
+        dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j ? p1 : p0, dv[dc], 0, 0, 0);
+        dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, j ? s1 : s0, dk[dc], 0, 0, 0);
       }
     }
     pos = npos;
