@@ -395,9 +395,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
-          const float pr = (live && ((bits >> e) & 1u))
-                               ? __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, -lse2))
-                               : 0.f;
+          // computed, then selected: a branch per element would split the
+          // block the MFMAs overlap with
+          const float ex = __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, -lse2));
+          const float pr = (live && ((bits >> e) & 1u)) ? ex : 0.f;
           ds[u] = pr * (dpt[u] - delta);
         }
       }
@@ -670,15 +671,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
         const float4 db4 = *reinterpret_cast<const float4*>(&s_delta[sl][r0 + 4]);
         const float l2[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
         const float dl[8] = {da4.x, da4.y, da4.z, da4.w, db4.x, db4.y, db4.z, db4.w};
+        // keep bits of this lane's key for the 8 rows, read together (a
+        // branch per element would split the block the MFMAs overlap with)
+        uint32_t bits = 0xFFu;
+        if (test) {
+          const int kk = 32 * w + n;  // key within the tile
+          bits = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            bits |= (uint32_t)((s_keep[sl][r0 + e][kk >> 6] >> (kk & 63)) & 1u) << e;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * st + e;
-          bool keep = l2[e] != -INFINITY;
-          if (test) {
-            const int kk = 32 * w + n;  // key within the tile
-            keep = keep && ((s_keep[sl][r0 + e][kk >> 6] >> (kk & 63)) & 1u);
-          }
-          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, -l2[e])) : 0.f;
+          const float ex = __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, -l2[e]));
+          const float pr = (((bits >> e) & 1u) && l2[e] != -INFINITY) ? ex : 0.f;
           pv[u] = pr;
           dsv[u] = pr * (dp[u] - dl[e]);
         }
