@@ -97,12 +97,14 @@ struct Loader {
   // the two buffers apart); completion is awaited explicitly with wait_vmcnt
   // before the barrier that publishes a buffer. The instruction has no
   // destination register: data goes to LDS at m0 + 16 * lane.
-  __device__ inline void issue(Tiles<D>& t, int kt, int w) const {
+  __device__ inline void issue(Tiles<D>& t, int kt, int w) const { issue(t.k, t.v, kt, w); }
+  // the same into separate K and V tiles of LDS (kTile * D elements each)
+  __device__ inline void issue(__bf16* tk, __bf16* tv, int kt, int w) const {
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
       const int slot = (j * C::NW + w) * 64;  // first 16-byte slot of the wave
-      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
-      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
+      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(tk + slot * 8);
+      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(tv + slot * 8);
       const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
       const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
       asm volatile(

@@ -30,6 +30,8 @@
 //    bias and have all rows valid take a leaner softmax.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_pipe.h"
 #include "bsm_internal.h"
@@ -76,13 +78,17 @@ struct LaneOffs {
 #pragma unroll
     for (int dc = 0; dc < D / 32; ++dc) {
       const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
-      v[dc] = (uint32_t)((row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4) * 2);
+      v[dc] = (uint32_t)(2 * kTile * D * 2 +
+                         (row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4) * 2);
     }
   }
 };
 
-template <int D, int RB, bool ST>
-__device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int kt,
+// SLOT: which of the two K and V buffers of lds holds the tile; a constant
+// (0, 1) makes every LDS operand address a lane offset plus an immediate, -1
+// takes it from slot_rt
+template <int D, int RB, int MODE, int SLOT>
+__device__ inline void compute_tile(const char* lds, int slot_rt, const AttnParams& p, int kt,
                                     bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
                                     int lane, int Sk, const float* cbrow) {
   constexpr int NS = D / 16;
@@ -91,8 +97,11 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
   const int k0 = kt * kTile;
   const bool check_k = k0 + kTile > Sk;
   const bool check_mask = !is_full && p.mask_kind != 0;
-  const char* kbase = reinterpret_cast<const char*>(t.k);
-  const char* vbase = reinterpret_cast<const char*>(t.v);
+  // K slot SLOT at SLOT * TB; the V slots' extra 2 * TB is in the lane offsets
+  constexpr int TB = kTile * D * 2;
+  const int slot = SLOT >= 0 ? SLOT : slot_rt;
+  const char* kbase = lds + slot * TB;
+  const char* vbase = lds + slot * TB;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
 #pragma unroll
@@ -136,9 +145,9 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       RowBlock<D>& R = rbk[r];
-      const bool plain = !ST && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
+      const bool plain = MODE != 2 && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
       float mloc = -INFINITY;
-      if (ST) {
+      if (MODE == 2) {
         // the tile's slice of the folded mask / bias row: -inf drops a key
         // (masked or past Sk); rows past Sq compute values nobody stores
 #pragma unroll
@@ -174,7 +183,7 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
           for (int sb = 0; sb < 2; ++sb) {
             const int kb = k0 + kc * 32 + 16 * sb + 8 * hh;  // 8 consecutive keys
             float bv[8];
-            if (R.brow) {
+            if (MODE == 1 && R.brow) {
               const uint4 raw = *reinterpret_cast<const uint4*>(R.brow + kb);
               const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -186,7 +195,7 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
             }
             uint32_t mbits = 0xFFu;
             if (check_mask) {
-              if (p.mask_kind == 2) {
+              if (MODE == 1 && p.mask_kind == 2) {
                 uint2 mb = make_uint2(0, 0);
                 if (R.mrow) mb = *reinterpret_cast<const uint2*>(R.mrow + kb);
                 mbits = 0;
@@ -264,15 +273,19 @@ __device__ inline void compute_tile(const Tiles<D>& t, const AttnParams& p, int 
   }
 }
 
-// ST: the mask / bias come as staged rows (p.staged)
-template <int D, int RB, bool ST>
+// MODE 0: no mask tensor and no bias (the DFlash predicate or nothing);
+// 1: mask / bias rows read per tile; 2: staged rows (p.staged)
+template <int D, int RB, int MODE>
 __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
   using C = V2Ctx<D, RB>;
   constexpr int NS = C::NS;
   constexpr int NDC = C::NDC;
   constexpr int WPH = C::NW / 2;  // waves per head
-  __shared__ __align__(1024) Tiles<D> buf0;
-  __shared__ __align__(1024) Tiles<D> buf1;
+  // K tiles (slots 0, 1), then V tiles (slots 0, 1)
+  constexpr int TB = kTile * D * 2;
+  __shared__ __align__(1024) char s_kv[4 * TB];
+  auto kslot = [&](int sl) { return reinterpret_cast<__bf16*>(s_kv + sl * TB); };
+  auto vslot = [&](int sl) { return reinterpret_cast<__bf16*>(s_kv + (2 + sl) * TB); };
   __shared__ __align__(16) float s_cb[2][2][kTile];  // staged rows: buffer, head of the pair
 
   // Work items: (head-pair group, query tile). Workgroup L runs on XCD L % 8.
@@ -334,9 +347,9 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
       const RowIv v = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
       R.iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
     }
-    R.mrow = (p.mask_kind == 2 && R.qvalid && !ST) ? aux_row(p.mask, 1, b, h, p.G, q)
-                                                    : nullptr;
-    R.brow = (p.has_bias && R.qvalid && !ST)
+    R.mrow = (MODE == 1 && p.mask_kind == 2 && R.qvalid) ? aux_row(p.mask, 1, b, h, p.G, q)
+                                                         : nullptr;
+    R.brow = (MODE == 1 && p.has_bias && R.qvalid)
         ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q)) : nullptr;
 #pragma unroll
     for (int i = 0; i < NDC; ++i) R.oacc[i] = f32x16{};
@@ -355,16 +368,16 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   // Staged rows: wave 0 loads the tile's 128-key slice of both heads' rows
   // (lanes 0-31 head h, 32-63 head h + 1, 16 bytes each) with the K/V tile.
   const __amdgpu_buffer_rsrc_t cbr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(ST ? p.cb + (int64_t)b * p.cb_sb : nullptr), 0,
-      ST ? (int)(p.cb_sb * 4) : 0, 0x00020000);
+      const_cast<float*>(MODE == 2 ? p.cb + (int64_t)b * p.cb_sb : nullptr), 0,
+      MODE == 2 ? (int)(p.cb_sb * 4) : 0, 0x00020000);
   uint32_t cboff = 0;
-  if (ST) {
+  if (MODE == 2) {
     const int hs = kvh * p.G + 2 * hp + (lane >> 5);
     const int64_t hc = p.cb_hmode == 1 ? hs : (p.cb_hmode == 2 ? hs / p.G : 0);
     cboff = (uint32_t)(hc * p.cb_sh * 4 + (lane & 31) * 16);
   }
   auto issue_cb = [&](int slot, int kt) {
-    if (ST && w == 0) {
+    if (MODE == 2 && w == 0) {
       const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)(&s_cb[slot][0][0]);
       asm volatile(
           "s_mov_b32 m0, %0\n\t"
@@ -382,28 +395,38 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
   if (ntiles > 0) {
-    ld.issue(buf0, kt_cur, w);
+    ld.issue(kslot(0), vslot(0), kt_cur, w);
     issue_cb(0, kt_cur);
   }
   // One barrier per tile: it publishes tile i (every wave has awaited its own
   // loads of it) and frees the other buffer (every wave has finished tile
   // i - 1), so the loads of tile i + 1 go out right after it and overlap the
   // whole of tile i's compute.
-  for (int it = 0; it < ntiles; ++it) {
-    Tiles<D>& cur = (it & 1) ? buf1 : buf0;
-    Tiles<D>& nxt = (it & 1) ? buf0 : buf1;
+  auto step = [&](auto slot_c, int it) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const int cs = SLOT >= 0 ? SLOT : (it & 1);  // slot of tile it
     bool full_nxt = false;
     const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) {
-      ld.issue(nxt, kt_nxt, w);
-      issue_cb((it + 1) & 1, kt_nxt);
+      ld.issue(kslot(cs ^ 1), vslot(cs ^ 1), kt_nxt, w);
+      issue_cb(cs ^ 1, kt_nxt);
     }
-    compute_tile<D, RB, ST>(cur, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
-                        &s_cb[it & 1][w / WPH][0]);
+    compute_tile<D, RB, MODE, SLOT>(s_kv, cs, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
+                                    &s_cb[cs][w / WPH][0]);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
+  };
+  if constexpr (MODE == 0) {
+    // fixed slots: no address arithmetic per LDS read
+    for (int it = 0; it < ntiles; it += 2) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
+    }
+  } else {
+    // the mask / bias paths keep one copy (two would not fit the registers)
+    for (int it = 0; it < ntiles; ++it) step(std::integral_constant<int, -1>{}, it);
   }
 
 #pragma unroll
@@ -525,20 +548,23 @@ hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
 #endif
   constexpr int RB = BSM_V2_RB;
   const dim3 grid(nWork);
+  const int mode = p.staged ? 2 : ((p.mask_kind == 2 || p.has_bias) ? 1 : 0);
   if (D == 128) {
-    if (p.staged)
-      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, true>), grid, dim3(V2Ctx<128, RB>::NT), 0, s,
-                         p, nWork);
+    constexpr int NT = V2Ctx<128, RB>::NT;
+    if (mode == 2)
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 2>), grid, dim3(NT), 0, s, p, nWork);
+    else if (mode == 1)
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 1>), grid, dim3(NT), 0, s, p, nWork);
     else
-      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, false>), grid, dim3(V2Ctx<128, RB>::NT), 0, s,
-                         p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 0>), grid, dim3(NT), 0, s, p, nWork);
   } else {
-    if (p.staged)
-      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, true>), grid, dim3(V2Ctx<64, RB>::NT), 0, s, p,
-                         nWork);
+    constexpr int NT = V2Ctx<64, RB>::NT;
+    if (mode == 2)
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 2>), grid, dim3(NT), 0, s, p, nWork);
+    else if (mode == 1)
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 1>), grid, dim3(NT), 0, s, p, nWork);
     else
-      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, false>), grid, dim3(V2Ctx<64, RB>::NT), 0, s,
-                         p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 0>), grid, dim3(NT), 0, s, p, nWork);
   }
   return hipGetLastError();
 }
