@@ -50,8 +50,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "c85785297c82feeb",
-                "fetch_kib": 86535.8, "write_kib": 65536.0,
+                "sha256_16": "e4f08729c2c45557",
+                "fetch_kib": 86556.2, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
