@@ -144,12 +144,6 @@ __device__ inline float max_pair(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-#ifdef BSM_MFMA_PRIO
-#define BSM_PRIO(x) __builtin_amdgcn_s_setprio(x)
-#else
-#define BSM_PRIO(x)
-#endif
-
 // A row's running max is raised only when a new score exceeds it by more than
 // this many powers of two; until then probabilities are taken against the
 // stale max and stay below 2^kRescaleLog2 (exact after the final division, which

@@ -107,7 +107,6 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     f32x16 sacc[RB][2];
-    BSM_PRIO(1);
     // K operand i of this half: chunk c = i / NS, k-step s = i % NS
     auto kop = [&](int i) {
       const int c = i / NS, s = i % NS;
@@ -124,7 +123,6 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
         sacc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             a, rbk[r].qf[s], s == 0 ? f32x16{} : sacc[r][c], 0, 0, 0);
     }
-    BSM_PRIO(0);
     // V operand i of this half: d-chunk dc = i / 4, key chunk c = (i / 2) % 2,
     // 16-key step sb = i % 2; two transposed reads of 4 keys each
     auto vop = [&](int i) {
@@ -257,7 +255,6 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    BSM_PRIO(1);
 #pragma unroll
     for (int i = 0; i < 4 * NDC; ++i) {
       const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
@@ -269,7 +266,6 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
         rbk[r].oacc[dc] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r][c][sb], rbk[r].oacc[dc], 0, 0, 0);
     }
-    BSM_PRIO(0);
   }
 }
 
@@ -543,10 +539,7 @@ bool attn_v2_applies(const AttnParams& p, int D) {
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
   const int nWork = p.B * p.KVH * (p.G / 2) * p.nQ;
   if (nWork == 0) return hipSuccess;
-#ifndef BSM_V2_RB
-#define BSM_V2_RB 1
-#endif
-  constexpr int RB = BSM_V2_RB;
+  constexpr int RB = 1;  // one 32-row block per wave (the 512-thread layout)
   const dim3 grid(nWork);
   const int mode = p.staged ? 2 : ((p.mask_kind == 2 || p.has_bias) ? 1 : 0);
   if (D == 128) {
