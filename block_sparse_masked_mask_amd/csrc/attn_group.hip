@@ -60,11 +60,16 @@ __device__ inline void load_gaux(int kt, int w, int hh, const uint8_t* const (&m
     }
 }
 
-template <int D, int RB>
-__global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
+// RB: 32-row blocks of the workgroup. With RB = 2, SPLIT gives each row block
+// its own four waves (512 threads, two waves per SIMD, one row block each);
+// otherwise every wave carries all RB row blocks.
+template <int D, int RB, bool SPLIT>
+__global__ __launch_bounds__(64 * kGWaves * (SPLIT ? 2 : 1), 1) void k_attn_group(AttnParams p) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
   constexpr int ROWS = 32 * RB;
+  constexpr int WRB = SPLIT ? 1 : RB;  // row blocks of one wave
+  static_assert(!SPLIT || RB == 2, "split row blocks come in pairs");
   __shared__ __align__(1024) Tiles<D> buf[2];
   __shared__ float s_m[kGWaves][ROWS];
   __shared__ float s_l[kGWaves][ROWS];
@@ -88,19 +93,21 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
   const int R = p.pack * p.Sq;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = tid >> 6;             // loader slot of the wave
+  const int kw = SPLIT ? (w & 3) : w;  // the wave's 32 keys of each tile
+  const int rb0 = SPLIT ? (w >> 2) : 0;  // the wave's first row block
   const int n = lane & 31;
   const int hh = lane >> 5;
 
-  // this lane's rows: r = 32 rb + n is query r % Sq of head h0 + r / Sq
-  bf16x8 qf[RB][NS];
-  RowIv32 iv[RB];
-  const uint8_t* mrow[RB];
-  const uint16_t* brow[RB];
-  bool rvalid[RB];
+  // this lane's rows: r = 32 (rb0 + rb) + n is query r % Sq of head h0 + r / Sq
+  bf16x8 qf[WRB][NS];
+  RowIv32 iv[WRB];
+  const uint8_t* mrow[WRB];
+  const uint16_t* brow[WRB];
+  bool rvalid[WRB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 32 * rb + n;
+  for (int rb = 0; rb < WRB; ++rb) {
+    const int r = 32 * (rb0 + rb) + n;
     rvalid[rb] = r < R;
     const int q = rvalid[rb] ? r % p.Sq : 0;
     const int h = h0 + (rvalid[rb] ? r / p.Sq : 0);
@@ -123,13 +130,13 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
                         (int64_t)kvh * p.k_sh;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         (int64_t)kvh * p.v_sh;
-  Loader<D, kGRB> ld;
+  Loader<D, SPLIT ? 1 : kGRB> ld;
   ld.init(kbase, vbase, p.k_sk, p.v_sk, p.Sk, w, lane);
 
-  f32x16 oacc[RB][NDC];
-  float m_run[RB], l_run[RB];
+  f32x16 oacc[WRB][NDC];
+  float m_run[WRB], l_run[WRB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < WRB; ++rb) {
 #pragma unroll
     for (int i = 0; i < NDC; ++i) oacc[rb][i] = f32x16{};
     m_run[rb] = -INFINITY;
@@ -148,10 +155,10 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
   const int t1 = (int)((int64_t)(sp + 1) * ntot / S);
   bool full_cur = false;
   int kt_cur = t0 < t1 ? tl.tile(t0, full_cur) : 0;
-  GAux aux_cur[RB], aux_nxt[RB];
+  GAux aux_cur[WRB], aux_nxt[WRB];
   if (t0 < t1) {
     ld.issue(buf[0], kt_cur, w);
-    load_gaux<RB>(kt_cur, w, hh, mrow, brow, aux_cur);
+    load_gaux<WRB>(kt_cur, kw, hh, mrow, brow, aux_cur);
   }
   for (int it = t0; it < t1; ++it) {
     const Tiles<D>& t = buf[(it - t0) & 1];
@@ -162,30 +169,30 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
     barrier();
     if (it + 1 < t1) {
       ld.issue(nxt, kt_nxt, w);
-      load_gaux<RB>(kt_nxt, w, hh, mrow, brow, aux_nxt);
+      load_gaux<WRB>(kt_nxt, kw, hh, mrow, brow, aux_nxt);
     }
     const int k0 = kt_cur * kTile;
-    const int krow = w * 32 + perm_row(n);
-    f32x16 sc[RB];
+    const int krow = kw * 32 + perm_row(n);
+    f32x16 sc[WRB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sc[rb] = f32x16{};
+    for (int rb = 0; rb < WRB; ++rb) sc[rb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(t.k + krow * D +
                                                         (((2 * s + hh) ^ swz_k<D>(krow)) * 8));
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < WRB; ++rb)
         sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], sc[rb], 0, 0, 0);
     }
     const bool check_k = k0 + kTile > p.Sk;
     const bool check_mask = !full_cur && p.mask_kind != 0;
-    bf16x8 pf[RB][2];
+    bf16x8 pf[WRB][2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < WRB; ++rb) {
       float mloc = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int kb = k0 + 32 * w + 16 * sb + 8 * hh;
+        const int kb = k0 + 32 * kw + 16 * sb + 8 * hh;
         uint32_t mbits = 0xFFu;
         if (check_mask) {
           if (p.mask_kind == 2) {
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
     for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int kb = w * 32 + 16 * sb;
+        const int kb = kw * 32 + 16 * sb;
         const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
         const int row0 = kb + 8 * (blk >> 1) + e4;
         const int row1 = row0 + 4;
@@ -256,13 +263,13 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
                                                  __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
                                                  5, 6, 7);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < WRB; ++rb)
           oacc[rb][dc] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][sb], oacc[rb][dc], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) aux_cur[rb] = aux_nxt[rb];
+    for (int rb = 0; rb < WRB; ++rb) aux_cur[rb] = aux_nxt[rb];
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   }
@@ -272,27 +279,27 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
   barrier();
   float* sO = reinterpret_cast<float*>(&buf[0]);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 32 * rb + n;
+  for (int rb = 0; rb < WRB; ++rb) {
+    const int r = 32 * (rb0 + rb) + n;
     const float l_pair = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(&sO[((int64_t)w * ROWS + r) * D + dc * 32 + 8 * g + 4 * hh]) =
+        *reinterpret_cast<float4*>(&sO[((int64_t)kw * ROWS + r) * D + dc * 32 + 8 * g + 4 * hh]) =
             make_float4(oacc[rb][dc][4 * g], oacc[rb][dc][4 * g + 1], oacc[rb][dc][4 * g + 2],
                         oacc[rb][dc][4 * g + 3]);
     if (hh == 0) {
-      s_m[w][r] = m_run[rb];
-      s_l[w][r] = l_pair;
+      s_m[kw][r] = m_run[rb];
+      s_l[kw][r] = l_pair;
     }
   }
   __syncthreads();
   // each wave finishes 32 / RB ... all rows: lanes (n, hh) of wave w cover row
   // r = 32 rb + n and d-chunks dc = w, w + 4, ...
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 32 * rb + n;
+  for (int rb = 0; rb < WRB; ++rb) {
+    const int r = 32 * (rb0 + rb) + n;
     if (!rvalid[rb]) continue;
     float mstar = -INFINITY;
 #pragma unroll
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
     __bf16* orow = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb + (int64_t)q * p.o_sq +
                    (int64_t)h * p.o_sh;
     const int64_t prow = (((int64_t)sp * p.B + b) * p.H + h) * p.Sq + q;
-    for (int dc = w; dc < NDC; dc += kGWaves) {
+    for (int dc = kw; dc < NDC; dc += kGWaves) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = dc * 32 + 8 * g + 4 * hh;
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(64 * kGWaves, 1) void k_attn_group(AttnParams p) {
         }
       }
     }
-    if (w == 0 && hh == 0) {
+    if (kw == 0 && hh == 0) {
       if (S == 1) {
         if (p.lse)
           p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)q * p.lse_sq] =
@@ -399,17 +406,17 @@ hipError_t launch_attn_group(const AttnParams& p, int D, hipStream_t s) {
   const int64_t nwg = (int64_t)p.B * (p.H / p.pack) * p.splits;
   if (nwg == 0) return hipSuccess;
   const int rb = p.pack * p.Sq > 32 ? 2 : 1;
-  const dim3 blk(64 * kGWaves);
+  const dim3 blk(64 * kGWaves), blk2(128 * kGWaves);
   if (D == 128) {
     if (rb == 2)
-      hipLaunchKernelGGL((k_attn_group<128, 2>), dim3((unsigned)nwg), blk, 0, s, p);
+      hipLaunchKernelGGL((k_attn_group<128, 2, true>), dim3((unsigned)nwg), blk2, 0, s, p);
     else
-      hipLaunchKernelGGL((k_attn_group<128, 1>), dim3((unsigned)nwg), blk, 0, s, p);
+      hipLaunchKernelGGL((k_attn_group<128, 1, false>), dim3((unsigned)nwg), blk, 0, s, p);
   } else {
     if (rb == 2)
-      hipLaunchKernelGGL((k_attn_group<64, 2>), dim3((unsigned)nwg), blk, 0, s, p);
+      hipLaunchKernelGGL((k_attn_group<64, 2, true>), dim3((unsigned)nwg), blk2, 0, s, p);
     else
-      hipLaunchKernelGGL((k_attn_group<64, 1>), dim3((unsigned)nwg), blk, 0, s, p);
+      hipLaunchKernelGGL((k_attn_group<64, 1, false>), dim3((unsigned)nwg), blk, 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
