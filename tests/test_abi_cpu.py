@@ -401,6 +401,44 @@ def test_forward_workspace_sizes(L):
         bsm.BSM_E_ARG  # misaligned workspace
 
 
+def test_forward_staged_row_workspace(L):
+    """Longer queries with a mask / bias that broadcast over the query dim ask
+    for one float row per (b, head of the widest rule) and key: the dynamic
+    top-k layout (mask and bias per KV head) needs B * KVH * K_round floats; a
+    per-head bias makes it B * H; per-query tensors or the predicate need none."""
+    geom = (2, 16, 4, 8000, 8000, 128)
+    Kr = 8064
+    keep = []
+
+    def need(mshape=None, bshape=None, dtype=bsm.BSM_BF16, **kw):
+        a = _attn_args(geom, dtype=dtype)
+        if mshape is not None:
+            m = _t4(mshape, bsm.BSM_BOOL)
+            keep.append(m)
+            a.mask = ctypes.pointer(m)
+        if bshape is not None:
+            bt = _t4(bshape, dtype)
+            keep.append(bt)
+            a.bias = ctypes.pointer(bt)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        n = ctypes.c_int64(-1)
+        assert L.attn_fwd_workspace_size(ctypes.byref(bsm.Geom(*geom)), ctypes.byref(a),
+                                         ctypes.byref(n)) == 0
+        return n.value
+
+    def rows(nrows):
+        return (nrows * Kr * 4 + 255) // 256 * 256
+    assert need((2, 4, 1, Kr), (2, 4, 1, Kr)) == rows(2 * 4)
+    assert need((2, 4, 1, Kr), (2, 16, 1, Kr)) == rows(2 * 16)
+    assert need((1, 1, 1, Kr), None) == rows(2 * 1)
+    assert need(None, (2, 1, 1, Kr)) == rows(2 * 1)
+    assert need((2, 4, 8000, Kr), (2, 4, 1, Kr)) == 0   # per-query mask
+    assert need(None, (2, 16, 8000, Kr)) == 0           # per-query bias
+    assert need(None, None) == 0
+    assert need((2, 4, 1, Kr), (2, 4, 1, Kr), dtype=bsm.BSM_F32) == 0  # f32 kernel
+
+
 def test_topk_fused_validation(L):
     geom = bsm.Geom(2, 16, 4, 8000, 8000, 128)
     bias = _t4((2, 4, 1, 8064), bsm.BSM_BF16)
