@@ -272,7 +272,8 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
 // MODE 0: no mask tensor and no bias (the DFlash predicate or nothing);
 // 1: mask / bias rows read per tile; 2: staged rows (p.staged)
 template <int D, int RB, int MODE>
-__global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int nWork) {
+__global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int nWork,
+                                                               const WorkOrder order) {
   using C = V2Ctx<D, RB>;
   constexpr int NS = C::NS;
   constexpr int NDC = C::NDC;
@@ -294,7 +295,16 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   const int pairs = p.G / 2;
   const int ngrp = nWork / p.nQ;
   int qt, grp;
-  if (p.varlen) {
+  if (p.varlen && order.n > 0) {
+    // Packed sequences, items in the host's order (heaviest first, by their
+    // visible key tiles): KVH * pairs workgroups per item, (KV head, pair)
+    // fastest, so a (b, KV head)'s work stays on one XCD.
+    const int per = p.KVH * pairs;
+    const int it = order.item[L / per];
+    const int b = it >> 10;
+    qt = it & 1023;
+    grp = b * per + L % per;
+  } else if (p.varlen) {
     // Packed sequences differ in cost: spread each sequence's groups over the
     // XCDs (group g on XCD g % 8 when the group count is a multiple of 8) and
     // run every group's heaviest (last) query tiles first; tiles past a
@@ -536,8 +546,11 @@ bool attn_v2_applies(const AttnParams& p, int D) {
   return true;
 }
 
-hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
-  const int nWork = p.B * p.KVH * (p.G / 2) * p.nQ;
+hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s,
+                               const WorkOrder* order) {
+  static const WorkOrder kNoOrder{};  // n = 0
+  const WorkOrder& ord = (order && p.varlen) ? *order : kNoOrder;
+  const int nWork = ord.n > 0 ? ord.n * p.KVH * (p.G / 2) : p.B * p.KVH * (p.G / 2) * p.nQ;
   if (nWork == 0) return hipSuccess;
   constexpr int RB = 1;  // one 32-row block per wave (the 512-thread layout)
   const dim3 grid(nWork);
@@ -545,19 +558,19 @@ hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s) {
   if (D == 128) {
     constexpr int NT = V2Ctx<128, RB>::NT;
     if (mode == 2)
-      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 2>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 2>), grid, dim3(NT), 0, s, p, nWork, ord);
     else if (mode == 1)
-      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 1>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 1>), grid, dim3(NT), 0, s, p, nWork, ord);
     else
-      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 0>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<128, RB, 0>), grid, dim3(NT), 0, s, p, nWork, ord);
   } else {
     constexpr int NT = V2Ctx<64, RB>::NT;
     if (mode == 2)
-      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 2>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 2>), grid, dim3(NT), 0, s, p, nWork, ord);
     else if (mode == 1)
-      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 1>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 1>), grid, dim3(NT), 0, s, p, nWork, ord);
     else
-      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 0>), grid, dim3(NT), 0, s, p, nWork);
+      hipLaunchKernelGGL((k_attn_bf16_v2<64, RB, 0>), grid, dim3(NT), 0, s, p, nWork, ord);
   }
   return hipGetLastError();
 }

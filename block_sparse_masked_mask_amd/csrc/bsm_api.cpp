@@ -11,13 +11,17 @@
 // view.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "bsm.h"
 #include "bsm_internal.h"
+#include "dflash_rows.h"
 
 using namespace bsm;
 
@@ -1040,6 +1044,61 @@ int build_block_mask_varlen(const bsm_varlen* vl, const bsm_dflash* pred,
                     "build_block_mask_varlen");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Heaviest-first order of a packed launch's (sequence, query tile) items, from
+// the host copies of cu_seqlens: the cost of an item is the number of key
+// tiles its rows see -- under the DFlash predicate the tiles spanned by the
+// context interval of its first row up to the context end of its last row,
+// plus those of its draft keys (the rows' intervals are monotone in the row);
+// without a mask, all of the sequence's key tiles. The order is an estimate
+// only: every item is still computed from the block mask or the predicate.
+// Leaves n = 0 (the kernel's own order) past kMaxOrder items or 64 sequences.
+void varlen_order(const bsm_varlen* vl, const VarlenInfo& vi, const DFlashRule* rule,
+                  WorkOrder& ord) {
+  ord.n = 0;
+  if (vi.B > 64 || vi.nQ > 1024) return;
+  std::vector<std::pair<int64_t, int>> items;  // (-cost, b << 10 | qt)
+  for (int64_t b = 0; b < vi.B; ++b) {
+    const int64_t Sq = vl->cu_seqlens_q_host[b + 1] - vl->cu_seqlens_q_host[b];
+    const int64_t Sk = vl->cu_seqlens_k_host[b + 1] - vl->cu_seqlens_k_host[b];
+    const int64_t nQ = (Sq + kTile - 1) / kTile;
+    const int64_t nK = (Sk + kTile - 1) / kTile;
+    DFlashRule r{};
+    if (rule) {  // the sequence's own geometry, as the kernels complete it
+      r = *rule;
+      r.C = Sk - Sq;
+      const int64_t nb = Sq / r.bs;
+      if (r.S == 0) r.S = nb > 0 ? r.C / nb : 0;
+    }
+    for (int64_t qt = 0; qt < nQ; ++qt) {
+      int64_t cost = nK;
+      if (rule) {
+        const RowIv a = dflash_row(r, qt * kTile);
+        const RowIv z = dflash_row(r, std::min(Sq, (qt + 1) * kTile) - 1);
+        auto span = [](int64_t lo, int64_t hi) {
+          return hi > lo ? (hi - 1) / kTile - lo / kTile + 1 : (int64_t)0;
+        };
+        cost = span(a.lo1, std::max(a.hi1, z.hi1)) + span(a.lo2, z.hi2);
+      }
+      items.emplace_back(-cost, (int)((b << 10) | qt));
+    }
+  }
+  if ((int64_t)items.size() > kMaxOrder) return;
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
+                     return x.first < y.first;
+                   });
+  for (size_t i = 0; i < items.size(); ++i) ord.item[i] = (uint16_t)items[i].second;
+  ord.n = (int32_t)items.size();
+}
+
+}  // namespace
+
+extern "C" {
+
 int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* a, hipStream_t stream) {
   VarlenInfo vi;
   int e = check_varlen(vl, vi);
@@ -1116,10 +1175,13 @@ int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* a, hipStre
   p.cu_k = vl->cu_seqlens_k;
   hipError_t he;
   if (dt == BSM_BF16) {
-    if (attn_v2_applies(p, (int)g.D))
-      he = launch_attn_bf16_v2(p, (int)g.D, stream);
-    else
+    if (attn_v2_applies(p, (int)g.D)) {
+      WorkOrder ord;
+      varlen_order(vl, vi, a->pred ? &p.rule : nullptr, ord);
+      he = launch_attn_bf16_v2(p, (int)g.D, stream, &ord);
+    } else {
       he = launch_attn_bf16(p, (int)g.D, stream);
+    }
   } else {
     he = launch_attn_f32(p, (int)g.D, stream);
   }

@@ -212,7 +212,16 @@ bool attn_v2_applies(const AttnParams& p, int D);
 bool staged_aux_applies(const AttnParams& p);
 int64_t staged_aux_bytes(const AttnParams& p);
 hipError_t launch_aux_combine(AttnParams& p, void* ws, hipStream_t s);
-hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s);
+// Order in which a packed (varlen) launch of the pipelined kernel takes its
+// (sequence, query tile) items: item[i] = b << 10 | qt, heaviest first; each
+// item spans KVH * G / 2 workgroups. n = 0: the kernel's own order.
+constexpr int kMaxOrder = 1024;
+struct WorkOrder {
+  int32_t n;
+  uint16_t item[kMaxOrder];
+};
+hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s,
+                               const WorkOrder* order = nullptr);
 // backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
 hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
