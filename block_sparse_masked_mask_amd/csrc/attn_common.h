@@ -99,11 +99,14 @@ struct TileList {
   // key tile of visit i, and whether it is full (no mask test needed)
   __device__ inline int tile(int i, bool& is_full) const {
     is_full = i < nfull;
+    // read through the constant address space: with a uniform index the load
+    // is a scalar one, which neither waits for nor is waited on by vector loads
+    typedef const __attribute__((address_space(4))) int32_t cint32;
     int kt;
     if (is_full)
-      kt = full ? full[i] : i;
+      kt = full ? ((cint32*)full)[i] : i;
     else
-      kt = part ? part[i - nfull] : i - nfull;
+      kt = part ? ((cint32*)part)[i - nfull] : i - nfull;
     return __builtin_amdgcn_readfirstlane(kt);  // uniform across the workgroup
   }
 };

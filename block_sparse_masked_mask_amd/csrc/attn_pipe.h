@@ -98,6 +98,25 @@ struct Loader {
   // before the barrier that publishes a buffer. The instruction has no
   // destination register: data goes to LDS at m0 + 16 * lane.
   __device__ inline void issue(Tiles<D>& t, int kt, int w) const { issue(t.k, t.v, kt, w); }
+  // the same with the LDS byte addresses of the K and V tiles given as
+  // workgroup-uniform integers (w uniform too), so that every destination
+  // address is scalar arithmetic
+  __device__ inline void issue_at(uint32_t lk0, uint32_t lv0, int kt, int w) const {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const uint32_t slot = (uint32_t)((j * C::NW + w) * 64 * 16);
+      const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
+      const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+          "s_mov_b32 m0, %3\n\t"
+          "buffer_load_dwordx4 %4, %5, 0 offen lds"
+          :
+          : "s"(lk0 + slot), "v"(ok), "s"(kr), "s"(lv0 + slot), "v"(ov), "s"(vr)
+          : "memory");
+    }
+  }
   // the same into separate K and V tiles of LDS (kTile * D elements each)
   __device__ inline void issue(__bf16* tk, __bf16* tv, int kt, int w) const {
 #pragma unroll

@@ -24,6 +24,10 @@
 //  * Work items (b, KV group pair, query tile) are laid out so that each XCD
 //    keeps the query tiles of the same (b, kvh) (one L2 per XCD) and runs the
 //    heaviest query tiles first.
+//  * A tile's softmax takes one max over its 128 keys; the LDS operand reads
+//    run several MFMAs ahead (K five, V three) and the exponentials of the
+//    tile's second half issue between the PV MFMAs of its first half. The
+//    mask / bias path, short of registers for that, takes two halves of 64.
 //  * The running max of a row is raised only when it grows by more than 2^8
 //    (otherwise O is not rescaled), row sums come from dot2 on the bf16
 //    probabilities the PV product uses, and tiles that need no mask test, no
@@ -84,6 +88,10 @@ struct LaneOffs {
   }
 };
 
+// One key tile: S^T of all four 32-key chunks, one max (and at most one
+// rescale) per row, then the probabilities and PV of the first 64 keys, with
+// the second half's exponentials issued between the first half's PV MFMAs.
+// The LDS operand reads are kept several MFMAs ahead of their use.
 // SLOT: which of the two K and V buffers of lds holds the tile; a constant
 // (0, 1) makes every LDS operand address a lane offset plus an immediate, -1
 // takes it from slot_rt
@@ -91,6 +99,233 @@ template <int D, int RB, int MODE, int SLOT>
 __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnParams& p, int kt,
                                     bool is_full, RowBlock<D>* rbk, const LaneOffs<D>& off,
                                     int lane, int Sk, const float* cbrow) {
+  constexpr int NS = D / 16;
+  constexpr int NDC = D / 32;
+  const int hh = lane >> 5;
+  const int k0 = kt * kTile;
+  const bool check_k = k0 + kTile > Sk;
+  const bool check_mask = !is_full && p.mask_kind != 0;
+  // K slot SLOT at SLOT * TB; the V slots' extra 2 * TB is in the lane offsets
+  constexpr int TB = kTile * D * 2;
+  const int slot = SLOT >= 0 ? SLOT : slot_rt;
+  const char* kbase = lds + slot * TB;
+  const char* vbase = lds + slot * TB;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T for the tile's four 32-key chunks
+  f32x16 sacc[RB][4];
+  auto kop = [&](int i) {
+    const int c = i / NS, s = i % NS;
+    return *reinterpret_cast<const bf16x8*>(kbase + off.k[s] + c * 32 * D * 2);
+  };
+  {
+    constexpr int PK = 5;  // K operands in flight
+    bf16x8 ka[PK];
+#pragma unroll
+    for (int j = 0; j < PK; ++j) ka[j] = kop(j);
+#pragma unroll
+    for (int i = 0; i < 4 * NS; ++i) {
+      const int c = i / NS, s = i % NS;
+      const bf16x8 a = ka[i % PK];
+      if (i + PK < 4 * NS) ka[i % PK] = kop(i + PK);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        sacc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, rbk[r].qf[s], s == 0 ? f32x16{} : sacc[r][c], 0, 0, 0);
+    }
+    // keep PK operand reads in flight ahead of the MFMAs (left alone, the
+    // scheduler issues each read right before its MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, PK, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+      if (i + PK < 4 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  // V operand i of a half: d-chunk dc = i / 4, key chunk c = (i / 2) % 2,
+  // 16-key step sb = i % 2; two transposed reads of 4 keys each
+  auto vop = [&](int half, int i) {
+    const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
+    const int kb = (2 * half + c) * 32 + 16 * sb;
+    const char* a0 = vbase + off.v[dc] + kb * D * 2;
+    const char* a1 = a0 + 4 * D * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                   __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // the first V operands load while the softmax runs
+  constexpr int NV = 4 * NDC;  // V operands per half
+  constexpr int PV = 3;        // V operands in flight
+  bf16x8 va[PV];
+#pragma unroll
+  for (int j = 0; j < PV; ++j) va[j] = vop(j / NV, j % NV);
+
+  // scores in log2 units, masked keys at -inf; one max (and at most one
+  // rescale) per row and tile
+  bool plain[RB];
+  float m_use[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    RowBlock<D>& R = rbk[r];
+    plain[r] = MODE != 2 && !check_k && !check_mask && R.brow == nullptr && R.qvalid;
+    float mloc = -INFINITY;
+    if (MODE == 2) {
+      // the tile's slice of the folded mask / bias row: -inf drops a key
+      // (masked or past Sk); rows past Sq compute values nobody stores
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const float4 c0 = *reinterpret_cast<const float4*>(cbrow + kc * 32 + 16 * sb + 8 * hh);
+          const float4 c1 =
+              *reinterpret_cast<const float4*>(cbrow + kc * 32 + 16 * sb + 8 * hh + 4);
+          const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 8 * sb + e;
+            const float sv = fmaf(sacc[r][kc][u], p.scale_log2, cv[e]);
+            sacc[r][kc][u] = sv;
+            mloc = fmaxf(mloc, sv);
+          }
+        }
+      }
+    } else if (plain[r]) {
+      // raw scores: the scale is folded into the exponent below
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) mloc = fmaxf(mloc, sacc[r][kc][u]);
+      mloc *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int kb = k0 + kc * 32 + 16 * sb + 8 * hh;  // 8 consecutive keys
+          float bv[8];
+          if (MODE == 1 && R.brow) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(R.brow + kb);
+            const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+          }
+          uint32_t mbits = 0xFFu;
+          if (check_mask) {
+            if (MODE == 1 && p.mask_kind == 2) {
+              uint2 mb = make_uint2(0, 0);
+              if (R.mrow) mb = *reinterpret_cast<const uint2*>(R.mrow + kb);
+              mbits = 0;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+                mbits |= (byte != 0u ? 1u : 0u) << e;
+              }
+            } else {
+              mbits = range_bits(R.iv.lo1, R.iv.hi1, kb) | range_bits(R.iv.lo2, R.iv.hi2, kb);
+            }
+          }
+          if (!R.qvalid) mbits = 0;
+          if (check_k) mbits &= range_bits(0, Sk, kb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 8 * sb + e;
+            float sv = sacc[r][kc][u] * p.scale_log2 + bv[e];
+            sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
+            sacc[r][kc][u] = sv;
+            mloc = fmaxf(mloc, sv);
+          }
+        }
+      }
+    }
+    mloc = max_pair(mloc);
+    // conditional rescale (see kRescaleLog2)
+    const bool grow = mloc > R.m_run + kRescaleLog2;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mloc : R.m_run;
+      // 1 where the max is kept (also for rows still at -inf: -inf - -inf is NaN)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(R.m_run - m_new) : 1.f;
+      R.l_run *= alpha;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) R.oacc[dc] *= alpha;
+      R.m_run = m_new;
+    }
+    m_use[r] = R.m_run == -INFINITY ? 0.f : R.m_run;
+  }
+
+  // probabilities of key chunks 2 * half and 2 * half + 1, as the PV product's
+  // B operand, and their bf16 row sum
+  auto probs = [&](int half, bf16x8 (&pf)[RB][2][2]) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const float mul = plain[r] ? p.scale_log2 : 1.f;
+      float lsum = rbk[r].l_run;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int u = 8 * sb + e;
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(sacc[r][2 * half + c][u], mul, -m_use[r]));
+            const float x1 =
+                __builtin_amdgcn_exp2f(fmaf(sacc[r][2 * half + c][u + 1], mul, -m_use[r]));
+            const bf16x2 pr = {(__bf16)x0, (__bf16)x1};
+            pf[r][c][sb][e] = pr[0];
+            pf[r][c][sb][e + 1] = pr[1];
+            // row sum of the bf16 probabilities the PV product uses
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          }
+        }
+      }
+      rbk[r].l_run = lsum;
+    }
+  };
+  auto pv = [&](int half, const bf16x8 (&pf)[RB][2][2]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int dc = i / 4, c = (i / 2) % 2, sb = i % 2;
+      // operand g of the tile; the next half's operands follow on
+      const int g = half * NV + i;
+      const bf16x8 a = va[g % PV];
+      if (g + PV < 2 * NV) va[g % PV] = vop((g + PV) / NV, (g + PV) % NV);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        rbk[r].oacc[dc] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r][c][sb], rbk[r].oacc[dc], 0, 0, 0);
+    }
+  };
+  bf16x8 pf0[RB][2][2], pf1[RB][2][2];
+  probs(0, pf0);
+  __builtin_amdgcn_sched_barrier(0);
+  // the second half's exponentials can issue under the first half's PV MFMAs
+  pv(0, pf0);
+  probs(1, pf1);
+  pv(1, pf1);
+  // PV MFMAs of the first half with the second half's exponentials between
+  // them, V operand reads PV operands ahead
+#pragma unroll
+  for (int i = 0; i < 2 * NV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 1);
+    if (i + PV < 2 * NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+  }
+}
+
+// The mask / bias path (MODE 1), which has no registers for a whole tile's
+// scores: the tile in two halves of 64 keys, each with its own max.
+// SLOT: which of the two K and V buffers of lds holds the tile; a constant
+// (0, 1) makes every LDS operand address a lane offset plus an immediate, -1
+// takes it from slot_rt
+template <int D, int RB, int MODE, int SLOT>
+__device__ inline void compute_tile_halves(const char* lds, int slot_rt, const AttnParams& p,
+                                           int kt, bool is_full, RowBlock<D>* rbk,
+                                           const LaneOffs<D>& off, int lane, int Sk,
+                                           const float* cbrow) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
   const int hh = lane >> 5;
@@ -281,8 +516,10 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   // K tiles (slots 0, 1), then V tiles (slots 0, 1)
   constexpr int TB = kTile * D * 2;
   __shared__ __align__(1024) char s_kv[4 * TB];
-  auto kslot = [&](int sl) { return reinterpret_cast<__bf16*>(s_kv + sl * TB); };
-  auto vslot = [&](int sl) { return reinterpret_cast<__bf16*>(s_kv + (2 + sl) * TB); };
+  // LDS byte addresses of the K and V slots
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)s_kv;
+  auto kslot = [&](int sl) { return lds0 + (uint32_t)(sl * TB); };
+  auto vslot = [&](int sl) { return lds0 + (uint32_t)((2 + sl) * TB); };
   __shared__ __align__(16) float s_cb[2][2][kTile];  // staged rows: buffer, head of the pair
 
   // Work items: (head-pair group, query tile). Workgroup L runs on XCD L % 8.
@@ -333,6 +570,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int h = kvh * p.G + 2 * hp + w / WPH;
@@ -398,10 +636,13 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   TileList tl;
   tl.init(p, b, kvh * p.G + 2 * hp, qt, seq.nK);  // identical for both heads of the pair
   const int ntiles = tl.count();
-  bool full_cur = false;
+  bool full_cur = false, full_nxt = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
+  // the next tile's index is read one step ahead, so that its load has a
+  // whole tile to arrive in
+  int kt_nxt = ntiles > 1 ? tl.tile(1, full_nxt) : 0;
   if (ntiles > 0) {
-    ld.issue(kslot(0), vslot(0), kt_cur, w);
+    ld.issue_at(kslot(0), vslot(0), kt_cur, wu);
     issue_cb(0, kt_cur);
   }
   // One barrier per tile: it publishes tile i (every wave has awaited its own
@@ -411,18 +652,24 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   auto step = [&](auto slot_c, int it) {
     constexpr int SLOT = decltype(slot_c)::value;
     const int cs = SLOT >= 0 ? SLOT : (it & 1);  // slot of tile it
-    bool full_nxt = false;
-    const int kt_nxt = it + 1 < ntiles ? tl.tile(it + 1, full_nxt) : 0;
     wait_vmcnt<0>();
     barrier();
     if (it + 1 < ntiles) {
-      ld.issue(kslot(cs ^ 1), vslot(cs ^ 1), kt_nxt, w);
+      ld.issue_at(kslot(cs ^ 1), vslot(cs ^ 1), kt_nxt, wu);
       issue_cb(cs ^ 1, kt_nxt);
     }
-    compute_tile<D, RB, MODE, SLOT>(s_kv, cs, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
-                                    &s_cb[cs][w / WPH][0]);
+    bool full_nn = false;
+    const int kt_nn = it + 2 < ntiles ? tl.tile(it + 2, full_nn) : 0;
+    if constexpr (MODE == 1)
+      compute_tile_halves<D, RB, MODE, SLOT>(s_kv, cs, p, kt_cur, full_cur, rbk, off, lane,
+                                             seq.Sk, &s_cb[cs][w / WPH][0]);
+    else
+      compute_tile<D, RB, MODE, SLOT>(s_kv, cs, p, kt_cur, full_cur, rbk, off, lane, seq.Sk,
+                                      &s_cb[cs][w / WPH][0]);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
+    kt_nxt = kt_nn;
+    full_nxt = full_nn;
   };
   if constexpr (MODE == 0) {
     // fixed slots: no address arithmetic per LDS read

@@ -312,4 +312,8 @@ def test_staged_mask_bias_rows(D, mshape, bshape):
     fin = torch.isfinite(lse1)
     assert torch.equal(torch.isfinite(lse), fin)
     if fin.any():
-        assert (lse[fin] - lse1[fin]).abs().max().item() <= 1e-3
+        # the two paths round their probabilities to bf16 against different
+        # running maxima (one per tile / one per 64 keys); each row sum then
+        # carries a relative error of at most 2^-9, so the LSEs may differ by
+        # up to 2 * 2^-9
+        assert (lse[fin] - lse1[fin]).abs().max().item() <= 2 * 2.0 ** -9
