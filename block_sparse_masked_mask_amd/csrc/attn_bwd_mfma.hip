@@ -38,6 +38,8 @@ constexpr int kD = 128;
 constexpr int kNS = kD / 16;    // 16-wide d steps
 constexpr int kNDC = kD / 32;   // 32-wide d chunks
 constexpr int kRowB = kD * 2;   // bytes per bf16 row
+constexpr int kAhead = 3;       // row operands (d-steps) read ahead of their MFMAs
+constexpr int kTrAhead = 2;     // transposed operands read ahead
 constexpr int kThreads = 256;
 constexpr int kMaxVisits = 4096;  // (head, query tile) positions listed in LDS by dK / dV
 
@@ -368,18 +370,26 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
 #pragma unroll
     for (int c = 0; c < kTile / 32; ++c) {
       f32x16 st = f32x16{}, dpt = f32x16{};
-      bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + off.krow[0] + c * 32 * kRowB);
-      bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + off.vrow[0] + c * 32 * kRowB);
+      // row operands kAhead d-steps ahead
+      bf16x8 ka[kAhead], va[kAhead];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) {
+        ka[j] = *reinterpret_cast<const bf16x8*>(kb + off.krow[j] + c * 32 * kRowB);
+        va[j] = *reinterpret_cast<const bf16x8*>(vb + off.vrow[j] + c * 32 * kRowB);
+      }
 #pragma unroll
       for (int s = 0; s < kNS; ++s) {
-        const bf16x8 a = ka, v = va;
-        if (s + 1 < kNS) {
-          ka = *reinterpret_cast<const bf16x8*>(kb + off.krow[s + 1] + c * 32 * kRowB);
-          va = *reinterpret_cast<const bf16x8*>(vb + off.vrow[s + 1] + c * 32 * kRowB);
+        const bf16x8 a = ka[s % kAhead], v = va[s % kAhead];
+        if (s + kAhead < kNS) {
+          ka[s % kAhead] =
+              *reinterpret_cast<const bf16x8*>(kb + off.krow[s + kAhead] + c * 32 * kRowB);
+          va[s % kAhead] =
+              *reinterpret_cast<const bf16x8*>(vb + off.vrow[s + kAhead] + c * 32 * kRowB);
         }
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st, 0, 0, 0);
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, df[s], dpt, 0, 0, 0);
       }
+      pin_reads_ahead<kNS, kAhead, 2, 2>();
       // lane: row q, keys k0 + 32 c + 16 sb + 8 hh + e for value 8 sb + e
       float ds[16];
 #pragma unroll
@@ -403,21 +413,28 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
         }
       }
       const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+      // K^T operand i = (d chunk i / 2, 16 keys i % 2), kTrAhead ahead
+      auto kop = [&](int i) {
+        const int rows = (32 * c + 16 * (i % 2)) * kRowB;
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc0[i / 2] + rows));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc1[i / 2] + rows));
+        return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                       __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      constexpr int NQ = 2 * kNDC;
+      bf16x8 kq[kTrAhead];
 #pragma unroll
-      for (int dc = 0; dc < kNDC; ++dc) {
+      for (int j = 0; j < kTrAhead; ++j) kq[j] = kop(j);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int rows = (32 * c + 16 * j) * kRowB;
-          const i16x4 lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc0[dc] + rows));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + off.kc1[dc] + rows));
-          const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
-                                                   __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3,
-                                                   4, 5, 6, 7);
-          dq[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j ? d1 : d0, dq[dc], 0, 0, 0);
-        }
+      for (int i = 0; i < NQ; ++i) {
+        const bf16x8 a = kq[i % kTrAhead];
+        if (i + kTrAhead < NQ) kq[i % kTrAhead] = kop(i + kTrAhead);
+        dq[i / 2] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, (i % 2) ? d1 : d0, dq[i / 2], 0, 0, 0);
       }
+      pin_reads_ahead<NQ, kTrAhead, 2, 1>();
     }
     kt_cur = kt_nxt;
     full_cur = full_nxt;
@@ -645,21 +662,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     for (int rb = 0; rb < kTile / 32; ++rb) {
       const int rbo = rb * 32 * kRowB;
       f32x16 s = f32x16{}, dp = f32x16{};
-      // row operands one d-step ahead
-      bf16x8 qa = ld8(tq + off.qrow[0] + rbo), da = ld8(tdo + off.drow[0] + rbo);
+      // row operands kAhead d-steps ahead
+      bf16x8 qa[kAhead], da[kAhead];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) {
+        qa[j] = ld8(tq + off.qrow[j] + rbo);
+        da[j] = ld8(tdo + off.drow[j] + rbo);
+      }
 #pragma unroll
       for (int ds_ = 0; ds_ < kNS; ++ds_) {
-        const bf16x8 a = qa, d = da;
-        if (ds_ + 1 < kNS) {
-          qa = ld8(tq + off.qrow[ds_ + 1] + rbo);
-          da = ld8(tdo + off.drow[ds_ + 1] + rbo);
+        const bf16x8 a = qa[ds_ % kAhead], d = da[ds_ % kAhead];
+        if (ds_ + kAhead < kNS) {
+          qa[ds_ % kAhead] = ld8(tq + off.qrow[ds_ + kAhead] + rbo);
+          da[ds_ % kAhead] = ld8(tdo + off.drow[ds_ + kAhead] + rbo);
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ds_], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d, vf[ds_], dp, 0, 0, 0);
       }
+      pin_reads_ahead<kNS, kAhead, 2, 2>();
       // the first transposed operands load while P and dS are computed
-      bf16x8 dca = tr8(tdo + off.dc0[0] + rbo, tdo + off.dc0[0] + rbo + 4 * kRowB);
-      bf16x8 qca = tr8(tq + off.qc0[0] + rbo, tq + off.qc1[0] + rbo);
+      // (operand i = (d chunk i / 2, 16 rows i % 2))
+      auto dop = [&](int i) {
+        const int o = rbo + 16 * (i % 2) * kRowB;
+        return tr8(tdo + off.dc0[i / 2] + o, tdo + off.dc0[i / 2] + o + 4 * kRowB);
+      };
+      auto qop = [&](int i) {
+        const int o = rbo + 16 * (i % 2) * kRowB;
+        return tr8(tq + off.qc0[i / 2] + o, tq + off.qc1[i / 2] + o);
+      };
+      bf16x8 dca[kTrAhead], qca[kTrAhead];
+#pragma unroll
+      for (int j = 0; j < kTrAhead; ++j) {
+        dca[j] = dop(j);
+        qca[j] = qop(j);
+      }
       // lane: key, rows rb*32 + 16 st + 8 hh + e for value u = 8 st + e
       float pv[16], dsv[16];
 #pragma unroll
@@ -692,20 +728,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
       }
       const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
       const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
-      // dV^T += dO^T P and dK^T += Q^T dS: operand i = (dc, half j), one ahead
+      // dV^T += dO^T P and dK^T += Q^T dS: operand i = (dc, half j), kTrAhead ahead
+      constexpr int NT = 2 * kNDC;
 #pragma unroll
-      for (int i = 0; i < 2 * kNDC; ++i) {
+      for (int i = 0; i < NT; ++i) {
         const int dc = i / 2, j = i % 2;
-        const bf16x8 a = dca, qb = qca;
-        if (i + 1 < 2 * kNDC) {
-          const int dn = (i + 1) / 2, jn = (i + 1) % 2;
-          const int o = rbo + 16 * jn * kRowB;
-          dca = tr8(tdo + off.dc0[dn] + o, tdo + off.dc0[dn] + o + 4 * kRowB);
-          qca = tr8(tq + off.qc0[dn] + o, tq + off.qc1[dn] + o);
+        const bf16x8 a = dca[i % kTrAhead], qb = qca[i % kTrAhead];
+        if (i + kTrAhead < NT) {
+          dca[i % kTrAhead] = dop(i + kTrAhead);
+          qca[i % kTrAhead] = qop(i + kTrAhead);
         }
         dv[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, j ? p1 : p0, dv[dc], 0, 0, 0);
         dk[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, j ? s1 : s0, dk[dc], 0, 0, 0);
       }
+      pin_reads_ahead<NT, kTrAhead, 4, 2>();
     }
     pos = npos;
     cls = ncls;

@@ -139,6 +139,20 @@ struct Loader {
   }
 };
 
+// Scheduling hint for an unrolled MFMA loop of N steps, each issuing M MFMAs
+// and R LDS reads for the step A ahead (A steps' reads issued up front): keeps
+// the reads A steps ahead of their MFMAs. Left alone, the scheduler moves each
+// read next to its MFMA and the wave waits out the LDS latency there.
+template <int N, int A, int R, int M, int SYNC = 0>
+__device__ inline void pin_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, A * R, SYNC);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, SYNC);
+    if (i + A < N) __builtin_amdgcn_sched_group_barrier(0x100, R, SYNC);
+  }
+}
+
 // Workgroup barrier without a memory fence: LDS-DMA completion is awaited
 // explicitly with wait_vmcnt, and a fence would wait for the prefetch as well.
 __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
