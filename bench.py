@@ -50,8 +50,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "b31a935b41693d68",
-                "fetch_kib": 86600.7, "write_kib": 65536.0,
+                "sha256_16": "803743d085e86c7c",
+                "fetch_kib": 86583.3, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 

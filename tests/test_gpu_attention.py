@@ -317,3 +317,27 @@ def test_staged_mask_bias_rows(D, mshape, bshape):
         # carries a relative error of at most 2^-9, so the LSEs may differ by
         # up to 2 * 2^-9
         assert (lse[fin] - lse1[fin]).abs().max().item() <= 2 * 2.0 ** -9
+
+
+def test_two_head_tile_list_lengths():
+    """Query tiles that visit 0, 1, 2, 3, 6 and 6 key tiles (full, partial and
+    past Sk mixed) in the two-head kernel: the loop reads each next tile index
+    ahead of its use, and odd / even counts end on different slots."""
+    B, Sq, Sk, H, KVH, D = 1, 768, 677, 4, 2, 128
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=31))
+    m = np.zeros((1, 1, Sq, 768), bool)
+    m[0, 0, 128:256, 256:384] = True                    # one full tile
+    m[0, 0, 256:384, 0:128] = True                      # a full and a partial tile
+    m[0, 0, 256:384, 600] = True
+    m[0, 0, 384:512, 128:256] = True                    # two full, one past Sk
+    m[0, 0, 384:512, 384:512] = True
+    m[0, 0, 384:512, 640:677] = True
+    m[0, 0, 512:640:2, :] = True                        # every tile partial
+    m[0, 0, 640:768, :677] = True                       # every tile kept
+    mask = torch.from_numpy(m).cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    n = bm.kv_num_blocks.cpu().numpy().ravel() + bm.full_kv_num_blocks.cpu().numpy().ravel()
+    assert list(n) == [0, 1, 2, 3, 6, 6], n
+    o, lse = _run_and_check(q, k, v, "bf16", mask=mask, bm=bm, what="tile list lengths")
+    assert (o[0, :128].float() == 0).all()
+    assert torch.isneginf(lse[0, :, :128]).all()
