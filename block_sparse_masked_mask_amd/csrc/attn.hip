@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include "attn_common.h"
+#include "attn_pipe.h"
 #include "bsm_internal.h"
 #include "dflash_rows.h"
 
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
           sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[c], 0, 0, 0);
         }
       }
+      pipe::pin_reads_ahead<2 * NS, 3, 1, 1>();
 
       // scale, bias, mask; row max over this half
       float mloc = -INFINITY;
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
           }
         }
       }
+      pipe::pin_reads_ahead<4 * NDC, 3, 1, 1>();
     }
   }
 
