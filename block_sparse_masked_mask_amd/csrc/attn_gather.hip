@@ -75,23 +75,15 @@ struct GatherLoader {
   // Offsets at or past 2^31 exceed the resource's range (Sk rows, < 2^31
   // bytes), so such chunks load as zeros.
   __device__ inline void issue(Tiles<D>& t, const int (&key)[C::LOADS], int w) const {
+    w = __builtin_amdgcn_readfirstlane(w);  // keeps the LDS destinations scalar
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
       const int slot = (j * C::NW + w) * 64;
-      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(t.k + slot * 8);
-      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(t.v + slot * 8);
       const bool in = (uint32_t)key[j] < nkeys;
       const uint32_t ok = in ? (uint32_t)key[j] * krow + kc[j] : 0x80000000u;
       const uint32_t ov = in ? (uint32_t)key[j] * vrow + vc[j] : 0x80000000u;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-          "s_mov_b32 m0, %3\n\t"
-          "buffer_load_dwordx4 %4, %5, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(lk)), "v"(ok), "s"(kr),
-            "s"(__builtin_amdgcn_readfirstlane(lv)), "v"(ov), "s"(vr)
-          : "memory");
+      dma16(kr, reinterpret_cast<char*>(t.k + slot * 8), ok);
+      dma16(vr, reinterpret_cast<char*>(t.v + slot * 8), ov);
     }
   }
 };

@@ -44,6 +44,18 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// One 16-byte LDS-DMA load per lane: the global bytes at buffer offset
+// voff + soff go to LDS at lds + 16 * lane (lds must be wave-uniform; the
+// compiler puts it in m0). Offsets past the resource's range load zeros.
+// Completion is awaited explicitly with wait_vmcnt before the barrier that
+// publishes a buffer. The compiler also waits for all outstanding LDS-DMA
+// loads (vmcnt(0)) before each transposing LDS read, since it cannot tell the
+// buffers apart; in these kernels the next tile's load has landed by then.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                             uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
 template <int D>
 struct Tiles {
   __bf16 k[kTile * D];
@@ -92,49 +104,53 @@ struct Loader {
     }
   }
 
-  // The loads are written as inline asm so that the compiler does not treat
-  // them as LDS stores it must wait for before every LDS read (it cannot tell
-  // the two buffers apart); completion is awaited explicitly with wait_vmcnt
-  // before the barrier that publishes a buffer. The instruction has no
-  // destination register: data goes to LDS at m0 + 16 * lane.
-  __device__ inline void issue(Tiles<D>& t, int kt, int w) const { issue(t.k, t.v, kt, w); }
-  // the same with the LDS byte addresses of the K and V tiles given as
-  // workgroup-uniform integers (w uniform too), so that every destination
-  // address is scalar arithmetic
-  __device__ inline void issue_at(uint32_t lk0, uint32_t lv0, int kt, int w) const {
+  // K and V tile kt into the LDS bytes at lk0 and lv0 (workgroup-uniform
+  // addresses; w uniform too, so every destination address is scalar)
+  __device__ inline void issue_at(char* lk0, char* lv0, int kt, int w) const {
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
-      const uint32_t slot = (uint32_t)((j * C::NW + w) * 64 * 16);
-      const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
-      const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-          "s_mov_b32 m0, %3\n\t"
-          "buffer_load_dwordx4 %4, %5, 0 offen lds"
-          :
-          : "s"(lk0 + slot), "v"(ok), "s"(kr), "s"(lv0 + slot), "v"(ov), "s"(vr)
-          : "memory");
+      const int slot = (j * C::NW + w) * 64 * 16;
+      dma16(kr, lk0 + slot, koff[j] + (uint32_t)kt * ktile_bytes);
+      dma16(vr, lv0 + slot, voff[j] + (uint32_t)kt * vtile_bytes);
     }
   }
+  __device__ inline void issue(Tiles<D>& t, int kt, int w) const { issue(t.k, t.v, kt, w); }
   // the same into separate K and V tiles of LDS (kTile * D elements each)
   __device__ inline void issue(__bf16* tk, __bf16* tv, int kt, int w) const {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    issue_at(reinterpret_cast<char*>(tk), reinterpret_cast<char*>(tv), kt, wu);
+  }
+};
+
+// Per-lane byte offsets of the LDS operand reads of the bf16 MFMA kernels,
+// computed once: the K operand of d-step s in key chunk 0 (chunk c adds 32
+// rows), and the first transposed V read of d-chunk dc at key 0 (the key step
+// adds rows). K rows are permuted by perm_row so that a lane's S^T values are
+// 8 consecutive keys per 16-key step, the B-operand layout of the PV product.
+// The swizzles depend only on a row's low bits, which the added rows leave
+// alone. vbase: byte offset of the V tiles from the K tiles, folded in so that
+// per-read immediates stay small.
+template <int D>
+struct LaneOffs {
+  uint32_t k[D / 16];
+  uint32_t v[D / 32];
+  __device__ inline void init(int lane, uint32_t vbase) {
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+    const int row = perm_row(n);
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-      const int slot = (j * C::NW + w) * 64;  // first 16-byte slot of the wave
-      const uint32_t lk = (uint32_t)(uintptr_t)(lds_void*)(tk + slot * 8);
-      const uint32_t lv = (uint32_t)(uintptr_t)(lds_void*)(tv + slot * 8);
-      const uint32_t ok = koff[j] + (uint32_t)kt * ktile_bytes;
-      const uint32_t ov = voff[j] + (uint32_t)kt * vtile_bytes;
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-          "s_mov_b32 m0, %3\n\t"
-          "buffer_load_dwordx4 %4, %5, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(lk)), "v"(ok), "s"(kr),
-            "s"(__builtin_amdgcn_readfirstlane(lv)), "v"(ov), "s"(vr)
-          : "memory");
+    for (int s = 0; s < D / 16; ++s)
+      k[s] = (uint32_t)((row * D + (((2 * s + hh) ^ swz_k<D>(row)) * 8)) * 2);
+    // transposed reads: in each 16-lane group, lane 4e + g reads 4 d-values of
+    // key row e (and e + 4 for the second read)
+    const int blk = lane >> 4;
+    const int e4 = (lane >> 2) & 3;
+    const int g4 = lane & 3;
+    const int row0 = 8 * (blk >> 1) + e4;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
+      v[dc] = vbase + (uint32_t)((row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4) * 2);
     }
   }
 };

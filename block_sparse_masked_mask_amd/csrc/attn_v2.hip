@@ -58,36 +58,6 @@ struct RowBlock {
   bool qvalid;
 };
 
-// Per-lane byte offsets of the LDS operand reads, computed once: the K operand
-// of d-step s in key chunk 0 (chunk c adds 32 rows), and the first transposed
-// V read of d-chunk dc at key 0 (the key step adds rows). The swizzles depend
-// only on a row's low bits, which the added rows leave alone.
-template <int D>
-struct LaneOffs {
-  uint32_t k[D / 16];
-  uint32_t v[D / 32];
-  __device__ inline void init(int lane) {
-    const int n = lane & 31;
-    const int hh = lane >> 5;
-    const int row = perm_row(n);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      k[s] = (uint32_t)((row * D + (((2 * s + hh) ^ swz_k<D>(row)) * 8)) * 2);
-    // transposed reads: in each 16-lane group, lane 4e + g reads 4 d-values of
-    // key row e (and e + 4 for the second read)
-    const int blk = lane >> 4;
-    const int e4 = (lane >> 2) & 3;
-    const int g4 = lane & 3;
-    const int row0 = 8 * (blk >> 1) + e4;
-#pragma unroll
-    for (int dc = 0; dc < D / 32; ++dc) {
-      const int chunk = 4 * dc + 2 * (blk & 1) + (g4 >> 1);
-      v[dc] = (uint32_t)(2 * kTile * D * 2 +
-                         (row0 * D + ((chunk ^ swz_v<D>(row0)) * 8) + (g4 & 1) * 4) * 2);
-    }
-  }
-};
-
 // One key tile: S^T of all four 32-key chunks, one max (and at most one
 // rescale) per row, then the probabilities and PV of the first 64 keys, with
 // the second half's exponentials issued between the first half's PV MFMAs.
@@ -516,10 +486,9 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   // K tiles (slots 0, 1), then V tiles (slots 0, 1)
   constexpr int TB = kTile * D * 2;
   __shared__ __align__(1024) char s_kv[4 * TB];
-  // LDS byte addresses of the K and V slots
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)s_kv;
-  auto kslot = [&](int sl) { return lds0 + (uint32_t)(sl * TB); };
-  auto vslot = [&](int sl) { return lds0 + (uint32_t)((2 + sl) * TB); };
+  // the K and V slots
+  auto kslot = [&](int sl) { return s_kv + sl * TB; };
+  auto vslot = [&](int sl) { return s_kv + (2 + sl) * TB; };
   __shared__ __align__(16) float s_cb[2][2][kTile];  // staged rows: buffer, head of the pair
 
   // Work items: (head-pair group, query tile). Workgroup L runs on XCD L % 8.
@@ -605,7 +574,7 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
   const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb +
                         seq.k0 * p.v_sk + (int64_t)kvh * p.v_sh;
   LaneOffs<D> off;
-  off.init(lane);
+  off.init(lane, 2 * TB);
   Loader<D, RB> ld;
   ld.init(kbase, vbase, p.k_sk, p.v_sk, seq.Sk, w, lane);
 
@@ -621,16 +590,8 @@ __global__ __launch_bounds__(512 / RB, 1) void k_attn_bf16_v2(AttnParams p, int 
     cboff = (uint32_t)(hc * p.cb_sh * 4 + (lane & 31) * 16);
   }
   auto issue_cb = [&](int slot, int kt) {
-    if (MODE == 2 && w == 0) {
-      const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)(&s_cb[slot][0][0]);
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(cboff + (uint32_t)kt * (kTile * 4)),
-            "s"(cbr)
-          : "memory");
-    }
+    if (MODE == 2 && w == 0)
+      dma16(cbr, reinterpret_cast<char*>(&s_cb[slot][0][0]), cboff + (uint32_t)kt * (kTile * 4));
   };
 
   TileList tl;
