@@ -54,7 +54,6 @@ def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
     stored values; mask: None, a DFlashGeom, or a bool (Bm, Hm, Qm, K>=Sk)
     array; bias: None or a float (Bb, Hb, Qb, K>=Sk) array.
     """
-    q = np.asarray(q, np.float64)
     B, Sq, H, D = q.shape
     Sk, KVH = k.shape[1], k.shape[2]
     G = H // KVH
@@ -63,7 +62,7 @@ def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
         scale = 1.0 / math.sqrt(D)
     Kh = np.asarray(k[b, :, h // G, :], np.float64)
     Vh = np.asarray(v[b, :, h // G, :], np.float64)
-    Q = q[b, rows, h, :]
+    Q = np.asarray(q[b, rows, h, :], np.float64)
     s = scale * (Q @ Kh.T)
     if bias is not None:
         s = s + _aux_rows(np.asarray(bias, np.float64), b, h, rows, H, KVH)[:, :Sk]
@@ -73,18 +72,17 @@ def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
         kept = dflash_dense_mask(mask, rows)[:, :Sk]
     else:
         kept = np.asarray(_aux_rows(np.asarray(mask, bool), b, h, rows, H, KVH)[:, :Sk])
+    # every requested row at once: a masked position takes score -inf, so its
+    # exp is 0 and it drops out of the max, the sum and the weighted sum of V
+    s = np.where(kept, s, -np.inf)
+    has = kept.any(axis=1)
+    m = np.where(has, s.max(axis=1), 0.0)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
     O = np.zeros((len(rows), D))
     lse = np.full(len(rows), -np.inf)
-    for r in range(len(rows)):
-        sel = kept[r]
-        if not sel.any():
-            continue
-        sr = s[r, sel]
-        m = sr.max()
-        p = np.exp(sr - m)
-        l = p.sum()
-        O[r] = (p @ Vh[sel]) / l
-        lse[r] = m + math.log(l)
+    O[has] = (p[has] @ Vh) / l[has, None]
+    lse[has] = m[has] + np.log(l[has])
     return O, lse
 
 
