@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
             const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+              bv[e] = bias_log2(bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))));
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) bv[e] = 0.f;
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         acc += __shfl_xor(acc, 2, 64);
         const int64_t key = k0 + j;
         float sc = acc * p.scale_log2;
-        if (brow && key < seq.Sk) sc += brow[key] * kLog2e;
+        if (brow && key < seq.Sk) sc += bias_log2(brow[key]);
         bool keep = qvalid && key < seq.Sk;
         if (keep && check_mask) {
           if (p.mask_kind == 2)

@@ -94,8 +94,8 @@ __device__ inline int tile_class(const AttnParams& f, int b, int h, int qt, int 
 __device__ inline float bias_at(const AttnParams& f, int b, int h, int q, int64_t j, bool bf16) {
   if (!f.has_bias) return 0.f;
   const uint8_t* row = aux_row(f.bias, bf16 ? 2 : 4, b, h, f.G, q);
-  return bf16 ? ld_elem(reinterpret_cast<const uint16_t*>(row), j)
-              : ld_elem(reinterpret_cast<const float*>(row), j);
+  return bias_nat(bf16 ? ld_elem(reinterpret_cast<const uint16_t*>(row), j)
+                       : ld_elem(reinterpret_cast<const float*>(row), j));
 }
 
 template <typename T, int D>

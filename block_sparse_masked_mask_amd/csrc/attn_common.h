@@ -13,6 +13,22 @@
 
 namespace bsm {
 
+// An additive bias in the log2 units the kernels' softmax works in, finite
+// values saturated at the largest finite float: a bias beyond
+// +-FLT_MAX / log2(e) (~2.36e38; the finfo(bf16 / f32).min pre-mask sentinel
+// of flash-sparse-attention PR #197, Changes, is one) scores as that bound, so
+// a kept key carrying it stays kept and keys that all carry it weigh the
+// same. A bias of -inf stays -inf: that key contributes nothing.
+__device__ inline float bias_log2(float b) {
+  const float x = fminf(fmaxf(b * 1.4426950408889634f, -3.402823466e38f), 3.402823466e38f);
+  return b == -INFINITY ? b : x;
+}
+// the same saturation in natural units (the backward's scores)
+__device__ inline float bias_nat(float b) {
+  const float x = fminf(fmaxf(b, -2.3586575e38f), 2.3586575e38f);
+  return b == -INFINITY ? b : x;
+}
+
 __device__ inline int64_t head_index(int mode, int h, int G) {
   return mode == 0 ? 0 : (mode == 1 ? h : h / G);
 }

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void k_attn_gather(AttnParams p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int u = 8 * sb + e;
-        const float bv = bf16_to_f32(ga_cur.bias[u]) * kLog2e;
+        const float bv = bias_log2(bf16_to_f32(ga_cur.bias[u]));
         float sv = fmaf(sc[u], p.scale_log2, bv);
         sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
         sc[u] = sv;

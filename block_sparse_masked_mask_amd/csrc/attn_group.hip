@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * kGWaves * (SPLIT ? 2 : 1), 1) void k_attn_grou
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
-          const float bv = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+          const float bv = bias_log2(bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))));
           float sv = fmaf(sc[rb][u], p.scale_log2, bv);
           sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
           sc[rb][u] = sv;

@@ -179,7 +179,7 @@ __device__ inline void compute_tile(const char* lds, int slot_rt, const AttnPara
             const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+              bv[e] = bias_log2(bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))));
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) bv[e] = 0.f;
@@ -391,7 +391,7 @@ __device__ inline void compute_tile_halves(const char* lds, int slot_rt, const A
               const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                bv[e] = bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))) * kLog2e;
+                bv[e] = bias_log2(bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))));
             } else {
 #pragma unroll
               for (int e = 0; e < 8; ++e) bv[e] = 0.f;
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void k_aux_combine(AttnParams p, float* cb, in
     for (int e = 0; e < 4; ++e) {
       const int k = k0 + e;
       const bool keep = k < p.Sk && (mrow == nullptr || mrow[k] != 0);
-      o[e] = keep ? (brow ? bf16_to_f32(brow[k]) * kLog2e : 0.f) : -INFINITY;
+      o[e] = keep ? (brow ? bias_log2(bf16_to_f32(brow[k])) : 0.f) : -INFINITY;
     }
     *reinterpret_cast<float4*>(cb + r * ((int64_t)p.nK * kTile) + k0) =
         make_float4(o[0], o[1], o[2], o[3]);

@@ -29,6 +29,24 @@ import numpy as np
 from .dflash import DFlashGeom, dflash_dense_mask
 
 
+# Readings where the pages leave huge and infinite biases open:
+#   * a finite bias beyond +-BIAS_BOUND = FLT_MAX / log2(e) (~2.36e38) counts
+#     as +-BIAS_BOUND: the bias is taken in log2 units (bias * log2 e) and
+#     saturated at the largest finite float32 there. A kept key carrying the
+#     pre-mask sentinel finfo(bf16 / f32).min ([FSA-197] Changes) therefore
+#     stays kept, and keys that all carry it weigh the same;
+#   * a bias of -inf stays -inf: that key contributes nothing, and a row whose
+#     kept keys all score -inf is treated as a fully masked row.
+_F32_MAX = (2.0 - 2.0 ** -23) * 2.0 ** 127
+BIAS_BOUND = _F32_MAX / math.log2(math.e)
+
+
+def saturate_bias(x):
+    """Finite values clipped to [-BIAS_BOUND, BIAS_BOUND]; -inf kept."""
+    x = np.asarray(x, np.float64)
+    return np.where(np.isneginf(x), x, np.clip(x, -BIAS_BOUND, BIAS_BOUND))
+
+
 def _aux_rows(t, b, h, rows, H, KVH):
     """Rows of a broadcastable 4D aux tensor for (b, h, rows)."""
     Bt, Ht, Qt, _ = t.shape
@@ -65,7 +83,7 @@ def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
     Q = np.asarray(q[b, rows, h, :], np.float64)
     s = scale * (Q @ Kh.T)
     if bias is not None:
-        s = s + _aux_rows(np.asarray(bias, np.float64), b, h, rows, H, KVH)[:, :Sk]
+        s = s + saturate_bias(_aux_rows(bias, b, h, rows, H, KVH)[:, :Sk])
     if mask is None:
         kept = np.ones(s.shape, bool)
     elif isinstance(mask, DFlashGeom):
@@ -75,7 +93,7 @@ def attention_rows(q, k, v, b, h, rows, scale=None, mask=None, bias=None):
     # every requested row at once: a masked position takes score -inf, so its
     # exp is 0 and it drops out of the max, the sum and the weighted sum of V
     s = np.where(kept, s, -np.inf)
-    has = kept.any(axis=1)
+    has = (s > -np.inf).any(axis=1)
     m = np.where(has, s.max(axis=1), 0.0)
     p = np.exp(s - m[:, None])
     l = p.sum(axis=1)

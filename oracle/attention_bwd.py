@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-from .attention import _aux_rows
+from .attention import _aux_rows, saturate_bias
 from .dflash import DFlashGeom, dflash_dense_mask
 
 
@@ -45,7 +45,7 @@ def head_grads(q, k, v, dout, b, h, scale=None, mask=None, bias=None):
     dO = np.asarray(dout[b, :, h, :], np.float64)
     s = scale * (Q @ K.T)
     if bias is not None:
-        s = s + _aux_rows(np.asarray(bias, np.float64), b, h, rows, H, KVH)[:, :Sk]
+        s = s + saturate_bias(_aux_rows(bias, b, h, rows, H, KVH)[:, :Sk])
     if mask is None:
         kept = np.ones(s.shape, bool)
     elif isinstance(mask, DFlashGeom):
@@ -54,7 +54,7 @@ def head_grads(q, k, v, dout, b, h, scale=None, mask=None, bias=None):
         kept = np.asarray(_aux_rows(np.asarray(mask, bool), b, h, rows, H, KVH)[:, :Sk])
     P = np.zeros((Sq, Sk))
     for r in range(Sq):
-        sel = kept[r]
+        sel = kept[r] & (s[r] > -np.inf)
         if not sel.any():
             continue
         sr = s[r, sel]

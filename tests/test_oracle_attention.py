@@ -138,3 +138,57 @@ def test_rows_subset_matches_full():
     np.testing.assert_array_equal(Or, O[1, [3, 17, 29], 1])
     np.testing.assert_array_equal(lr, lse[1, 1, [3, 17, 29]])
     assert math.isclose(1 / math.sqrt(8), 0.3535533905932738)
+
+
+# ---------------------------------------------------------------------------
+# Huge and infinite biases (readings: finite biases saturate at
+# +-FLT_MAX / log2 e, -inf stays -inf and drops the key)
+
+BF16_MIN = -(2.0 - 2.0 ** -7) * 2.0 ** 127   # finfo(bf16).min, from the format
+
+
+def _one_row(bias_row, kept_row, seed=3):
+    Sk = len(bias_row)
+    q, k, v = _qkv(1, 1, Sk, 1, 1, 8, seed)
+    K = 128 * ((Sk + 127) // 128)
+    bias = np.zeros((1, 1, 1, K))
+    bias[0, 0, 0, :Sk] = bias_row
+    mask = np.zeros((1, 1, 1, K), bool)
+    mask[0, 0, 0, :Sk] = kept_row
+    O, L = attention_rows(q, k, v, 0, 0, [0], mask=mask, bias=bias)
+    return O[0], L[0], v[0, :, 0, :]
+
+
+def test_sentinel_on_every_kept_key_weighs_them_equally():
+    """Every kept key carries finfo(bf16).min: the scores all equal -BIAS_BOUND
+    (the dot products vanish beside it), so O is the plain mean of their V rows
+    and LSE = -BIAS_BOUND (log of the key count vanishes too)."""
+    from oracle.attention import BIAS_BOUND
+    kept = np.array([1, 0, 1, 1, 0, 1], bool)
+    O, L, V = _one_row(np.full(6, BF16_MIN), kept)
+    np.testing.assert_allclose(O, V[kept].mean(axis=0), rtol=0, atol=1e-12)
+    assert L == -BIAS_BOUND
+
+
+def test_sentinel_beside_an_ordinary_key_weighs_nothing():
+    O, L, V = _one_row(np.array([BF16_MIN, 0.25, BF16_MIN]), np.ones(3, bool))
+    np.testing.assert_allclose(O, V[1], rtol=0, atol=1e-12)
+
+
+def test_values_beyond_the_bound_saturate_to_one_score():
+    """-3e38 and -2.4e38 are both beyond FLT_MAX / log2 e: equal weights;
+    -2e38 and -1e38 are not: the larger wins outright."""
+    O, _, V = _one_row(np.array([-3.0e38, -2.4e38]), np.ones(2, bool))
+    np.testing.assert_allclose(O, V.mean(axis=0), rtol=0, atol=1e-12)
+    O, _, V = _one_row(np.array([-2.0e38, -1.0e38]), np.ones(2, bool))
+    np.testing.assert_allclose(O, V[1], rtol=0, atol=1e-12)
+
+
+def test_minus_inf_bias_drops_the_key():
+    bias = np.array([0.5, -np.inf, -1.0, 0.0])
+    O, L, _ = _one_row(bias, np.ones(4, bool))
+    O2, L2, _ = _one_row(np.where(np.isinf(bias), 0.0, bias), np.array([1, 0, 1, 1], bool))
+    np.testing.assert_allclose(O, O2, rtol=0, atol=1e-14)
+    assert abs(L - L2) < 1e-14
+    O, L, _ = _one_row(np.full(3, -np.inf), np.ones(3, bool))
+    assert (O == 0).all() and L == -np.inf
