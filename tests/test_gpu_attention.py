@@ -8,8 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows,
-                         sample_rows, say, synth)
+from gpu_helpers import assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows, say, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -141,63 +140,19 @@ def test_deterministic():
     assert torch.equal(o1, o2)
 
 
-# ---------------------------------------------------------------------------
-# full-size workloads, sampled rows
+# The workloads at full size are compared in test_gpu_fullsize.py.
 
 
-def _dflash_full(name, layer, rows_per_head=24, heads=(0, 5, 31)):
-    cfg = synth.CONFIGS[name]
-    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
-                   is_causal=layer["is_causal"], layer_type=layer["layer_type"],
-                   sliding_window=layer["window"])
-    q, k, v = cuda(*synth.qkv(cfg["B"], d.Sq, d.Sk, cfg["H"], cfg["KVH"], cfg["D"], cfg["dtype"],
-                              seed=0, scale=cfg["qkv_scale"]))
+@pytest.mark.parametrize("layer", ["full", "sliding"])
+def test_xcd_grouped_work_mapping(layer):
+    """B * KVH * G / 2 = 8 head-pair groups: the two-head kernel's mapping that
+    gives each XCD whole groups (the training and long-context shapes take it
+    too), on every row."""
+    kw = dict(layer_type="sliding", sliding_window=300) if layer == "sliding" else {}
+    d = bsm.DFlash(512, 32, 16, **kw)
+    q, k, v = cuda(*synth.qkv(2, d.Sq, d.Sk, 8, 4, 128, "bf16", seed=40))
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
-    rows = sample_rows(d.Sq, rows_per_head, seed=1)
-    _run_and_check(q, k, v, cfg["dtype"], pred=d, bm=bm, rows=rows, heads=heads,
-                   what=f"{name}/{layer['name']}")
-
-
-@pytest.mark.parametrize("layer", synth.CONFIGS["dflash_train_bf16"]["layers"],
-                         ids=lambda l: l["name"])
-def test_dflash_train_full_size(layer):
-    _dflash_full("dflash_train_bf16", layer)
-
-
-def test_long_dflash_full_size():
-    _dflash_full("long_dflash_bf16", synth.CONFIGS["long_dflash_bf16"]["layers"][0],
-                 rows_per_head=12, heads=(0, 31))
-
-
-def test_dynamic_topk_attention_full_size():
-    cfg = synth.CONFIGS["dynamic_topk_bf16"]
-    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
-    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0))
-    bias, pad2d = synth.topk_inputs(cfg, seed=0)
-    bias, pad2d = bias.cuda(), pad2d.cuda()
-    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
-    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
-    rows = sample_rows(Sq, 16, seed=2)
-    _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, rows=rows, heads=(0, 7, 15),
-                   what="dynamic top-k")
-
-
-def test_decode_full_size():
-    cfg = synth.CONFIGS["decode_swap_bf16"]
-    B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
-    q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0))
-    bias, _ = synth.topk_inputs(cfg, seed=0)
-    bias = bias.cuda()
-    mask = bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"])
-    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
-    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm, return_lse=True)
-    torch.cuda.synchronize()
-    say("decode full size: comparing sampled (b, h)")
-    for b in (0, 17, 63):
-        for h in (0, 13, 31):
-            want_o, want_l = oracle_rows(q, k, v, b, h, [0], mask=mask, bias=bias)
-            assert_close(o[b, 0, h].float().cpu().numpy()[None], want_o, "bf16", f"O b={b} h={h}")
-            assert_close(lse[b, h].cpu().numpy(), want_l, "bf16", f"LSE b={b} h={h}")
+    _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what=f"xcd groups {layer}")
 
 
 @pytest.mark.parametrize("Sq", [1, 7, 20, 32])
@@ -341,3 +296,62 @@ def test_two_head_tile_list_lengths():
     o, lse = _run_and_check(q, k, v, "bf16", mask=mask, bm=bm, what="tile list lengths")
     assert (o[0, :128].float() == 0).all()
     assert torch.isneginf(lse[0, :, :128]).all()
+
+
+# ---------------------------------------------------------------------------
+# huge and infinite biases: finite values saturate at +-FLT_MAX / log2 e in
+# the kernels' log2 units (a kept key carrying the pre-mask sentinel
+# finfo.min stays kept), -inf drops the key
+
+BF16_MIN = -(2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def _extreme_bias(shape, seed):
+    """A normal bias whose rows (by head and query) are, in turn: every key at
+    the sentinel, the sentinel beside five ordinary keys, values beyond the
+    bound (-3e38 and -2.4e38), a -inf on every third key, or left as drawn."""
+    b = synth.normal(shape, seed, synth.TID_BIAS).astype(np.float64)
+    for hb in range(shape[1]):
+        for row in range(shape[2]):
+            kind = (hb + row) % 5
+            r = b[:, hb, row]
+            if kind == 0:
+                r[:] = BF16_MIN
+            elif kind == 1:
+                r[:] = BF16_MIN
+                r[:, :5] = 0.5
+            elif kind == 2:
+                r[:, 0::2] = -3.0e38
+                r[:, 1::2] = -2.4e38
+            elif kind == 3:
+                r[:, ::3] = -np.inf
+    return b
+
+
+@pytest.mark.parametrize("dt,Sq,bq", [("bf16", 300, True), ("bf16", 300, False),
+                                      ("bf16", 20, True), ("f32", 300, True)])
+def test_huge_and_infinite_biases(dt, Sq, bq):
+    B, Sk, H, KVH, D = 2, 600, 4, 2, 128
+    K = 640
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, dt, seed=50))
+    # a query-broadcast bias comes with a query-broadcast mask (the staged rows)
+    m = synth.random_bool((B, 1, Sq if bq else 1, K), 0.6, 50, synth.TID_MASK)
+    m[..., :5] = True
+    mask = torch.from_numpy(m).cuda()
+    shape = (B, H, Sq, K) if bq else (B, KVH, 1, K)
+    bias_np = _extreme_bias(shape, 50)
+    bias = torch.from_numpy(bias_np).to(torch.bfloat16 if dt == "bf16" else torch.float32).cuda()
+    say("extreme biases", dt, Sq, shape)
+    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            want_o, want_l = oracle_rows(q, k, v, b, h, np.arange(Sq), mask=mask, bias=bias)
+            assert_close(o[b, :, h], want_o, dt, f"extreme O b={b} h={h}")
+            huge = np.abs(want_l) > 1e30
+            assert np.array_equal(np.isneginf(lse[b, h]), np.isneginf(want_l))
+            rel = np.abs(lse[b, h][huge] - want_l[huge]) / np.abs(want_l[huge])
+            assert (rel <= 1e-6).all(), f"LSE of saturated rows, rel err {rel.max():.2e}"
+            small = ~huge
+            assert_close(lse[b, h][small], want_l[small], dt, f"extreme LSE b={b} h={h}")

@@ -56,24 +56,6 @@ def test_dense_dflash_mask_and_dense_builder(case):
     assert_bm_equal(got, np_bm(bsm.build_block_mask(geom, pred=d)), "dense vs pred")
 
 
-def test_long_context_pred_block_mask_sampled():
-    """Long-context DFlash: one head-shared (1,1,256,512) block mask; sampled
-    query tiles against the oracle, plus the 7215 full / 961 partial totals."""
-    d = bsm.DFlash(32768, 2048, 16, is_causal=True, layer_type="sliding", sliding_window=4096)
-    geom = (1, 32, 8, d.Sq, d.Sk, 128)
-    kvn, kvi, fn, fi = np_bm(bsm.build_block_mask(geom, pred=d))
-    assert kvi.shape == (1, 1, 256, 512)
-    assert (int(fn.sum()), int(kvn.sum())) == (7215, 961)
-    og = oracle_geom(d)
-    for t in [0, 1, 30, 31, 32, 100, 200, 254, 255]:
-        band = oracle.dflash_dense_mask(og, np.arange(128 * t, 128 * t + 128))
-        part, full = oracle.blockmask.classify_tile_band(band, og.Sk)
-        np.testing.assert_array_equal(kvi[0, 0, t, :kvn[0, 0, t]], part)
-        np.testing.assert_array_equal(fi[0, 0, t, :fn[0, 0, t]], full)
-        assert (kvi[0, 0, t, kvn[0, 0, t]:] == -1).all()
-        assert (fi[0, 0, t, fn[0, 0, t]:] == -1).all()
-
-
 def test_long_context_dense_stand_in():
     """The 2 GiB (1,1,32768,65536) dense form of the long-context mask: the dense
     builder gives exactly the predicate builder's block mask."""
