@@ -89,9 +89,19 @@ def sample_rows(Sq, n, seed):
     return np.array(sorted(base))
 
 
+def oracle_topk_mask(bias, seqlen_k, k, dtype="bf16"):
+    """The oracle's top-k keep mask of a stored bias, as a bool tensor on the
+    bias's device. Tests that need a top-k mask for attention use this one for
+    both the GPU run and the oracle, so the oracle never takes a mask the GPU
+    built (the GPU's top-k is compared with it bit for bit elsewhere)."""
+    m = oracle.topk_keep_mask(synth.as_f64(bias), None, seqlen_k, k, dtype)
+    return torch.from_numpy(m).to(bias.device)
+
+
 def cuda(*ts):
     return [None if t is None else t.cuda() for t in ts]
 
 
 __all__ = ["bsm", "synth", "oracle", "say", "oracle_geom", "np_bm", "assert_bm_equal",
-           "assert_close", "oracle_rows", "sample_rows", "cuda", "batch_slice"]
+           "assert_close", "oracle_rows", "sample_rows", "cuda", "batch_slice",
+           "oracle_topk_mask"]

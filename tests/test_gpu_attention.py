@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows, say, synth
+from gpu_helpers import (assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows,
+                         oracle_topk_mask, say, synth)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,7 +119,7 @@ def test_decode_swap_small(with_mask):
     bias = synth.normal_tensor((B, H, 1, 1024), 4, synth.TID_BIAS, "bf16").cuda()
     mask = bm = None
     if with_mask:
-        mask = bsm.dynamic_topk_mask(bias, None, Sk, 100)
+        mask = oracle_topk_mask(bias, Sk, 100)
         bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
         assert bm.kv_indices.shape == (B, KVH, 1, 8)
     _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, what="swap")

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import bsm, cuda, oracle_geom, say, synth
+from gpu_helpers import bsm, cuda, oracle_geom, oracle_topk_mask, say, synth
 from oracle.attention_bwd import attention_bwd, group_grads
 
 pytestmark = pytest.mark.gpu
@@ -134,7 +134,7 @@ def test_decode_swap(with_mask):
     bias = synth.normal_tensor((B, H, 1, 384), 4, synth.TID_BIAS, "bf16").cuda()
     mask = bm = None
     if with_mask:
-        mask = bsm.dynamic_topk_mask(bias, None, Sk, 50)
+        mask = oracle_topk_mask(bias, Sk, 50)
         bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
     _check_full(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, need_dbias=True, seed=4,
                 what="swap")

@@ -6,7 +6,8 @@ pool of host processes (tests/oracle_pool.py):
     placed differently per head -- plus rows 0, 127, 128 and the last; and the
     head-shared block mask on all 256 query tiles, bit-exact;
   * dynamic top-k: every row of every (b, h);
-  * decode with the head-group swap: every (b, h).
+  * decode with the head-group swap: every (b, h), through the block mask and
+    through the kept-key list.
 
 Every mask the oracle uses is its own (its DFlash rule, its top-k), never the
 GPU's. Bars: bf16 max |err| <= 2e-2 and mean |err| <= 2e-3 per (b, h), on O and
@@ -130,7 +131,9 @@ def test_dynamic_topk_every_row():
 
 def test_decode_every_head():
     """Decode (Sq = 1, head-group swap): every (b, h) against the unswapped
-    definition, with the oracle's own top-k mask of each batch."""
+    definition with the oracle's own top-k mask of each batch, through both
+    decode paths -- the block mask over key tiles, and the kept-key list with
+    the key-gather kernel."""
     name = "decode_swap_bf16"
     cfg = synth.CONFIGS[name]
     B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
@@ -139,17 +142,21 @@ def test_decode_every_head():
     q, k, v, bias = qc.cuda(), kc.cuda(), vc.cuda(), bias_c.cuda()
     say("decode, every (b, h)")
     mask = bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"])
-    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
-    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm, return_lse=True)
-    torch.cuda.synchronize()
-    o = o.float().cpu().numpy()
-    lse = lse.cpu().numpy()
-    del q, k, v, mask, bm
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    keys = bsm.build_key_list(geom, mask)
+    got = {}
+    for path, kw in (("tiles", dict(block_mask=bm)), ("gather", dict(keys=keys))):
+        o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, return_lse=True, **kw)
+        torch.cuda.synchronize()
+        got[path] = (o.float().cpu().numpy(), lse.cpu().numpy())
+    del q, k, v, mask, bm, keys
     masks = oracle_pool.run(oracle_pool.topk_mask_rows, [(name, b) for b in range(B)])
     for b in range(B):
         qb, kb, vb = synth.as_f64(qc[b:b + 1]), synth.as_f64(kc[b:b + 1]), synth.as_f64(vc[b:b + 1])
         bb = synth.as_f64(bias_c[b:b + 1])
         for h in range(H):
             want_o, want_l = oracle.attention_rows(qb, kb, vb, 0, h, [0], mask=masks[b], bias=bb)
-            assert_close(o[b, 0, h][None], want_o, "bf16", f"decode O b={b} h={h}")
-            assert_close(lse[b, h], want_l, "bf16", f"decode LSE b={b} h={h}")
+            for path, (o, lse) in got.items():
+                assert_close(o[b, 0, h][None], want_o, "bf16", f"decode {path} O b={b} h={h}")
+                assert_close(lse[b, h], want_l, "bf16", f"decode {path} LSE b={b} h={h}")

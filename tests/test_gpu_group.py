@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows, say, synth
+from gpu_helpers import (assert_close, bsm, cuda, oracle, oracle_geom, oracle_rows,
+                         oracle_topk_mask, say, synth)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +118,7 @@ def test_swapped_decode_few_sequences(B):
     Sk, H, KVH, D = 16384, 32, 8, 128
     q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=83))
     bias = synth.normal_tensor((B, H, 1, Sk), 83, synth.TID_BIAS, "bf16").cuda()
-    mask = bsm.dynamic_topk_mask(bias, None, Sk, 1024)
+    mask = oracle_topk_mask(bias, Sk, 1024)
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
     _check(q, k, v, f"swap B={B}", mask=mask, bias=bias, bm=bm, heads=[0, 5, 31])
     _check(q, k, v, f"swap B={B} no mask", heads=[0, 30])

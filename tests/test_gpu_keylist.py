@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_close, bsm, cuda, oracle_rows, say, synth
+import oracle_pool
+from gpu_helpers import assert_close, bsm, cuda, oracle_rows, oracle_topk_mask, say, synth
 from oracle.keylist import key_list
 
 pytestmark = pytest.mark.gpu
@@ -70,17 +71,19 @@ def test_key_list_matches_oracle(geom, shape, density):
 
 
 def test_key_list_decode_full_size_sampled():
-    """Decode shape (B=64, H=32, KVH=8, Sk=16384, top-1024 per head): lists of
-    sampled (b, KV head) pairs against the oracle, and every list's count
-    against the union of its four top-k rows."""
-    cfg = synth.CONFIGS["decode_swap_bf16"]
+    """Decode shape (B=64, H=32, KVH=8, Sk=16384, top-1024 per head), built
+    from the oracle's top-k masks: lists of sampled (b, KV head) pairs against
+    the oracle, and every list's count against the union of its four top-k
+    rows."""
+    name = "decode_swap_bf16"
+    cfg = synth.CONFIGS[name]
     B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
     geom = (B, H, KVH, 1, Sk, D)
-    bias, _ = synth.topk_inputs(cfg, seed=0)
-    mask = bsm.dynamic_topk_mask(bias.cuda(), None, Sk, cfg["topk"])
-    kl = bsm.build_key_list(geom, mask)
+    mask_np = np.concatenate(oracle_pool.run(oracle_pool.topk_mask_rows,
+                                             [(name, b) for b in range(B)]))
+    kl = bsm.build_key_list(geom, torch.from_numpy(mask_np).cuda())
     torch.cuda.synchronize()
-    m = _iter_mask(mask.cpu().numpy(), geom)
+    m = _iter_mask(mask_np, geom)
     union = m[..., :Sk].any(axis=2).sum(axis=-1)
     np.testing.assert_array_equal(kl.num_keys.cpu().numpy(), union)
     pairs = [(0, 0), (17, 3), (40, 7), (63, 5)]
@@ -114,7 +117,7 @@ def test_gather_decode_swap(D, with_bias):
     B, Sk, H, KVH = 3, 1000, 8, 2
     q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=30 + D))
     bias = synth.normal_tensor((B, H, 1, 1024), 30, synth.TID_BIAS, "bf16").cuda()
-    mask = bsm.dynamic_topk_mask(bias, None, Sk, 100)
+    mask = oracle_topk_mask(bias, Sk, 100)
     keys = bsm.build_key_list(bsm.geometry_of(q, k), mask)
     _gather_check(q, k, v, mask, bias if with_bias else None, keys, f"swap D={D}")
 
@@ -168,24 +171,3 @@ def test_gather_list_with_keys_out_of_range():
     for h in range(H):
         want_o, _ = oracle_rows(q, k, v, 0, h, [0], mask=mask2)
         assert_close(out[0, 0, h].float().cpu().numpy()[None], want_o, "bf16", f"h={h}")
-
-
-def test_gather_decode_full_size_sampled():
-    """The decode workload (B=64, H=32, KVH=8, Sk=16384, per-head bias, top-1024)
-    through the key list, sampled (b, h) against the oracle."""
-    cfg = synth.CONFIGS["decode_swap_bf16"]
-    B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
-    q, k, v = cuda(*synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0))
-    bias, _ = synth.topk_inputs(cfg, seed=0)
-    bias = bias.cuda()
-    mask = bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"])
-    keys = bsm.build_key_list(bsm.geometry_of(q, k), mask)
-    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, keys=keys, return_lse=True)
-    torch.cuda.synchronize()
-    say("gather decode full size: comparing sampled (b, h)")
-    for b in (0, 17, 63):
-        for h in (0, 13, 31):
-            want_o, want_l = oracle_rows(q, k, v, b, h, [0], mask=mask, bias=bias)
-            assert_close(o[b, 0, h].float().cpu().numpy()[None], want_o, "bf16",
-                         f"O b={b} h={h}")
-            assert_close(lse[b, h].cpu().numpy(), want_l, "bf16", f"LSE b={b} h={h}")

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle_pool
 from gpu_helpers import assert_bm_equal, bsm, np_bm, oracle, say, synth
 from oracle.keylist import key_list
 
@@ -105,7 +106,8 @@ def test_fused_pre_masked_rows_and_mask_not_written():
 
 def test_fused_decode_full_size():
     """The decode workload (B=64, H=32, KVH=8, Sk=16384, k=1024): fused outputs
-    equal the unfused kernels' in full; sampled lists against the oracle."""
+    equal the unfused kernels' in full, the mask equals the oracle's top-k, and
+    sampled lists match the oracle's lists of the oracle's mask."""
     cfg = synth.CONFIGS["decode_swap_bf16"]
     B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
     geom = (B, H, KVH, 1, Sk, D)
@@ -119,7 +121,10 @@ def test_fused_decode_full_size():
     assert torch.equal(mask, ref_mask)
     assert_bm_equal(np_bm(bm), np_bm(ref_bm), "decode bm")
     assert torch.equal(keys.num_keys, ref_keys.num_keys)
-    it = _iter_view(ref_mask.cpu().numpy(), geom)
+    omask = np.concatenate(oracle_pool.run(oracle_pool.topk_mask_rows,
+                                           [("decode_swap_bf16", b) for b in range(B)]))
+    np.testing.assert_array_equal(mask.cpu().numpy(), omask)
+    it = _iter_view(omask, geom)
     for b, h in ((0, 0), (31, 4), (63, 7)):
         wn, wk, wb = key_list(it[b:b + 1, h:h + 1], Sk, H // KVH)
         n = int(wn[0, 0])
