@@ -29,7 +29,8 @@ BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
            "key_list_shape", "build_key_list", "dynamic_topk_mask", "dynamic_topk_fused",
            "dflash_dense_mask",
-           "masked_attn_fwd", "attn_fwd_workspace_size", "attn_bwd_workspace_size",
+           "masked_attn_fwd", "attn_fwd_workspace_size",
+           "attn_bwd_workspace_size",
            "masked_attn_bwd",
            "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
            "unpad_index", "gather_rows", "scatter_rows", "bsm_last_error")
@@ -168,9 +169,22 @@ def tensor4(t, dims=4):
     return x
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
+def _stream(stream, *owned):
+    """The HIP stream handle to launch on: `stream`, or torch's current stream
+    when None. On a stream other than the current one, the launch must see what
+    the current stream has queued (inputs written there, outputs zero-filled by
+    this module), so `stream` first waits for it; and every tensor this module
+    allocated for the call (`owned`: outputs, workspaces, or tuples of them) is
+    recorded as used on `stream`, so that torch's caching allocator does not
+    hand its memory out again before the launch has completed."""
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        return c_void_p(cur.cuda_stream)
+    stream.wait_stream(cur)
+    for t in owned:
+        for x in (t if isinstance(t, tuple) else (t,)):
+            if isinstance(x, torch.Tensor) and x.is_cuda:
+                x.record_stream(stream)
     return c_void_p(stream.cuda_stream)
 
 
@@ -295,7 +309,7 @@ def build_block_mask(geom, pred=None, mask=None, device=None, stream=None):
     bc = bm.c()
     _check(lib().build_block_mask(ctypes.byref(g), ctypes.byref(pc) if pc else None,
                                   ctypes.byref(mc) if mc else None, ctypes.byref(bc),
-                                  _stream(stream)))
+                                  _stream(stream, bm)))
     return bm
 
 
@@ -316,19 +330,21 @@ def build_key_list(geom, mask, stream=None):
     mc = tensor4(mask)
     kc = kl.c()
     _check(lib().build_key_list(ctypes.byref(Geometry(*geom).c()), ctypes.byref(mc),
-                                ctypes.byref(kc), _stream(stream)))
+                                ctypes.byref(kc), _stream(stream, kl)))
     return kl
 
 
 def dynamic_topk_mask(bias, premask, seqlen_k, k, out=None, stream=None):
     """Top-k keep mask (bool, bias's shape) over a 4D bias."""
+    owned = out is None
     if out is None:
         out = torch.empty(bias.shape, dtype=torch.bool, device=bias.device)
     bc = tensor4(bias)
     pc = tensor4(premask) if premask is not None else None
     _check(lib().dynamic_topk_mask(ctypes.byref(bc), ctypes.byref(pc) if pc else None,
                                    int(seqlen_k), int(k),
-                                   out.data_ptr() if out.numel() else None, _stream(stream)))
+                                   out.data_ptr() if out.numel() else None,
+                                   _stream(stream, out if owned else None)))
     return out
 
 
@@ -360,7 +376,8 @@ def dynamic_topk_fused(geom, bias, premask, k, want_mask=True, want_block_mask=T
                                     ctypes.byref(pc) if pc else None, int(k),
                                     mask.data_ptr() if mask is not None and mask.numel() else None,
                                     ctypes.byref(bmc) if bmc else None,
-                                    ctypes.byref(kc) if kc else None, _stream(stream)))
+                                    ctypes.byref(kc) if kc else None,
+                                    _stream(stream, mask, bm, keys)))
     return mask, bm, keys
 
 
@@ -420,28 +437,28 @@ def create_mask(attention_bias, attention_mask, batch_size, query_len, key_len, 
 def dflash_dense_mask(geom, pred, out=None, stream=None):
     """Dense (Sq, K_round) bool DFlash mask, written by the library's kernel."""
     g = Geometry(*geom)
+    owned = out is None
     if out is None:
         out = torch.empty((g.Sq, round_multiple(g.Sk)), dtype=torch.bool, device="cuda")
     pc = pred.c()
     _check(lib().dflash_dense_mask(ctypes.byref(g.c()), ctypes.byref(pc),
-                                   out.data_ptr() if out.numel() else None, _stream(stream)))
+                                   out.data_ptr() if out.numel() else None,
+                                   _stream(stream, out if owned else None)))
     return out
 
 
-def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
-                    softmax_scale=None, return_lse=False, out=None, lse=None, stream=None,
-                    keys=None, split=True, workspace=None):
-    """Masked attention forward; returns O (and LSE if return_lse).
-
-    split: allocate (unless given) the workspace attn_fwd_workspace_size asks
-    for, which lets short query blocks split their keys over several
-    workgroups and folds a query-broadcast mask / bias into staged rows;
-    split=False runs without either."""
+def _fwd_args(q, k, v, pred, mask, bias, block_mask, softmax_scale, return_lse, out, lse,
+              keys):
+    """AttnArgs of a forward call; returns (geometry, args, the ctypes objects
+    it points to, out, lse, the tensors allocated here)."""
     geom = geometry_of(q, k)
+    owned = []
     if out is None:
         out = torch.empty_like(q)
+        owned.append(out)
     if return_lse and lse is None:
         lse = torch.empty((geom.B, geom.H, geom.Sq), dtype=torch.float32, device=q.device)
+        owned.append(lse)
     a = AttnArgs()
     a.q, a.k, a.v = tensor4(q), tensor4(k), tensor4(v)
     a.o = out.data_ptr() if out.numel() else None
@@ -471,6 +488,20 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
         kc = keys.c()
         keep.append(kc)
         a.keys = ctypes.pointer(kc)
+    return geom, a, keep, out, lse, owned
+
+
+def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
+                    softmax_scale=None, return_lse=False, out=None, lse=None, stream=None,
+                    keys=None, split=True, workspace=None):
+    """Masked attention forward; returns O (and LSE if return_lse).
+
+    split: allocate (unless given) the workspace attn_fwd_workspace_size asks
+    for, which lets short query blocks split their keys over several
+    workgroups and folds a query-broadcast mask / bias into staged rows;
+    split=False runs without either."""
+    geom, a, keep, out, lse, owned = _fwd_args(q, k, v, pred, mask, bias, block_mask,
+                                               softmax_scale, return_lse, out, lse, keys)
     gc = geom.c()
     if split:
         if workspace is None:
@@ -479,10 +510,12 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
                                                  ctypes.byref(need)))
             if need.value > 0:
                 workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+                owned.append(workspace)
         if workspace is not None:
             a.workspace = workspace.data_ptr()
             a.workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().masked_attn_fwd(ctypes.byref(gc), ctypes.byref(a), _stream(stream)))
+    _check(lib().masked_attn_fwd(ctypes.byref(gc), ctypes.byref(a),
+                                 _stream(stream, *owned)))
     return (out, lse) if return_lse else out
 
 
@@ -529,7 +562,8 @@ def masked_attn_bwd(q, k, v, out, dout, lse, pred=None, mask=None, bias=None, bl
     ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
     a.workspace = ws.data_ptr()
     a.workspace_bytes = nbytes.value
-    _check(lib().masked_attn_bwd(ctypes.byref(gc), ctypes.byref(a), _stream(stream)))
+    _check(lib().masked_attn_bwd(ctypes.byref(gc), ctypes.byref(a),
+                                 _stream(stream, dq, dk, dv, dbias, ws)))
     if dbias is not None:
         dbias = dbias[..., :geom.Sk]
     return dq, dk, dv, dbias
@@ -590,7 +624,7 @@ def build_block_mask_varlen(varlen, pred, stream=None):
                    torch.empty((Bm, Hm, nQm, nK), dtype=torch.int32, device=dev))
     vc, pc, bc = varlen.c(), pred.c(), bm.c()
     _check(lib().build_block_mask_varlen(ctypes.byref(vc), ctypes.byref(pc), ctypes.byref(bc),
-                                         _stream(stream)))
+                                         _stream(stream, bm)))
     return bm
 
 
@@ -601,6 +635,7 @@ def masked_attn_varlen_fwd(q, k, v, varlen, pred=None, block_mask=None, softmax_
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("packed q, k, v must be 3D (rows, heads, D)")
     q4, k4, v4 = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    owned = out is None
     if out is None:
         out = torch.empty_like(q)
     o4 = out.unsqueeze(0)
@@ -624,7 +659,8 @@ def masked_attn_varlen_fwd(q, k, v, varlen, pred=None, block_mask=None, softmax_
         keep.append(bmc)
         a.bm = ctypes.pointer(bmc)
     vc = varlen.c()
-    _check(lib().masked_attn_varlen_fwd(ctypes.byref(vc), ctypes.byref(a), _stream(stream)))
+    _check(lib().masked_attn_varlen_fwd(ctypes.byref(vc), ctypes.byref(a),
+                                        _stream(stream, out if owned else None, lse)))
     return (out, lse[0]) if return_lse else out
 
 
@@ -641,7 +677,11 @@ def unpad(x, valid, stream=None):
     cu = torch.empty(B + 1, dtype=torch.int32, device=x.device)
     idx = torch.empty(max(B * S, 1), dtype=torch.int32, device=x.device)
     _check(lib().unpad_index(valid.data_ptr() if valid.numel() else None, B, S,
-                             valid.stride(0), cu.data_ptr(), idx.data_ptr(), _stream(stream)))
+                             valid.stride(0), cu.data_ptr(), idx.data_ptr(),
+                             _stream(stream, xc, cu, idx)))
+    if stream is not None:
+        # the read-back runs on the current stream: order it after the index pass
+        torch.cuda.current_stream().wait_stream(stream)
     cu_host = cu.cpu()
     total = int(cu_host[-1])
     lens = cu_host[1:] - cu_host[:-1]
@@ -650,7 +690,7 @@ def unpad(x, valid, stream=None):
     packed = torch.empty((total,) + row_shape, dtype=x.dtype, device=x.device)
     if total:
         _check(lib().gather_rows(xc.data_ptr(), row_bytes, packed.data_ptr(), row_bytes,
-                                 row_bytes, idx.data_ptr(), total, _stream(stream)))
+                                 row_bytes, idx.data_ptr(), total, _stream(stream, packed)))
     return packed, idx[:total], cu, int(lens.max()) if B else 0
 
 
@@ -662,6 +702,6 @@ def pad(packed, indices, B, S, stream=None):
     if n:
         row_bytes = pc[0].numel() * pc.element_size()
         _check(lib().scatter_rows(pc.data_ptr(), row_bytes, out.data_ptr(), row_bytes,
-                                  row_bytes, indices.data_ptr(), n, _stream(stream)))
+                                  row_bytes, indices.data_ptr(), n, _stream(stream, pc, out)))
     return out
 
