@@ -25,11 +25,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsm.so")
 BSM_OK, BSM_E_ARG, BSM_E_SHAPE, BSM_E_STRIDE, BSM_E_DTYPE, BSM_E_UNSUPPORTED, BSM_E_HIP = \
     0, -1, -2, -3, -4, -5, -6
 BSM_BOOL, BSM_BF16, BSM_F32 = 0, 1, 2
+# bytes of the static device scratch of masked_attn_fwd_noalloc (BSM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
            "key_list_shape", "build_key_list", "dynamic_topk_mask", "dynamic_topk_fused",
            "dflash_dense_mask",
-           "masked_attn_fwd", "attn_fwd_workspace_size",
+           "masked_attn_fwd", "masked_attn_fwd_noalloc", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size",
            "masked_attn_bwd",
            "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
@@ -116,6 +118,7 @@ def lib():
                                          POINTER(KeyListC), c_void_p]
         L.dflash_dense_mask.argtypes = [POINTER(Geom), POINTER(DFlashC), c_void_p, c_void_p]
         L.masked_attn_fwd.argtypes = [POINTER(Geom), POINTER(AttnArgs), c_void_p]
+        L.masked_attn_fwd_noalloc.argtypes = L.masked_attn_fwd.argtypes
         L.attn_fwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnArgs), POINTER(c_int64)]
         L.attn_bwd_workspace_size.argtypes = [POINTER(Geom), POINTER(AttnBwdArgs),
                                               POINTER(c_int64)]
@@ -517,6 +520,19 @@ def masked_attn_fwd(q, k, v, pred=None, mask=None, bias=None, block_mask=None,
     _check(lib().masked_attn_fwd(ctypes.byref(gc), ctypes.byref(a),
                                  _stream(stream, *owned)))
     return (out, lse) if return_lse else out
+
+
+def masked_attn_fwd_noalloc(q, k, v, out, lse=None, pred=None, mask=None, bias=None,
+                            block_mask=None, softmax_scale=None, stream=None, keys=None):
+    """masked_attn_fwd through the library's entry point that allocates
+    nothing: the caller passes O (and LSE, or None), and any workspace comes
+    from the library's static device scratch (see NOALLOC_SCRATCH_BYTES).
+    Calls that overlap in time on one device share that scratch and race."""
+    geom, a, keep, out, lse, _ = _fwd_args(q, k, v, pred, mask, bias, block_mask,
+                                           softmax_scale, lse is not None, out, lse, keys)
+    _check(lib().masked_attn_fwd_noalloc(ctypes.byref(geom.c()), ctypes.byref(a),
+                                         _stream(stream)))
+    return out
 
 
 def masked_attn_bwd(q, k, v, out, dout, lse, pred=None, mask=None, bias=None, block_mask=None,

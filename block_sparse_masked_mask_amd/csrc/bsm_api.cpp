@@ -273,6 +273,11 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+int bsm::set_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
 extern "C" {
 
 const char* bsm_last_error(void) { return g_err.c_str(); }

@@ -236,4 +236,7 @@ bool short_query_applies(const AttnParams& p, int D);
 hipError_t launch_attn_group(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_attn_gather(const AttnParams& p, int D, hipStream_t s);
 
+// Sets the thread's error string (bsm_last_error) and returns `code`.
+int set_error(int code, const char* msg);
+
 }  // namespace bsm

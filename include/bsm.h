@@ -41,7 +41,8 @@
  *     and masked_attn_fwd both apply it, so a block mask always lives in the
  *     iteration space of the attention kernel; block_mask_shape reports it.
  *   Ownership. The caller allocates every device buffer; the library allocates
- *     no device memory and keeps no state except a thread-local error string.
+ *     no device memory and keeps no state except a thread-local error string
+ *     and the static scratch array of masked_attn_fwd_noalloc (below).
  *     Work is enqueued on `stream` with no host synchronisation, so inputs and
  *     outputs must stay alive until that stream's work completes.
  *   Errors. Every entry point returns 0 (BSM_OK) or a negative bsm_status. On a
@@ -271,6 +272,30 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* args,
  * With a smaller or NULL workspace the same call runs without them; the result
  * is the same up to float rounding order. */
 int attn_fwd_workspace_size(const bsm_geom* geom, const bsm_attn_args* args, int64_t* bytes);
+
+/* Bytes of the static device scratch array of masked_attn_fwd_noalloc. */
+#define BSM_NOALLOC_SCRATCH_BYTES (32LL << 20)
+
+/* masked_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * args->workspace must be NULL and args->workspace_bytes 0. The call runs the
+ * kernels masked_attn_fwd runs when given attn_fwd_workspace_size's bytes, with
+ * that workspace taken from a static device array of BSM_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on each device it runs on until the process
+ * ends; results are identical to that call's. It allocates nothing and calls
+ * no allocating routine.
+ * Errors: a call that would need more than BSM_NOALLOC_SCRATCH_BYTES returns
+ * BSM_E_UNSUPPORTED (use masked_attn_fwd with a workspace); a stream of another
+ * device than the current one returns BSM_E_ARG; nothing is enqueued then.
+ * The first call on a device that needs the scratch looks up that device's
+ * copy of the array (loading the library's device code there if nothing has
+ * yet): make it outside graph capture. All calls on one device share its one
+ * array. Every byte a call reads from it is written earlier in the same call,
+ * so nothing needs clearing, but calls that overlap in time on one device
+ * (other streams, other host threads) race on it and corrupt each other's
+ * results: order them on one stream or synchronise between them. */
+int masked_attn_fwd_noalloc(const bsm_geom* geom, const bsm_attn_args* args,
+                            hipStream_t stream);
 
 /* Arguments of masked_attn_bwd: the forward's inputs, its output O and LSE,
  * the incoming gradient dL/dO, and the gradient outputs. */

@@ -469,3 +469,42 @@ def test_topk_fused_validation(L):
                                 None, None, None) == bsm.BSM_E_SHAPE
     assert bm.Bm == 2
 
+
+
+def test_noalloc_scratch_size_matches_header(tmp_path):
+    src = tmp_path / "scratch.c"
+    src.write_text('#include <stdio.h>\n#include "bsm.h"\n'
+                   'int main(void) { printf("%lld\\n", (long long)BSM_NOALLOC_SCRATCH_BYTES); '
+                   'return 0; }\n')
+    exe = tmp_path / "scratch"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("no C compiler for the header: " + r.stderr[:200])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    assert int(out) == bsm.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_noalloc_rejects_before_any_launch(L):
+    """The entry point without allocation refuses a caller's workspace, and a
+    call whose plan needs more than the static scratch, before touching a
+    device (the stream argument is never used on these paths)."""
+    geom = (2, 32, 8, 1, 16384, 128)
+    g = bsm.Geom(*geom)
+    a = _attn_args(geom)
+    a.workspace, a.workspace_bytes = 1 << 24, 256
+    assert L.masked_attn_fwd_noalloc(ctypes.byref(g), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    assert b"workspace" in L.bsm_last_error()
+    # staged query-broadcast bias rows of (8, 32 heads, 100096 keys) floats: 102.5 MB
+    big = (8, 32, 8, 256, 100000, 128)
+    g = bsm.Geom(*big)
+    a = _attn_args(big)
+    bias = _t4((8, 32, 1, 100096), bsm.BSM_BF16)
+    a.bias = ctypes.pointer(bias)
+    need = ctypes.c_int64(0)
+    assert L.attn_fwd_workspace_size(ctypes.byref(g), ctypes.byref(a), ctypes.byref(need)) == 0
+    assert need.value == 8 * 32 * 782 * 128 * 4 > bsm.NOALLOC_SCRATCH_BYTES
+    assert L.masked_attn_fwd_noalloc(ctypes.byref(g), ctypes.byref(a), None) == \
+        bsm.BSM_E_UNSUPPORTED
+    assert b"scratch" in L.bsm_last_error()
