@@ -16,9 +16,17 @@ value = counted flops of the step / step time, where counted flops are
   mask_build   -- the dense-mask block-mask builder on the long-context DFlash
                   mask materialised densely (1 x 1 x 32768 x 65536 bytes), GB/s
                   against HBM peak;
-  cpu_baseline -- the CPU oracle timed on a bounded sample of the same work.
+  configs      -- the other workloads at full size: long-context DFlash (TFLOP/s,
+                  fraction of peak, device memory), dynamic top-k (TFLOP/s,
+                  fraction of peak), decode (GB/s of the tile and the gather
+                  path against HBM peak), tiny fp32 (launch time);
+  cpu_baseline -- the CPU oracle on a pool of one-thread host processes, one
+                  per usable core (at most 16), on a bounded random sample of
+                  every workload: wall seconds, oracle seconds, extrapolated
+                  full-workload seconds; `value` is the training step's.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-configs] [--no-mask-build]
 """
 
 import argparse
@@ -50,8 +58,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "803743d085e86c7c",
-                "fetch_kib": 86583.3, "write_kib": 65536.0,
+                "sha256_16": "401bf5e7df5dc120",
+                "fetch_kib": 86622.6, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -357,7 +365,9 @@ def measure_decode():
     out = {}
     cfg = synth.CONFIGS["decode_swap_bf16"]
     B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
-    q, k, v = [t.cuda() for t in synth.qkv(B, 1, Sk, H, KVH, D, "bf16", seed=0)]
+    q = _device_normal((B, 1, H, D), 111)
+    k = _device_normal((B, Sk, KVH, D), 112)
+    v = _device_normal((B, Sk, KVH, D), 113)
     bias, _ = synth.topk_inputs(cfg, seed=0)
     bias = bias.cuda()
     mask = torch.empty(bias.shape, dtype=torch.bool, device="cuda")
@@ -396,40 +406,344 @@ def measure_decode():
     return out
 
 
-def cpu_baseline(step, budget_s=20.0):
-    """The fp64 oracle on a bounded sample of the step's work, in the metric's unit."""
-    import oracle
-    from threadpoolctl import threadpool_info
+# ---------------------------------------------------------------------------
+# the other workloads at full size, in the default line
 
-    cfg = step.cfg
-    q, k, v = step.q.cpu(), step.k.cpu(), step.v.cpu()
-    rng = np.random.default_rng(0)
-    done_flops = 0
-    units = 0
+
+def _device_normal(shape, seed, scale=1.0):
+    """bf16 N(0, scale^2) draws made on the device (torch's generator seeded
+    `seed`): the same distribution as the host generator, for inputs too large
+    to draw on the host within the run."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    y = x.to(torch.bfloat16)
+    del x
+    return y
+
+
+def measure_long_context(reps=3):
+    """Long-context DFlash (B=1, H=32, KVH=8, D=128, 32768 queries, 65536 keys,
+    causal in-block, window 4096): block mask from the predicate, attention on
+    the kept tiles, and the device memory the call needs beyond its tensors."""
+    cfg = synth.CONFIGS["long_dflash_bf16"]
+    lay = cfg["layers"][0]
+    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"], is_causal=lay["is_causal"],
+                   layer_type=lay["layer_type"], sliding_window=lay["window"])
+    B, H, KVH, D = cfg["B"], cfg["H"], cfg["KVH"], cfg["D"]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    q = _device_normal((B, d.Sq, H, D), 101)
+    k = _device_normal((B, d.Sk, KVH, D), 102)
+    v = _device_normal((B, d.Sk, KVH, D), 103)
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+    tensors = sum(t.numel() * t.element_size() for t in (q, k, v, o))
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, pred=d)
+    bm_bytes = sum(t.numel() * t.element_size() for t in bm)
+    bm_us = 1e3 * _time_ms(lambda: bsm.build_block_mask(geom, pred=d))
+    fl = counted_flops(bm, geom)
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, out=o), reps=reps)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    del q, k, v, o
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"attn_ms": ms, "TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS, "flops": int(fl),
+            "block_mask_us": bm_us, "block_mask_bytes": int(bm_bytes),
+            "peak_device_bytes": int(tensors + extra), "tensor_bytes": int(tensors),
+            "peak_bytes_beyond_tensors": int(extra),
+            "dense_mask_bytes_per_head_copy": int(B * H * d.Sq * d.Sk)}
+
+
+def measure_dynamic_topk(reps=5):
+    """Dynamic-mask workload (B=2, H=16, KVH=4, Sq=Sk=8000, bias (2,4,1,8064),
+    2D right padding, top-2048): top-k, block mask, attention."""
+    cfg = synth.CONFIGS["dynamic_topk_bf16"]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = [t.cuda() for t in synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0)]
+    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    fl = counted_flops(bm, geom)
+    o = torch.empty_like(q)
+    topk_us = 1e3 * _time_ms(lambda: bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"]))
+    bm_us = 1e3 * _time_ms(lambda: bsm.build_block_mask(geom, mask=mask))
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o), reps=reps)
+    del q, k, v, o
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"attn_ms": ms, "TFLOP/s": tf, "frac": tf / PEAK_BF16_TFLOPS, "flops": int(fl),
+            "topk_us": topk_us, "block_mask_us": bm_us}
+
+
+def measure_decode_swap(reps=5):
+    """Decode with the head-group swap (B=64, H=32, KVH=8, Sk=16384, per-head
+    bias, top-1024): top-k, then the tile path (block mask + tile-visiting
+    kernel, every K/V row read) and the gather path (kept-key list + key-gather
+    kernel, listed rows read). GB/s counts the bytes each path must move."""
+    cfg = synth.CONFIGS["decode_swap_bf16"]
+    B, H, KVH, D, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sk"))
+    q = _device_normal((B, 1, H, D), 111)
+    k = _device_normal((B, Sk, KVH, D), 112)
+    v = _device_normal((B, Sk, KVH, D), 113)
+    bias = synth.topk_inputs(cfg, seed=0)[0].cuda()
+    mask = torch.empty(bias.shape, dtype=torch.bool, device="cuda")
+    topk_us = 1e3 * _time_ms(lambda: bsm.dynamic_topk_mask(bias, None, Sk, cfg["topk"], out=mask))
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    bm_us = 1e3 * _time_ms(lambda: bsm.build_block_mask(geom, mask=mask))
+    o = torch.empty_like(q)
+    row_bytes = 2 * D * 2  # one K row and one V row, bf16
+    small = bias.numel() * 2 + 2 * q.numel() * 2
+    ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm,
+                                              out=o), reps=reps)
+    t_bytes = row_bytes * B * KVH * Sk + mask.numel() + small
+    keys = bsm.build_key_list(geom, mask)
+    kl_us = 1e3 * _time_ms(lambda: bsm.build_key_list(geom, mask))
+    listed = int(keys.num_keys.sum())
+    mg = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, keys=keys, out=o),
+                  reps=reps)
+    g_bytes = row_bytes * listed + listed * 8 + small
+    del q, k, v, o
+    return {"topk_us": topk_us,
+            "tiles": {"block_mask_us": bm_us, "attn_ms": ms, "bytes": int(t_bytes),
+                      "GB/s": t_bytes / (ms * 1e-3) / 1e9,
+                      "frac": t_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "gather": {"key_list_us": kl_us, "attn_ms": mg, "bytes": int(g_bytes),
+                       "listed_frac": listed / (B * KVH * Sk),
+                       "GB/s": g_bytes / (mg * 1e-3) / 1e9,
+                       "frac": g_bytes / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+
+def measure_tiny(reps=20):
+    """Tiny DFlash, fp32 (B=1, H=2, D=64, 64 queries, 320 keys): launch-bound."""
+    cfg = synth.CONFIGS["tiny_dflash_fp32"]
+    d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"])
+    q, k, v = [t.cuda() for t in synth.qkv(1, d.Sq, d.Sk, cfg["H"], cfg["KVH"], cfg["D"], "f32",
+                                           seed=0)]
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, pred=d)
+    o = torch.empty_like(q)
+    us = 1e3 * _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, out=o),
+                        reps=reps)
+    return {"attn_us": us, "block_mask_us": 1e3 * _time_ms(
+        lambda: bsm.build_block_mask(geom, pred=d), reps=reps)}
+
+
+def measure_configs():
+    return {"tiny_dflash_fp32": measure_tiny(),
+            "long_dflash_bf16": measure_long_context(),
+            "dynamic_topk_bf16": measure_dynamic_topk(),
+            "decode_swap_bf16": measure_decode_swap()}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a pool of host processes, one BLAS thread
+# each. Workers draw their inputs with the same generator as the GPU run (or,
+# for the two workloads whose inputs the GPU run draws on the device, with the
+# host generator: the same shapes and distribution) and cache what they reuse.
+
+_WCACHE = {}
+_THREAD_ENV = {"OMP_NUM_THREADS": "1", "OPENBLAS_NUM_THREADS": "1", "MKL_NUM_THREADS": "1"}
+
+
+def host_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def start_host_pool():
+    """The pool of oracle workers. Call before this process touches the GPU:
+    the workers come from a fork server started here, never from a process
+    that has used the GPU."""
+    import multiprocessing as mp
+    saved = {k: os.environ.get(k) for k in _THREAD_ENV}
+    os.environ.update(_THREAD_ENV)
+    try:
+        ctx = mp.get_context("forkserver")
+        pool = ctx.Pool(host_workers(), initializer=_worker_init)
+        manager = ctx.Manager()
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    return pool, manager
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    _WCACHE["limits"] = threadpool_limits(1)
+
+
+def _f32(t):
+    return t.to(torch.float32).numpy()
+
+
+def _dflash_geom(name, li):
+    import oracle
+    cfg = synth.CONFIGS[name]
+    lay = cfg["layers"][li]
+    return oracle.DFlashGeom(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"], 0, 0,
+                             lay["is_causal"], lay["layer_type"], lay["window"])
+
+
+def _load(name):
+    """Inputs a worker keeps for a workload (whole tensors, or K/V only)."""
+    if name in _WCACHE:
+        return _WCACHE[name]
+    cfg = synth.CONFIGS[name]
+    if cfg["kind"] == "dflash":
+        g = _dflash_geom(name, 0)
+        Sq, Sk = g.Sq, g.Sk
+    else:
+        Sq, Sk = cfg["Sq"], cfg["Sk"]
+    B, H, KVH, D, dt, sc = (cfg[x] for x in ("B", "H", "KVH", "D", "dtype", "qkv_scale"))
+    if name == "long_dflash_bf16":   # K/V only; each unit draws its own query rows
+        kv = [_f32(synth.normal_tensor((B, Sk, KVH, D), 0, t, dt, sc))
+              for t in (synth.TID_K, synth.TID_V)]
+        val = (None, kv[0], kv[1])
+    else:
+        val = tuple(_f32(t) for t in synth.qkv(B, Sq, Sk, H, KVH, D, dt, seed=0, scale=sc))
+    if cfg["kind"] == "topk" and name != "decode_swap_bf16":
+        bias_t, pad2d = synth.topk_inputs(cfg, seed=0)
+        val = val + (_f32(bias_t).astype(np.float64), None if pad2d is None else pad2d.numpy())
+    _WCACHE[name] = val
+    return val
+
+
+def _preload(job):
+    """Draw a workload's inputs in this worker, then wait at the barrier so that
+    every worker takes exactly one preload job."""
+    name, barrier = job
+    if name != "decode_swap_bf16":
+        _load(name)
+    barrier.wait()
+    return os.getpid()
+
+
+def _tile_flops(band, Sk, D):
+    from oracle.blockmask import classify_tile_band
+    part, full = classify_tile_band(band, Sk)
+    rows = band.shape[0]
+    return 4 * D * rows * sum(min(128, Sk - 128 * int(t)) for t in list(part) + list(full))
+
+
+def oracle_unit(job):
+    """One unit of oracle work; returns (oracle seconds, counted flops). The
+    seconds cover the oracle's steps only (dense mask rows or top-k, tile
+    classification, attention), not the drawing of inputs."""
+    import oracle
+    name, li, b, h, qt = job
+    cfg = synth.CONFIGS[name]
+    D, H = cfg["D"], cfg["H"]
+    if cfg["kind"] == "dflash":
+        q, k, v = _load(name)
+        g = _dflash_geom(name, li)
+        r0, r1 = 128 * qt, min(128 * qt + 128, g.Sq)
+        sliced = q is None   # this unit's query rows only (batch entry b of a B = 1 workload)
+        if sliced:
+            q = _f32(synth.normal_rows((cfg["B"], g.Sq, H, D), 0, synth.TID_Q, b, r0, r1,
+                                       cfg["dtype"], cfg["qkv_scale"]))
+        t0 = time.perf_counter()
+        band = oracle.dflash_dense_mask(g, np.arange(r0, r1))
+        fl = _tile_flops(band, g.Sk, D)
+        if sliced:
+            oracle.attention_rows(q, k, v, 0, h, np.arange(r1 - r0), mask=band[None, None])
+        else:
+            oracle.attention_rows(q, k, v, b, h, np.arange(r0, r1), mask=g)
+        return time.perf_counter() - t0, fl
+    if name == "dynamic_topk_bf16":
+        q, k, v, bias, pad2d = _load(name)
+        Sq, Sk, G = cfg["Sq"], cfg["Sk"], H // cfg["KVH"]
+        r0, r1 = 128 * qt, min(128 * qt + 128, Sq)
+        t0 = time.perf_counter()
+        pre = oracle.normalize_premask(pad2d[b:b + 1], 1, Sk)
+        m = oracle.topk_keep_mask(bias[b:b + 1, h // G:h // G + 1], pre, Sk, cfg["topk"], "bf16")
+        fl = _tile_flops(np.broadcast_to(m[0, 0, 0], (r1 - r0, m.shape[-1])), Sk, D)
+        oracle.attention_rows(q[b:b + 1], k[b:b + 1], v[b:b + 1], 0, h, np.arange(r0, r1),
+                              mask=m, bias=bias[b:b + 1, h // G:h // G + 1])
+        return time.perf_counter() - t0, fl
+    # decode: one batch entry, all heads
+    B, KVH, Sk = cfg["B"], cfg["KVH"], cfg["Sk"]
+    K = synth.round_up_128(Sk)
+    q = _f32(synth.normal_rows((B, 1, H, D), 0, synth.TID_Q, b, 0, 1, "bf16"))
+    k = _f32(synth.normal_rows((B, Sk, KVH, D), 0, synth.TID_K, b, 0, Sk, "bf16"))
+    v = _f32(synth.normal_rows((B, Sk, KVH, D), 0, synth.TID_V, b, 0, Sk, "bf16"))
+    bias = _f32(synth.normal_rows((B, H, 1, K), 0, synth.TID_BIAS, b, 0, H, "bf16"))
+    bias = bias.astype(np.float64)
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        li = units % len(step.layers)
-        _, d = step.layers[li]
-        b = int(rng.integers(cfg["B"]))
-        h = int(rng.integers(cfg["H"]))
-        qt = int(rng.integers(d.Sq // 128))
-        og = oracle.DFlashGeom(d.ctx_len, d.num_blocks, d.block_size, d.ctx_per_block,
-                               d.ctx_end_offset, d.is_causal, d.layer_type, d.sliding_window)
-        rows = np.arange(128 * qt, 128 * qt + 128)
-        qb = synth.as_f64(q[b:b + 1])
-        kb = synth.as_f64(k[b:b + 1])
-        vb = synth.as_f64(v[b:b + 1])
-        oracle.attention_rows(qb, kb, vb, 0, h, rows, mask=og)
-        band = oracle.dflash_dense_mask(og, rows)
-        part, full = oracle.blockmask.classify_tile_band(band, og.Sk)
-        done_flops += 4 * cfg["D"] * 128 * 128 * (len(part) + len(full))
-        units += 1
-    el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{units} random (layer, b, h, 128-row query tile) units of the "
-                      f"{WORKLOAD} step, float64, {el:.1f} s"}
+    m = oracle.topk_keep_mask(bias, None, Sk, cfg["topk"], "bf16")
+    for hh in range(H):
+        oracle.attention_rows(q, k, v, 0, hh, [0], mask=m, bias=bias)
+    return time.perf_counter() - t0, 4 * D * H * Sk
+
+
+def _units(name):
+    """Every unit of a workload: (name, layer, b, h, query tile)."""
+    cfg = synth.CONFIGS[name]
+    if cfg["kind"] == "dflash":
+        nq = -(-_dflash_geom(name, 0).Sq // 128)
+        return [(name, li, b, h, qt) for li in range(len(cfg["layers"])) for b in range(cfg["B"])
+                for h in range(cfg["H"]) for qt in range(nq)]
+    if name == "dynamic_topk_bf16":
+        nq = -(-cfg["Sq"] // 128)
+        return [(name, 0, b, h, qt) for b in range(cfg["B"]) for h in range(cfg["H"])
+                for qt in range(nq)]
+    return [(name, 0, b, 0, 0) for b in range(cfg["B"])]
+
+
+UNIT_DESC = {"tiny_dflash_fp32": "(b, h, 128-row query tile)",
+             "dflash_train_bf16": "(layer, b, h, 128-row query tile)",
+             "long_dflash_bf16": "(b, h, 128-row query tile)",
+             "dynamic_topk_bf16": "(b, h, 128-row query tile) incl. its top-k row",
+             "decode_swap_bf16": "(b): top-k of 32 head rows + 32 one-row attentions"}
+
+
+def cpu_baseline(pool, manager, budgets=None):
+    """The fp64 oracle, as it stands, on a bounded random sample of every
+    workload's units, run by the pool in waves of one unit per worker. Per
+    workload: units done / total, wall seconds of the waves (inputs drawn
+    beforehand, except the decode units, which draw their batch entry's K/V),
+    the oracle's own seconds summed over units, and the full workload's oracle
+    time at this core count extrapolated from the sample. `value` is the
+    training-shape step's counted TFLOP/s over that workload's wall time."""
+    W = host_workers()
+    budgets = budgets or {"tiny_dflash_fp32": 0.0, "dflash_train_bf16": 8.0,
+                          "long_dflash_bf16": 5.0, "dynamic_topk_bf16": 5.0,
+                          "decode_swap_bf16": 5.0}
+    rng = np.random.default_rng(0)
+    out = {}
+    for name, budget in budgets.items():
+        units = _units(name)
+        order = rng.permutation(len(units))
+        barrier = manager.Barrier(W)
+        pool.map(_preload, [(name, barrier)] * W, chunksize=1)
+        done = []
+        t0 = time.perf_counter()
+        i = 0
+        while i < len(units) and (not done or time.perf_counter() - t0 < budget):
+            done += pool.map(oracle_unit, [units[j] for j in order[i:i + W]], chunksize=1)
+            i += W
+        wall = time.perf_counter() - t0
+        osec = sum(s for s, _ in done)
+        fl = sum(f for _, f in done)
+        out[name] = {"unit": UNIT_DESC[name], "units_done": len(done), "units_total": len(units),
+                     "wall_s": wall, "oracle_s": osec,
+                     "est_full_workload_s": len(units) * wall / len(done),
+                     "counted_TFLOP/s": fl / wall / 1e12}
+    main = out[WORKLOAD]
+    return {"value": main["counted_TFLOP/s"], "unit": "TFLOP/s", "cores": W, "kind": "oracle",
+            "sample": f"{main['units_done']} random {UNIT_DESC[WORKLOAD]} units of the "
+                      f"{WORKLOAD} step on {W} one-thread worker processes, float64, "
+                      f"{main['wall_s']:.1f} s wall; per-workload samples under 'configs'",
+            "configs": out}
 
 
 def main():
@@ -439,6 +753,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mask-build", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' full-size lines (long context, dynamic "
+                         "top-k, decode, tiny)")
     ap.add_argument("--components", action="store_true",
                     help="also time the other workloads' kernels (top-k, builders, attention)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -452,6 +769,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
               "is measured on a single MI355X; sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
+    pool = manager = None
+    if not (args.no_cpu_baseline or args.copy_probe or args.backward_only or args.only):
+        pool, manager = start_host_pool()   # before this process touches the GPU
     torch.cuda.init()
     if args.copy_probe:
         copy_probe()
@@ -513,10 +833,16 @@ def main():
     }
     if not args.no_mask_build:
         line["mask_build"] = measure_mask_build()
+    if not args.no_configs:
+        del step
+        line["configs"] = measure_configs()
     if args.components:
         line["components"] = measure_components()
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(step)
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(pool, manager)
+        pool.close()
+        pool.join()
+        manager.shutdown()
     print(json.dumps(line), flush=True)
 
 

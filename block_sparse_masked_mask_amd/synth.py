@@ -36,6 +36,31 @@ def normal(shape, seed, tensor_id, scale=1.0):
     return out.reshape(shape)
 
 
+def normal_range(seed, tensor_id, lo, hi, scale=1.0):
+    """float32 elements [lo, hi) of the flat stream that `normal` lays out (the
+    same values; only the chunks that overlap the range are drawn, each up to
+    the range's end)."""
+    out = np.empty(max(0, hi - lo), np.float32)
+    for c in range(lo // CHUNK, (hi - 1) // CHUNK + 1 if hi > lo else lo // CHUNK):
+        base = c * CHUNK
+        a, b = max(lo, base), min(hi, base + CHUNK)
+        rng = np.random.default_rng([seed, tensor_id, c])
+        out[a - lo:b - lo] = rng.standard_normal(b - base, dtype=np.float32)[a - base:]
+    if scale != 1.0:
+        out *= np.float32(scale)
+    return out
+
+
+def normal_rows(shape, seed, tensor_id, b, r0, r1, dtype, scale=1.0):
+    """Rows [r0, r1) of batch b of the (B, S, X, Y) tensor normal_tensor would
+    make, as a (1, r1 - r0, X, Y) tensor in the storage dtype."""
+    B, S, X, Y = shape
+    row = X * Y
+    lo = (b * S + r0) * row
+    arr = normal_range(seed, tensor_id, lo, lo + (r1 - r0) * row, scale)
+    return storage(arr.reshape(1, r1 - r0, X, Y), dtype)
+
+
 def storage(arr, dtype):
     """torch CPU tensor in the storage dtype ('bf16' or 'f32')."""
     t = torch.from_numpy(np.ascontiguousarray(arr))
