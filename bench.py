@@ -224,9 +224,32 @@ def measure_backward():
     return out
 
 
+def measure_one_head():
+    """The DFlash training geometry with MHA (H = KVH = 32, so no head pairs):
+    attention on the one-head-per-workgroup kernel, TFLOP/s on kept tiles."""
+    out = {}
+    cfg = synth.CONFIGS["dflash_train_bf16"]
+    for lay in cfg["layers"]:
+        d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
+                       is_causal=lay["is_causal"], layer_type=lay["layer_type"],
+                       sliding_window=lay["window"])
+        q, k, v = [t.cuda() for t in synth.qkv(cfg["B"], d.Sq, d.Sk, 32, 32, cfg["D"], "bf16",
+                                               seed=0, scale=cfg["qkv_scale"])]
+        geom = bsm.geometry_of(q, k)
+        bm = bsm.build_block_mask(geom, pred=d)
+        fl = counted_flops(bm, geom)
+        o = torch.empty_like(q)
+        ms = _time_ms(lambda: bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, out=o), reps=5)
+        out[f"attn_one_head/dflash_train_mha_bf16/{lay['name']}_ms"] = ms
+        out[f"attn_one_head/dflash_train_mha_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+        del q, k, v, o
+    return out
+
+
 def measure_components():
     """Per-kernel times of the other workloads (parity cases, not the headline)."""
     out = measure_backward()
+    out.update(measure_one_head())
     # DFlash block masks from the predicate (integer work, output only)
     for name in ("dflash_train_bf16", "long_dflash_bf16"):
         cfg = synth.CONFIGS[name]
@@ -762,7 +785,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the DFlash training-shape backward and print it")
-    ap.add_argument("--only", choices=["decode", "dynamic", "infer", "varlen", "components"],
+    ap.add_argument("--only", choices=["decode", "dynamic", "infer", "varlen", "one_head",
+                                       "components"],
                     help="only time one group of the other workloads' kernels and print it")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -782,7 +806,7 @@ def main():
     if args.only:
         fn = {"decode": measure_decode, "dynamic": measure_dynamic,
               "infer": measure_dflash_infer, "varlen": measure_varlen,
-              "components": measure_components}[args.only]
+              "one_head": measure_one_head, "components": measure_components}[args.only]
         print(json.dumps(fn()), flush=True)
         return
     step = Step()

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsm.so")
 
 SOURCES = ["bsm_api.cpp", "block_mask.hip", "topk.hip", "key_list.hip", "attn.hip", "attn_v2.hip",
-           "attn_gather.hip", "attn_group.hip", "attn_bwd.hip", "attn_bwd_mfma.hip", "varlen.hip",
+           "attn_gather.hip", "attn_group.hip", "attn_bwd.hip", "attn_bwd_mfma.hip", "varlen.hip", "attn_h1.hip",
            "noalloc.hip"]
 ARCH = os.environ.get("BSM_OFFLOAD_ARCH", "gfx950")
 

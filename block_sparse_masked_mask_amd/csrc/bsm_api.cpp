@@ -800,6 +800,8 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
       if (staged_aux_applies(p) && a->workspace_bytes >= staged_aux_bytes(p))
         he = launch_aux_combine(p, a->workspace, stream);
       if (he == hipSuccess) he = launch_attn_bf16_v2(p, D, stream);
+    } else if (attn_h1_applies(p, D)) {
+      he = launch_attn_bf16_h1(p, D, stream);
     } else {
       he = launch_attn_bf16(p, D, stream);
     }

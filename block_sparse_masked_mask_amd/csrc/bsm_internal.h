@@ -222,6 +222,10 @@ struct WorkOrder {
 };
 hipError_t launch_attn_bf16_v2(const AttnParams& p, int D, hipStream_t s,
                                const WorkOrder* order = nullptr);
+// bf16, one head per workgroup, 64-key sub-tiles, two workgroups per CU (no
+// mask tensor, no bias, not packed)
+bool attn_h1_applies(const AttnParams& p, int D);
+hipError_t launch_attn_bf16_h1(const AttnParams& p, int D, hipStream_t s);
 // backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
 hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);

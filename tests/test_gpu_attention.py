@@ -356,3 +356,28 @@ def test_huge_and_infinite_biases(dt, Sq, bq):
             assert (rel <= 1e-6).all(), f"LSE of saturated rows, rel err {rel.max():.2e}"
             small = ~huge
             assert_close(lse[b, h][small], want_l[small], dt, f"extreme LSE b={b} h={h}")
+
+
+ONE_HEAD_CASES = [
+    # (H, KVH, D, DFlash geometry or None for no mask, Sq, Sk without a mask, block mask)
+    (4, 4, 128, dict(ctx_len=260, num_blocks=13, block_size=16), 0, 0, True),  # MHA, ragged
+    (4, 4, 128, dict(ctx_len=260, num_blocks=13, block_size=16), 0, 0, False),
+    (6, 2, 64, dict(ctx_len=260, num_blocks=13, block_size=16, layer_type="sliding",
+                    sliding_window=100), 0, 0, True),                          # G = 3
+    (6, 2, 64, dict(ctx_len=260, num_blocks=13, block_size=16, layer_type="sliding",
+                    sliding_window=100), 0, 0, False),
+    (3, 1, 128, dict(ctx_len=999, num_blocks=3, block_size=200, is_causal=True), 0, 0, True),
+    (2, 2, 128, None, 300, 777, False),                                        # MHA, no mask
+]
+
+
+@pytest.mark.parametrize("H,KVH,D,case,Sq,Sk,with_bm", ONE_HEAD_CASES)
+def test_odd_group_sizes(H, KVH, D, case, Sq, Sk, with_bm):
+    """Odd head groups (MHA, G = 3) without a mask tensor or bias: one head per
+    workgroup with 64-key sub-tiles; several query and key tiles, ragged ends."""
+    d = bsm.DFlash(**case) if case is not None else None
+    if d is not None:
+        Sq, Sk = d.Sq, d.Sk
+    q, k, v = cuda(*synth.qkv(2, Sq, Sk, H, KVH, D, "bf16", seed=60 + H + D))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d) if with_bm else None
+    _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what=f"G={H // KVH} D={D} {case}")
