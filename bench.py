@@ -221,6 +221,23 @@ def measure_backward():
         out[f"attn_bwd/dflash_train_bf16/{lay['name']}_ms"] = ms
         out[f"attn_bwd/dflash_train_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
         del q, k, v, o, do
+    # the dynamic-mask workload: top-k mask, bias per KV head broadcast over
+    # queries, and its gradient dbias
+    cfg = synth.CONFIGS["dynamic_topk_bf16"]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = [t.cuda() for t in synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0)]
+    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    geom = bsm.geometry_of(q, k)
+    bm = bsm.build_block_mask(geom, mask=mask)
+    o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm, return_lse=True)
+    do = synth.normal_tensor(tuple(q.shape), 0, synth.TID_DOUT, "bf16").cuda()
+    ms = _time_ms(lambda: bsm.masked_attn_bwd(q, k, v, o, do, lse, mask=mask, bias=bias,
+                                              block_mask=bm, need_dbias=True), reps=3)
+    fl = 2.5 * counted_flops(bm, geom)
+    out["attn_bwd/dynamic_topk_bf16_dbias_ms"] = ms
+    out["attn_bwd/dynamic_topk_bf16_dbias_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+    del q, k, v, o, do
     return out
 
 

@@ -1,6 +1,6 @@
-// Masked attention backward on the bf16 matrix cores (gfx950), D = 128, for
-// calls without bias and without a dense mask (no mask, or the DFlash
-// predicate): the training path of the DFlash layers.
+// Masked attention backward on the bf16 matrix cores (gfx950), D = 128: the
+// training path of the DFlash layers (no mask or the DFlash predicate) and of
+// masked calls with a dense bool mask and / or an additive bias, with dbias.
 //
 // Same gradients as the generic kernels (attn_bwd.hip; flash-sparse-attention
 // PR #190, Changes: mha_bwd): P = exp(s - LSE) on kept keys, dS = P (dP - Delta)
@@ -19,8 +19,15 @@
 //    Per 32-row block: S = Q K^T and dP = dO V^T with the wave's K and V rows
 //    held in registers and query rows permuted the same way, then
 //    dV^T += dO^T P and dK^T += Q^T dS with transposed LDS reads of dO and Q.
-//    Partial tiles of the predicate use a keep-bit table of the query tile
-//    built in LDS (one 64-key word per row and half tile).
+//    Partial tiles use a keep-bit table of the query tile built in LDS (one
+//    64-key word per row and half tile) from the predicate or the mask bytes.
+//  * Bias: added to the scores in log2 units (bias_log2) wherever P is formed.
+//    dbias = dS summed over the dims where the bias broadcasts: the dK / dV
+//    workgroup holds every (head of its group, query) of its keys, so a bias
+//    broadcast over queries is summed per key in a register and added once
+//    per target row (float atomics only across workgroups: batches or KV
+//    groups sharing a bias row); a bias per query takes one atomic add per
+//    (query, key) and head.
 #include <math.h>
 
 #include "attn_common.h"
@@ -117,6 +124,8 @@ __device__ inline bf16x8 pack8(const float* x) {
 
 // ---------------------------------------------------------------- dQ
 
+// AUX: the call has a dense mask and / or a bias (their code compiles out otherwise)
+template <bool AUX>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
   const AttnParams& f = P.f;
   __shared__ __align__(1024) Tile sk;
@@ -153,6 +162,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
              : -INFINITY;
   const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
   const bool live = lse2 != -INFINITY;  // rows with no kept key have zero gradients
+  const uint8_t* mrow = (AUX && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
+  const uint16_t* brow = (AUX && f.has_bias && qvalid)
+      ? reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, q)) : nullptr;
   RowIv32 iv{0, 0, 0, 0};
   if (f.mask_kind == 1) {
     const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
@@ -194,18 +206,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
         const int kb = k0 + 32 * c + 16 * sb + 8 * hh;
         uint32_t bits = 0xFFu;
         if (test) {
-          // partial tiles of the predicate test the row's intervals; keys past
-          // Sk and rows past Sq keep nothing
+          // partial tiles test the row's predicate intervals or mask bytes;
+          // keys past Sk and rows past Sq keep nothing
           if (!full && f.mask_kind == 1)
             bits = range_bits(iv.lo1, iv.hi1, kb) | range_bits(iv.lo2, iv.hi2, kb);
+          if (AUX && !full && f.mask_kind == 2)
+            bits = mrow ? byte_bits8(*reinterpret_cast<const uint2*>(mrow + kb)) : 0u;
           bits &= range_bits(0, f.Sk, kb);
           if (!qvalid) bits = 0;
         }
+        float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (AUX && brow) bias8_log2(brow + kb, bv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
           const float pr = (live && ((bits >> e) & 1u))
-                               ? __builtin_amdgcn_exp2f(st[u] * f.scale_log2 - lse2)
+                               ? __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, bv[e] - lse2))
                                : 0.f;
           ds[u] = pr * (dpt[u] - delta);
         }
@@ -274,6 +290,7 @@ struct DqOffs {
   }
 };
 
+template <bool AUX>
 __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWork) {
   const AttnParams& f = P.f;
   __shared__ __align__(1024) Tiles<kD> buf0;
@@ -330,6 +347,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
              : -INFINITY;
   const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
   const bool live = lse2 != -INFINITY;
+  const uint8_t* mrow = (AUX && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
+  const uint16_t* brow = (AUX && f.has_bias && qvalid)
+      ? reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, q)) : nullptr;
   RowIv32 iv{0, 0, 0, 0};
   if (f.mask_kind == 1) {
     const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
@@ -399,15 +419,19 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
         if (test) {
           if (!full_cur && f.mask_kind == 1)
             bits = range_bits(iv.lo1, iv.hi1, kbk) | range_bits(iv.lo2, iv.hi2, kbk);
+          if (AUX && !full_cur && f.mask_kind == 2)
+            bits = mrow ? byte_bits8(*reinterpret_cast<const uint2*>(mrow + kbk)) : 0u;
           bits &= range_bits(0, f.Sk, kbk);
           if (!qvalid) bits = 0;
         }
+        float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (AUX && brow) bias8_log2(brow + kbk, bv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
           // computed, then selected: a branch per element would split the
           // block the MFMAs overlap with
-          const float ex = __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, -lse2));
+          const float ex = __builtin_amdgcn_exp2f(fmaf(st[u], f.scale_log2, bv[e] - lse2));
           const float pr = (live && ((bits >> e) & 1u)) ? ex : 0.f;
           ds[u] = pr * (dpt[u] - delta);
         }
@@ -511,6 +535,7 @@ struct DkdvOffs {
   }
 };
 
+template <bool AUX>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) {
   const AttnParams& f = P.f;
   // two slots: Q tile (.k) and dO tile (.v) of a visited (head, query tile), with
@@ -520,6 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   __shared__ float s_lse2[2][kTile];
   __shared__ float s_delta[2][kTile];
   __shared__ uint64_t s_keep[2][kTile][2];  // keep bits: row, 64-key half
+  __shared__ float s_bias[2][kTile];        // a query-broadcast bias row (log2 units)
   // key tile major, lowest key tile first: under causal-like masks the low key
   // tiles are seen by the most query tiles, so the longest work items start first
   const int kt = blockIdx.x / (f.B * f.KVH);
@@ -603,7 +629,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
       s_lse2[sl][tid] = l2;
       s_delta[sl][tid] = dl;
     }
-    if (cls == 1 || test_k) {  // keep bits: row tid / 2, keys of half tid % 2
+    if (AUX && f.has_bias && f.bias.q_bcast && tid < kTile) {
+      const uint16_t* br = reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, 0));
+      s_bias[sl][tid] = bias_log2(bf16_to_f32(br[k0 + tid]));
+    }
+    if (AUX && f.mask_kind == 2 && (cls == 1 || test_k)) {
+      // keep bits from the mask bytes of row tid / 2, keys of half tid % 2
+      const int r = tid >> 1, half = tid & 1;
+      const int q = q0 + r;
+      uint64_t bits = 0;
+      if (q < f.Sq) {
+        const uint8_t* mr = aux_row(f.mask, 1, b, h, f.G, q) + k0 + 64 * half;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t kb = k0 + 64 * half + 8 * j;
+          const uint32_t mb = cls == 1 ? byte_bits8(*reinterpret_cast<const uint2*>(mr + 8 * j))
+                                       : 0xFFu;
+          bits |= (uint64_t)(mb & range_bits(0, f.Sk, kb)) << (8 * j);
+        }
+      }
+      s_keep[sl][r][half] = bits;
+    } else if (cls == 1 || test_k) {  // keep bits: row tid / 2, keys of half tid % 2
       const int r = tid >> 1, half = tid & 1;
       const int q = q0 + r;
       uint64_t bits = 0;
@@ -638,6 +684,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     if (listed) return it + 1 < nvis ? listed_visit(it + 1, cls) : end;
     return next_visit(pos + 1, cls);
   };
+  // dbias of a query-broadcast bias: this lane's key summed over the rows of
+  // the visits whose heads share one bias row (db_h: such a head, -1: none)
+  float dbacc = 0.f;
+  int db_h = -1;
+  auto db_flush = [&]() {
+    const float t = dbacc + __shfl_xor(dbacc, 32, 64);
+    if (db_h >= 0 && hh == 0 && kvalid)
+      atomicAdd(reinterpret_cast<float*>(const_cast<uint8_t*>(aux_row(P.dbias, 4, b, db_h, f.G, 0))) +
+                    key, t);
+    dbacc = 0.f;
+  };
+  const bool db_rows = AUX && P.dbias_acc != nullptr && !f.bias.q_bcast;
   int cls = 0;
   int pos = listed ? (nvis > 0 ? listed_visit(0, cls) : end) : next_visit(0, cls);
   if (pos < end) prepare(0, pos, cls);
@@ -649,6 +707,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     const int npos = following(it, pos, ncls);
     if (npos < end) prepare(sl ^ 1, npos, ncls);
     const bool test = cls == 1 || test_k;
+    const int vh = kvh * f.G + pos / f.nQ;  // this visit's head and first row
+    const int vq0 = (pos % f.nQ) * kTile;
+    if (AUX && P.dbias_acc && f.bias.q_bcast) {
+      if (db_h >= 0 && head_index(P.dbias.h_mode, vh, f.G) != head_index(P.dbias.h_mode, db_h, f.G))
+        db_flush();
+      db_h = vh;
+    }
     const char* tq = reinterpret_cast<const char*>(buf[sl].k);
     const char* tdo = reinterpret_cast<const char*>(buf[sl].v);
     auto ld8 = [](const char* a) { return *reinterpret_cast<const bf16x8*>(a); };
@@ -717,13 +782,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
           for (int e = 0; e < 8; ++e)
             bits |= (uint32_t)((s_keep[sl][r0 + e][kk >> 6] >> (kk & 63)) & 1u) << e;
         }
+        // the bias of (row, this lane's key) in log2 units
+        float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (AUX && f.has_bias) {
+          if (f.bias.q_bcast) {
+            const float bk = s_bias[sl][32 * w + n];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = bk;
+          } else if (kvalid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int q = vq0 + r0 + e;
+              if (q < f.Sq)
+                bv[e] = bias_log2(bf16_to_f32(reinterpret_cast<const uint16_t*>(
+                    aux_row(f.bias, 2, b, vh, f.G, q))[key]));
+            }
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * st + e;
-          const float ex = __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, -l2[e]));
+          const float ex = __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, bv[e] - l2[e]));
           const float pr = (((bits >> e) & 1u) && l2[e] != -INFINITY) ? ex : 0.f;
           pv[u] = pr;
           dsv[u] = pr * (dp[u] - dl[e]);
+        }
+        if (AUX && P.dbias_acc) {
+          if (!db_rows) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dbacc += dsv[8 * st + e];
+          } else if (kvalid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int q = vq0 + r0 + e;
+              if (q < f.Sq && dsv[8 * st + e] != 0.f)
+                atomicAdd(reinterpret_cast<float*>(const_cast<uint8_t*>(
+                              aux_row(P.dbias, 4, b, vh, f.G, q))) + key,
+                          dsv[8 * st + e]);
+            }
+          }
         }
       }
       const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
@@ -746,6 +843,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     pos = npos;
     cls = ncls;
   }
+  if (AUX && P.dbias_acc && f.bias.q_bcast) db_flush();
   // dK^T / dV^T accumulators: lane holds d = 32 dc + 8 (r / 4) + 4 hh + r % 4 of its key
   if (kvalid) {
     __bf16* ko = reinterpret_cast<__bf16*>(P.dk) + (int64_t)b * P.dk_sb + (int64_t)key * P.dk_sk +
@@ -773,7 +871,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
 
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D) {
   // the dK / dV kernel's tile loads use 32-bit offsets within one (b, head)
-  return D == kD && !p.f.has_bias && p.f.mask_kind != 2 && !p.dbias_acc &&
+  return D == kD && !p.f.varlen && (p.f.has_bias || !p.dbias_acc) &&
          (int64_t)p.f.Sq * p.f.q_sq * 2 < ((int64_t)1 << 31) &&
          (int64_t)p.f.Sq * p.do_sq * 2 < ((int64_t)1 << 31);
 }
@@ -787,15 +885,24 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
   const bool pair = f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1) && !f.varlen &&
                     (int64_t)f.Sk * f.k_sk * 2 < ((int64_t)1 << 31) &&
                     (int64_t)f.Sk * f.v_sk * 2 < ((int64_t)1 << 31);
+  const bool aux = f.has_bias || f.mask_kind == 2;
   if (nq > 0) {
-    if (pair) {
-      const int nWork = (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
-      hipLaunchKernelGGL(k_bwd_dq_pair, dim3(nWork), dim3(512), 0, s, p, nWork);
-    } else {
-      hipLaunchKernelGGL(k_bwd_dq_mfma, dim3(nq), dim3(kThreads), 0, s, p);
-    }
+    const int nWork = (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
+    if (pair && aux)
+      hipLaunchKernelGGL(k_bwd_dq_pair<true>, dim3(nWork), dim3(512), 0, s, p, nWork);
+    else if (pair)
+      hipLaunchKernelGGL(k_bwd_dq_pair<false>, dim3(nWork), dim3(512), 0, s, p, nWork);
+    else if (aux)
+      hipLaunchKernelGGL(k_bwd_dq_mfma<true>, dim3(nq), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_bwd_dq_mfma<false>, dim3(nq), dim3(kThreads), 0, s, p);
   }
-  if (nk > 0) hipLaunchKernelGGL(k_bwd_dkdv_mfma, dim3(nk), dim3(kThreads), 0, s, p);
+  if (nk > 0) {
+    if (aux)
+      hipLaunchKernelGGL(k_bwd_dkdv_mfma<true>, dim3(nk), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_bwd_dkdv_mfma<false>, dim3(nk), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

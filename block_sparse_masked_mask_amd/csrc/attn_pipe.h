@@ -186,6 +186,26 @@ __device__ inline uint32_t range_bits(int lo, int hi, int kb) {
   return ((1u << c) - 1u) & ~((1u << a) - 1u);
 }
 
+// Keep bits of 8 mask bytes (nonzero = keep), byte e -> bit e.
+__device__ inline uint32_t byte_bits8(uint2 mb) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t byte = ((e < 4 ? mb.x : mb.y) >> (8 * (e & 3))) & 0xFFu;
+    bits |= (byte != 0u ? 1u : 0u) << e;
+  }
+  return bits;
+}
+
+// 8 consecutive bf16 bias values (16-byte aligned) in log2 units, saturated
+// like every attention kernel reads a bias (bias_log2).
+__device__ inline void bias8_log2(const uint16_t* p, float (&out)[8]) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = bias_log2(bf16_to_f32((uint16_t)(wv[e >> 1] >> (16 * (e & 1)))));
+}
+
 // max of x over lanes l and l ^ 32 (the two lanes that share a query row)
 __device__ inline float max_pair(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),

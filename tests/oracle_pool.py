@@ -181,3 +181,30 @@ def topk_mask_rows(job):
     cfg, bias, pad2d = _CACHE[key]
     sub = dict(cfg, B=1)
     return topk_mask(sub, bias[b:b + 1], None if pad2d is None else pad2d[b:b + 1])
+
+
+def _dout(name, shape, seed, dtype):
+    key = ("dout", name, seed)
+    if key not in _CACHE:
+        from block_sparse_masked_mask_amd import synth
+        _CACHE[key] = _f32(synth.normal_tensor(tuple(shape), seed, synth.TID_DOUT, dtype))
+    return _CACHE[key]
+
+
+def bwd_head(job):
+    """(name, layer index, b, h, dO seed) -> the oracle's dQ (Sq, D), dK and dV
+    (Sk, D) of head h of batch b, and its dS summed over queries (Sk,), under
+    the workload's own mask (DFlash rule, or the oracle's top-k and the bias)."""
+    from oracle.attention_bwd import head_grads
+    from block_sparse_masked_mask_amd import synth
+    name, li, b, h, seed = job
+    cfg = synth.CONFIGS[name]
+    if cfg["kind"] == "dflash":
+        q, k, v, g = _dflash(name, li)
+        mask, bias = g, None
+    else:
+        q, k, v, bias, mask = _topk(name)
+    do = _dout(name, q.shape, seed, cfg["dtype"])
+    dQ, dK, dV, dS = head_grads(q, k, v, do, b, h, mask=mask, bias=bias)
+    return dQ, dK, dV, dS.sum(axis=0)
+

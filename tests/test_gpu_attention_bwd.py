@@ -11,8 +11,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle_pool
 from gpu_helpers import bsm, cuda, oracle_geom, oracle_topk_mask, say, synth
-from oracle.attention_bwd import attention_bwd, group_grads
+from oracle.attention_bwd import attention_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +93,7 @@ def test_small_dflash(case, D, dt):
     _check_full(q, k, v, dt, pred=d, bm=bm, seed=1, what=f"dflash {case} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("mshape,bshape", [
     ((2, 4, 150, 256), (2, 4, 150, 256)),   # full bias: dbias = dS
@@ -100,8 +102,10 @@ def test_small_dflash(case, D, dt):
     (None, (1, 1, 1, 256)),                 # one bias row for everything
     (None, None),
 ])
-def test_dense_mask_and_bias(dt, mshape, bshape):
-    B, Sq, Sk, H, KVH, D = 2, 150, 200, 4, 2, 64
+def test_dense_mask_and_bias(dt, mshape, bshape, D):
+    """Dense masks and biases of every broadcast shape, with dbias; bf16 at
+    D = 128 takes the matrix-core kernels, the rest the generic ones."""
+    B, Sq, Sk, H, KVH = 2, 150, 200, 4, 2
     q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, dt, seed=2))
     mask = bias = None
     if mshape is not None:
@@ -140,24 +144,60 @@ def test_decode_swap(with_mask):
                 what="swap")
 
 
-def test_dflash_train_layer_sampled():
-    """The DFlash training shape's sliding layer, one (b, KV group) checked in
-    full against the oracle."""
-    cfg = synth.CONFIGS["dflash_train_bf16"]
-    layer = cfg["layers"][1]
+def _check_groups(name, li, groups, dq, dk, dv, dbias=None, seed=5, what=""):
+    """(b, KV head) groups of a full-size backward against the oracle, head by
+    head on the host pool: dQ of the G heads, dK / dV summed over them, and
+    (with a bias per KV head, broadcast over queries) dbias."""
+    cfg = synth.CONFIGS[name]
+    G = cfg["H"] // cfg["KVH"]
+    jobs = [(name, li, b, kvh * G + g, seed) for b, kvh in groups for g in range(G)]
+    res = oracle_pool.run(oracle_pool.bwd_head, jobs)
+    for i, (b, kvh) in enumerate(groups):
+        part = res[i * G:(i + 1) * G]
+        say("backward group", what, b, kvh)
+        rq = np.stack([r[0] for r in part], axis=1)
+        rk = sum(r[1] for r in part)
+        rv = sum(r[2] for r in part)
+        _close(dq[b, :, kvh * G:(kvh + 1) * G].float().cpu().numpy(), rq, "bf16", f"{what} dq")
+        _close(dk[b, :, kvh].float().cpu().numpy(), rk, "bf16", f"{what} dk")
+        _close(dv[b, :, kvh].float().cpu().numpy(), rv, "bf16", f"{what} dv")
+        if dbias is not None:
+            rdb = sum(r[3] for r in part)
+            _close(dbias[b, kvh, 0].float().cpu().numpy(), rdb, "bf16", f"{what} dbias")
+
+
+@pytest.mark.parametrize("li", [0, 1], ids=["full", "sliding"])
+def test_dflash_train_backward_groups(li):
+    """The DFlash training shape, each layer: three (b, KV group)s of the
+    backward checked in full against the oracle."""
+    name = "dflash_train_bf16"
+    cfg = synth.CONFIGS[name]
+    layer = cfg["layers"][li]
     d = bsm.DFlash(cfg["ctx_len"], cfg["num_blocks"], cfg["block_size"],
                    is_causal=layer["is_causal"], layer_type=layer["layer_type"],
                    sliding_window=layer["window"])
     q, k, v = cuda(*synth.qkv(cfg["B"], d.Sq, d.Sk, cfg["H"], cfg["KVH"], cfg["D"], "bf16",
                               seed=0, scale=cfg["qkv_scale"]))
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
-    do, dq, dk, dv, _ = _run(q, k, v, "bf16", pred=d, bm=bm, seed=5, what="dflash train sliding")
-    G = cfg["H"] // cfg["KVH"]
-    for b, kvh in ((1, 5),):
-        say("oracle group", b, kvh)
-        rq, rk, rv = group_grads(synth.as_f64(q[b:b + 1]), synth.as_f64(k[b:b + 1]),
-                                 synth.as_f64(v[b:b + 1]), synth.as_f64(do[b:b + 1]), 0, kvh,
-                                 mask=oracle_geom(d))
-        _close(dq[b, :, kvh * G:(kvh + 1) * G].float().cpu().numpy(), rq, "bf16", "dq")
-        _close(dk[b, :, kvh].float().cpu().numpy(), rk, "bf16", "dk")
-        _close(dv[b, :, kvh].float().cpu().numpy(), rv, "bf16", "dv")
+    do, dq, dk, dv, _ = _run(q, k, v, "bf16", pred=d, bm=bm, seed=5,
+                             what=f"dflash train {layer['name']}")
+    del q, k, v, do
+    _check_groups(name, li, [(0, 0), (1, 5), (0, 7)], dq, dk, dv, what=layer["name"])
+
+
+def test_dynamic_topk_backward_groups():
+    """The dynamic-mask workload (Sq = Sk = 8000, top-2048 of a bias per KV
+    head broadcast over queries, 2D padding): backward with dbias; two
+    (b, KV group)s in full against the oracle (its own top-k mask), dbias of
+    those groups summed over their heads and queries."""
+    name = "dynamic_topk_bf16"
+    cfg = synth.CONFIGS[name]
+    B, H, KVH, D, Sq, Sk = (cfg[x] for x in ("B", "H", "KVH", "D", "Sq", "Sk"))
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=0))
+    bias, pad2d = [t.cuda() for t in synth.topk_inputs(cfg, seed=0)]
+    mask = bsm.create_mask(bias, pad2d, B, Sq, Sk, cfg["topk"])
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    do, dq, dk, dv, dbias = _run(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, need_dbias=True,
+                                 seed=5, what="dynamic top-k")
+    del q, k, v, do
+    _check_groups(name, 0, [(0, 1), (1, 3)], dq, dk, dv, dbias, what="dynamic")
