@@ -46,8 +46,9 @@ Modules:
                 oracle, torch autograd in float64, broadcast dbias reductions).
   normalize  -- 2D/4D pre-mask normalisation and key-length rounding.
   varlen     -- packed variable-length sequences: pad / unpad, per-sequence
-                DFlash geometry, packed attention and its block mask (pinned:
-                worked example, round trip, padded-batch equivalences).
+                DFlash geometry, packed attention, its gradients and its
+                block mask (pinned: worked example, round trip, padded-batch
+                equivalences, finite differences of the packed forward).
   keylist    -- kept-key list of a dense mask over at most 32 query rows, with
                 a bit per row (pinned: hand-worked example, round trip,
                 top-k count invariant, attention over the gathered keys).
@@ -67,5 +68,5 @@ from .attention import attention_rows, attention_full  # noqa: F401
 from .attention_bwd import attention_bwd, group_grads, head_grads  # noqa: F401
 from .normalize import round_multiple, normalize_premask  # noqa: F401
 from .keylist import key_list, expand_key_list  # noqa: F401
-from .varlen import (attention_varlen, block_mask_varlen, dflash_varlen_geoms,  # noqa: F401
-                     pad, unpad)
+from .varlen import (attention_varlen, attention_varlen_bwd, block_mask_varlen,  # noqa: F401
+                     dflash_varlen_geoms, pad, unpad)

@@ -25,6 +25,7 @@ layer's causality and window shared by every sequence.
 import numpy as np
 
 from .attention import attention_full
+from .attention_bwd import attention_bwd
 from .blockmask import TILE, classify_tiles
 from .dflash import DFlashGeom, dflash_dense_mask
 
@@ -85,6 +86,31 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale=None, geoms=None):
         o[q0:q1] = ob[0]
         lse[:, q0:q1] = lb[0]
     return o, lse
+
+
+def attention_varlen_bwd(q, k, v, dout, cu_q, cu_k, scale=None, geoms=None):
+    """dQ (total_q, H, D), dK and dV (total_k, KVH, D) of attention_varlen for
+    dL/dO = dout: attention_bwd applied to each sequence alone, so a sequence's
+    keys get gradient from its own queries only (zero if it has none)."""
+    q = np.asarray(q, np.float64)
+    total_q, H, D = q.shape
+    total_k, KVH = k.shape[0], k.shape[1]
+    dq = np.zeros((total_q, H, D))
+    dk = np.zeros((total_k, KVH, D))
+    dv = np.zeros((total_k, KVH, D))
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        mask = None if geoms is None else geoms[b]
+        gq, gk, gv, _ = attention_bwd(q[None, q0:q1], np.asarray(k[None, k0:k1], np.float64),
+                                      np.asarray(v[None, k0:k1], np.float64),
+                                      np.asarray(dout[None, q0:q1], np.float64), scale=scale,
+                                      mask=mask)
+        dq[q0:q1] = gq[0]
+        dk[k0:k1] = gk[0]
+        dv[k0:k1] = gv[0]
+    return dq, dk, dv
 
 
 def block_mask_varlen(geoms):

@@ -1,15 +1,16 @@
 """Pins for the varlen oracle: pad / unpad on a hand-worked example and a
 round trip, packed attention against the padded batch (equal lengths) and
 against a padded batch with a dense mask that hides the padding (unequal
-lengths), and the per-sequence block mask against its expansion."""
+lengths), the per-sequence block mask against its expansion, and the packed
+gradients against central finite differences of the packed forward."""
 
 import numpy as np
 import pytest
 
 from oracle import attention_full, dflash_dense_mask, round_multiple
 from oracle.blockmask import expand_block_mask
-from oracle.varlen import (attention_varlen, block_mask_varlen, dflash_varlen_geoms, pad,
-                           unpad)
+from oracle.varlen import (attention_varlen, attention_varlen_bwd, block_mask_varlen,
+                           dflash_varlen_geoms, pad, unpad)
 
 
 def test_unpad_pad_worked_example():
@@ -119,3 +120,43 @@ def test_geoms_reject_non_dflash_lengths():
         dflash_varlen_geoms([0, 10], [0, 30], 4)   # 10 queries, blocks of 4
     with pytest.raises(ValueError):
         dflash_varlen_geoms([0, 8], [0, 4], 4)     # fewer keys than queries
+
+
+def _fd(fn, x, eps=1e-6):
+    g = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        old = x[i]
+        x[i] = old + eps
+        lp = fn()
+        x[i] = old - eps
+        lm = fn()
+        x[i] = old
+        g[i] = (lp - lm) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("layer", [dict(is_causal=True),
+                                   dict(is_causal=False, layer_type="sliding",
+                                        sliding_window=3)])
+def test_varlen_grads_match_finite_differences(layer):
+    """Three sequences, the middle one keys without queries: every gradient,
+    including the middle sequence's zero dK / dV, against finite differences
+    of the packed forward's loss sum(O * dO)."""
+    bs, H, KVH, D = 2, 2, 1, 3
+    cu_q = np.array([0, 4, 4, 6])
+    cu_k = np.array([0, 10, 15, 21])
+    q, k, v = _qkv(6, 21, H, KVH, D, 5)
+    dout = np.random.default_rng(6).standard_normal((6, H, D))
+    geoms = dflash_varlen_geoms(cu_q, cu_k, bs, **layer)
+    scale = 0.7
+
+    def loss():
+        o, _ = attention_varlen(q, k, v, cu_q, cu_k, scale=scale, geoms=geoms)
+        return float((o * dout).sum())
+
+    dq, dk, dv = attention_varlen_bwd(q, k, v, dout, cu_q, cu_k, scale=scale, geoms=geoms)
+    np.testing.assert_allclose(dq, _fd(loss, q), rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dk, _fd(loss, k), rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dv, _fd(loss, v), rtol=0, atol=1e-7)
+    assert not dk[10:15].any() and not dv[10:15].any()
+    assert np.abs(dk[:10]).max() > 1e-3 and np.abs(dv[15:]).max() > 1e-3
