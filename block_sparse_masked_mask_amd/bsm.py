@@ -35,6 +35,7 @@ EXPORTS = ("resolve_dflash_is_causal", "block_mask_shape", "build_block_mask",
            "attn_bwd_workspace_size",
            "masked_attn_bwd",
            "block_mask_varlen_shape", "build_block_mask_varlen", "masked_attn_varlen_fwd",
+           "masked_attn_varlen_bwd_workspace_size", "masked_attn_varlen_bwd",
            "unpad_index", "gather_rows", "scatter_rows", "bsm_last_error")
 
 
@@ -128,6 +129,8 @@ def lib():
         L.build_block_mask_varlen.argtypes = [POINTER(VarlenC), POINTER(DFlashC),
                                               POINTER(BlockMaskC), c_void_p]
         L.masked_attn_varlen_fwd.argtypes = [POINTER(VarlenC), POINTER(AttnArgs), c_void_p]
+        L.masked_attn_varlen_bwd_workspace_size.argtypes = [POINTER(VarlenC), POINTER(c_int64)]
+        L.masked_attn_varlen_bwd.argtypes = [POINTER(VarlenC), POINTER(AttnBwdArgs), c_void_p]
         L.unpad_index.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                   c_void_p]
         L.gather_rows.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p,
@@ -678,6 +681,45 @@ def masked_attn_varlen_fwd(q, k, v, varlen, pred=None, block_mask=None, softmax_
     _check(lib().masked_attn_varlen_fwd(ctypes.byref(vc), ctypes.byref(a),
                                         _stream(stream, out if owned else None, lse)))
     return (out, lse[0]) if return_lse else out
+
+
+def masked_attn_varlen_bwd(q, k, v, out, dout, lse, varlen, pred=None, block_mask=None,
+                           softmax_scale=None, stream=None):
+    """Backward of masked_attn_varlen_fwd: q, out, dout (total_q, H, D), k, v
+    (total_k, KVH, D), lse (H, total_q) as that forward returns it; returns
+    (dq, dk, dv) in the packed layouts."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dim() != 3:
+            raise ValueError(f"packed {name} must be 3D (rows, heads, D)")
+    if lse.dim() != 2 or tuple(lse.shape) != (q.shape[1], q.shape[0]):
+        raise ValueError("lse must be (H, total_q)")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = AttnBwdArgs()
+    a.q, a.k, a.v = tensor4(q.unsqueeze(0)), tensor4(k.unsqueeze(0)), tensor4(v.unsqueeze(0))
+    a.o, a.dout = tensor4(out.unsqueeze(0)), tensor4(dout.unsqueeze(0))
+    lse = lse.contiguous()
+    a.lse = lse.data_ptr() if lse.numel() else None
+    a.dq, a.dk, a.dv = tensor4(dq.unsqueeze(0)), tensor4(dk.unsqueeze(0)), tensor4(dv.unsqueeze(0))
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.reserved = 0
+    keep = []
+    if pred is not None:
+        pc = pred.c()
+        keep.append(pc)
+        a.pred = ctypes.pointer(pc)
+    if block_mask is not None:
+        bmc = block_mask.c()
+        keep.append(bmc)
+        a.bm = ctypes.pointer(bmc)
+    vc = varlen.c()
+    nbytes = c_int64(0)
+    _check(lib().masked_attn_varlen_bwd_workspace_size(ctypes.byref(vc), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    a.workspace = ws.data_ptr()
+    a.workspace_bytes = nbytes.value
+    _check(lib().masked_attn_varlen_bwd(ctypes.byref(vc), ctypes.byref(a),
+                                        _stream(stream, dq, dk, dv, ws, lse)))
+    return dq, dk, dv
 
 
 def unpad(x, valid, stream=None):

@@ -254,7 +254,13 @@ hipError_t launch_typed(const AttnBwdParams& p, hipStream_t s) {
   const dim3 blk(64 * kWavesPerBlock);
   const int64_t rows = (int64_t)p.f.B * p.f.H * p.f.Sq;
   const int64_t keys = (int64_t)p.f.B * p.f.KVH * p.f.Sk;
-  if (rows == 0) return hipSuccess;
+  if (rows == 0) {
+    // no query attends to any key: dK = dV = 0, written by the row kernel's empty loop
+    if (keys > 0)
+      hipLaunchKernelGGL((k_bwd_dkdv<T, D>), dim3((keys + kWavesPerBlock - 1) / kWavesPerBlock),
+                         blk, 0, s, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
                      blk, 0, s, p);
   if (sizeof(T) == 2 && attn_bwd_mfma_applies(p, D)) return launch_attn_bwd_mfma(p, s);

@@ -1195,6 +1195,153 @@ int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* a, hipStre
   return hip_status(he, "masked_attn_varlen_fwd");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Rows r0 .. r0 + n - 1 of a packed (1, rows, heads, D) tensor, as a batch of one.
+bsm_tensor4 seq_rows(const bsm_tensor4& t, int64_t r0, int64_t n) {
+  bsm_tensor4 s = t;
+  s.size[1] = n;
+  if (t.data && n > 0)
+    s.data = static_cast<const char*>(t.data) + r0 * t.stride[1] * elem_size(t.dtype);
+  return s;
+}
+
+// Delta of sequence b of a varlen backward: H * Sq_b floats, 256-byte aligned.
+int64_t varlen_delta_bytes(const bsm_varlen* vl, int64_t b) {
+  const int64_t sq = (int64_t)vl->cu_seqlens_q_host[b + 1] - vl->cu_seqlens_q_host[b];
+  return round_multiple(vl->H * sq * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int masked_attn_varlen_bwd_workspace_size(const bsm_varlen* vl, int64_t* bytes) {
+  VarlenInfo vi;
+  int e = check_varlen(vl, vi);
+  if (e) return e;
+  if (!bytes) return fail(BSM_E_ARG, "bytes is NULL");
+  int64_t n = 0;
+  for (int64_t b = 0; b < vi.B; ++b) n += varlen_delta_bytes(vl, b);
+  *bytes = n;
+  return BSM_OK;
+}
+
+int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
+                           hipStream_t stream) {
+  VarlenInfo vi;
+  int e = check_varlen(vl, vi);
+  if (e) return e;
+  if (!a) return fail(BSM_E_ARG, "args is NULL");
+  if (a->reserved != 0) return fail(BSM_E_ARG, "args.reserved must be 0");
+  if (vl->D != 64 && vl->D != 128)
+    return fail(BSM_E_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)vl->D);
+  if (a->mask || a->bias || a->dbias)
+    return fail(BSM_E_UNSUPPORTED, "varlen backward takes a DFlash predicate or no mask");
+  const int32_t dt = a->q.dtype;
+  if (dt != BSM_BF16 && dt != BSM_F32) return fail(BSM_E_DTYPE, "q must be bf16 or f32");
+  const int64_t tq = vl->total_q, tk = vl->total_k;
+  if ((e = check_tensor_qkv(&a->q, "q", 1, tq, vl->H, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->k, "k", 1, tk, vl->KVH, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->v, "v", 1, tk, vl->KVH, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->o, "o", 1, tq, vl->H, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dout, "dout", 1, tq, vl->H, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dq, "dq", 1, tq, vl->H, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dk, "dk", 1, tk, vl->KVH, vl->D, dt))) return e;
+  if ((e = check_tensor_qkv(&a->dv, "dv", 1, tk, vl->KVH, vl->D, dt))) return e;
+  if (!a->lse && vl->H * tq > 0) return fail(BSM_E_ARG, "lse is NULL");
+  if (std::isnan(a->softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
+  DFlashRule unused{};
+  if (a->pred && (e = check_dflash_varlen(a->pred, vl, unused))) return e;
+  const bsm_block_mask* bm = a->bm;
+  if (bm) {
+    if (!a->pred) return fail(BSM_E_ARG, "a block mask needs pred");
+    if (bm->Bm != vi.B || bm->Hm != 1 || bm->nQm != vi.nQ || bm->nK != vi.nK)
+      return fail(BSM_E_SHAPE, "block mask dims do not match these sequences");
+    if (vi.B * vi.nQ > 0 && (!bm->kv_num_blocks || !bm->full_kv_num_blocks ||
+                             (vi.nK > 0 && (!bm->kv_indices || !bm->full_kv_indices))))
+      return fail(BSM_E_ARG, "block mask buffer is NULL");
+  }
+  int64_t need = 0;
+  for (int64_t b = 0; b < vi.B; ++b) need += varlen_delta_bytes(vl, b);
+  if (a->workspace_bytes < need)
+    return fail(BSM_E_ARG, "workspace of %lld bytes, %lld needed", (long long)a->workspace_bytes,
+                (long long)need);
+  if (need > 0 && (!a->workspace || (uintptr_t)a->workspace % 256))
+    return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
+
+  // Each sequence is a padded batch of one: its rows of the packed tensors,
+  // its DFlash geometry (C_b = Sk_b - Sq_b context tokens, NB_b = Sq_b / bs
+  // blocks), its row of the block mask, and its LSE columns.
+  char* ws = static_cast<char*>(a->workspace);
+  const int32_t* cq = vl->cu_seqlens_q_host;
+  const int32_t* ck = vl->cu_seqlens_k_host;
+  for (int64_t b = 0; b < vi.B; ++b) {
+    const int64_t q0 = cq[b], sq = (int64_t)cq[b + 1] - cq[b];
+    const int64_t k0 = ck[b], sk = (int64_t)ck[b + 1] - ck[b];
+    char* delta = ws;
+    ws += varlen_delta_bytes(vl, b);
+    if (sq == 0 && sk == 0) continue;
+    bsm_geom gb{1, vl->H, vl->KVH, sq, sk, vl->D};
+    Geo g;
+    if ((e = check_geom(&gb, g))) return e;
+    g.swap = false;  // the forward over packed sequences applies no swap
+    bsm_dflash pb{};
+    const bool pred = a->pred && sq > 0;
+    if (pred) {
+      pb = *a->pred;
+      pb.ctx_len = sk - sq;
+      pb.num_blocks = sq / a->pred->block_size;
+    }
+    AttnInputs in;
+    if ((e = check_attn_aux(g, dt, pred ? &pb : nullptr, nullptr, nullptr, nullptr,
+                            a->softmax_scale, in)))
+      return e;
+    const bool has_bm = bm && pred;
+    if (has_bm) {
+      in.bmv.kv_num = bm->kv_num_blocks + b * vi.nQ;
+      in.bmv.kv_idx = bm->kv_indices + b * vi.nQ * vi.nK;
+      in.bmv.full_num = bm->full_kv_num_blocks + b * vi.nQ;
+      in.bmv.full_idx = bm->full_kv_indices + b * vi.nQ * vi.nK;
+      in.bmv.Bm = 1;
+      in.bmv.Hm = 1;
+      in.bmv.nQm = vi.nQ;  // query tiles past this sequence's are never visited
+      in.bmv.nK = vi.nK;   // the row stride of the index lists
+      in.bmv.h_mode = 0;
+    }
+    const bsm_tensor4 q = seq_rows(a->q, q0, sq), k = seq_rows(a->k, k0, sk);
+    const bsm_tensor4 v = seq_rows(a->v, k0, sk), o = seq_rows(a->o, q0, sq);
+    const bsm_tensor4 dout = seq_rows(a->dout, q0, sq), dq = seq_rows(a->dq, q0, sq);
+    const bsm_tensor4 dk = seq_rows(a->dk, k0, sk), dv = seq_rows(a->dv, k0, sk);
+    AttnBwdParams p{};
+    fill_params(g, q, k, v, const_cast<void*>(o.data), o.stride,
+                a->lse ? const_cast<float*>(a->lse) + q0 : nullptr, a->softmax_scale, pred,
+                false, false, has_bm, in, p.f);
+    p.f.lse_sb = 0;
+    p.f.lse_sh = tq;  // (1, H, total_q): this sequence's columns
+    p.f.lse_sq = 1;
+    p.scale = p.f.scale_log2 / 1.4426950408889634f;
+    p.dout = dout.data;
+    qlike_strides(g, dout.stride, p.do_sb, p.do_sq, p.do_sh);
+    p.dq = const_cast<void*>(dq.data);
+    qlike_strides(g, dq.stride, p.dq_sb, p.dq_sq, p.dq_sh);
+    p.dk = const_cast<void*>(dk.data);
+    p.dk_sb = dk.stride[0];
+    p.dk_sk = dk.stride[1];
+    p.dk_sh = dk.stride[2];
+    p.dv = const_cast<void*>(dv.data);
+    p.dv_sb = dv.stride[0];
+    p.dv_sk = dv.stride[1];
+    p.dv_sh = dv.stride[2];
+    p.delta = reinterpret_cast<float*>(delta);
+    const hipError_t he = launch_attn_bwd(p, (int)g.D, dt == BSM_BF16, stream);
+    if (he != hipSuccess) return hip_status(he, "masked_attn_varlen_bwd");
+  }
+  return BSM_OK;
+}
+
 int unpad_index(const uint8_t* valid, int64_t batch, int64_t seqlen, int64_t row_stride,
                 int32_t* cu_seqlens, int32_t* indices, hipStream_t stream) {
   if (batch < 0 || seqlen < 0) return fail(BSM_E_ARG, "negative batch or seqlen");

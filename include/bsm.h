@@ -383,6 +383,21 @@ int build_block_mask_varlen(const bsm_varlen* vl, const bsm_dflash* pred,
  * (BSM_E_UNSUPPORTED). No head-group swap is applied. */
 int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* args, hipStream_t stream);
 
+/* Backward of masked_attn_varlen_fwd ([FSA-197] Changes: the varlen entry
+ * point; [FSA-190] Changes: mha_bwd): dQ, dK, dV of packed sequences, each
+ * sequence exactly as masked_attn_bwd on it alone. args as for masked_attn_bwd
+ * with q, o, dout, dq (1, total_q, H, D), k, v, dk, dv (1, total_k, KVH, D),
+ * lse float (1, H, total_q) contiguous (the forward's); mask source args.pred
+ * with the per-sequence geometry of block_mask_varlen_shape, or none; args.bm
+ * NULL or built by build_block_mask_varlen; args.mask, bias and dbias must be
+ * NULL (BSM_E_UNSUPPORTED). A sequence with keys and no queries gets zero dK,
+ * dV. args.workspace: at least masked_attn_varlen_bwd_workspace_size bytes of
+ * device memory, 256-byte aligned, owned by the caller (the per-sequence
+ * Delta = rowsum(dO * O)). The sequences run one after another on stream. */
+int masked_attn_varlen_bwd_workspace_size(const bsm_varlen* vl, int64_t* bytes);
+int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* args,
+                           hipStream_t stream);
+
 /* Packing index of a padded batch: valid is a device bool array (batch,
  * seqlen) with row b at valid + b * row_stride (bytes). Writes cu_seqlens
  * (batch + 1 int32: cu_seqlens[b] = valid positions in rows 0 .. b-1) and

@@ -58,6 +58,24 @@ def assert_close(got, want, dtype, what=""):
         assert err.max() <= F32_MAX, f"{what}: max |err| {err.max():.3e} > {F32_MAX}"
 
 
+def assert_grad_close(got, want, dt, what):
+    """Gradients against the fp64 oracle, the bars scaled by max(1, max|want|):
+    bf16 max |err| <= 2e-2 and mean |err| <= 2e-3, f32 max |err| <= 1e-4."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    m = max(1.0, float(np.abs(want).max()) if want.size else 1.0)
+    err = np.abs(got - want)
+    if err.size == 0:
+        return
+    if dt == "bf16":
+        assert err.max() <= 2e-2 * m, f"{what}: max |err| {err.max():.3e} > {2e-2 * m:.3e}"
+        assert err.mean() <= 2e-3 * m, f"{what}: mean |err| {err.mean():.3e} > {2e-3 * m:.3e}"
+    else:
+        assert err.max() <= 1e-4 * m, f"{what}: max |err| {err.max():.3e} > {1e-4 * m:.3e}"
+
+
 def batch_slice(t, b):
     """Batch b of a 4D aux tensor that broadcasts over batch when its dim is 1."""
     if t is None:

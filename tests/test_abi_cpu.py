@@ -369,6 +369,43 @@ def test_varlen_shapes_and_validation(L):
     assert L.masked_attn_varlen_fwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_SHAPE
 
 
+def test_varlen_bwd_workspace_and_validation(L):
+    vl, keep = _varlen([0, 32, 32, 192], [0, 132, 132, 592])
+    need = ctypes.c_int64(-1)
+    assert L.masked_attn_varlen_bwd_workspace_size(ctypes.byref(vl), ctypes.byref(need)) == 0
+    assert need.value == 8 * 32 * 4 + 8 * 160 * 4          # Delta per sequence, 256-aligned
+    a = _bwd_args((1, 8, 2, 192, 592, 128))
+    a.workspace, a.workspace_bytes = 1 << 24, need.value
+    pc = bsm.varlen_dflash(16).c()
+    a.pred = ctypes.pointer(pc)
+    m = _t4((1, 1, 192, 640))
+    a.mask = ctypes.pointer(m)
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(a), None) == \
+        bsm.BSM_E_UNSUPPORTED
+    a.mask = None
+    a.workspace_bytes = need.value - 256
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    a.workspace_bytes = need.value
+    a.workspace = (1 << 24) + 16                              # not 256-byte aligned
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    a.workspace = 1 << 24
+    a.lse = None
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_ARG
+    a.lse = 1 << 21
+    bm = bsm.BlockMaskC(1 << 20, 1 << 20, 1 << 20, 1 << 20, 3, 1, 1, 5)   # nQ is 2
+    a.bm = ctypes.pointer(bm)
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(a), None) == bsm.BSM_E_SHAPE
+    a.bm = None
+    b2 = _bwd_args((2, 8, 2, 96, 296, 128))                    # a padded (B=2) layout
+    b2.workspace, b2.workspace_bytes = 1 << 24, need.value
+    assert L.masked_attn_varlen_bwd(ctypes.byref(vl), ctypes.byref(b2), None) == bsm.BSM_E_SHAPE
+    bad, keep2 = _varlen([0, 30, 62], [0, 130, 262])          # 30 queries, blocks of 16
+    c = _bwd_args((1, 8, 2, 62, 262, 128))
+    c.workspace, c.workspace_bytes = 1 << 24, 1 << 20
+    c.pred = ctypes.pointer(pc)
+    assert L.masked_attn_varlen_bwd(ctypes.byref(bad), ctypes.byref(c), None) == bsm.BSM_E_SHAPE
+
+
 def test_row_copy_validation(L):
     assert L.gather_rows(1 << 20, 48, 1 << 21, 48, 40, 1 << 22, 5, None) == bsm.BSM_E_STRIDE
     assert L.gather_rows(1 << 20, 32, 1 << 21, 64, 64, 1 << 22, 5, None) == bsm.BSM_E_STRIDE

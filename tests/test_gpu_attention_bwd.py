@@ -12,26 +12,11 @@ import pytest
 import torch
 
 import oracle_pool
+from gpu_helpers import assert_grad_close as _close
 from gpu_helpers import bsm, cuda, oracle_geom, oracle_topk_mask, say, synth
 from oracle.attention_bwd import attention_bwd
 
 pytestmark = pytest.mark.gpu
-
-
-def _close(got, want, dt, what):
-    got = np.asarray(got, np.float64)
-    want = np.asarray(want, np.float64)
-    assert got.shape == want.shape, (what, got.shape, want.shape)
-    assert np.isfinite(got).all(), f"{what}: non-finite values"
-    m = max(1.0, float(np.abs(want).max()) if want.size else 1.0)
-    err = np.abs(got - want)
-    if err.size == 0:
-        return
-    if dt == "bf16":
-        assert err.max() <= 2e-2 * m, f"{what}: max |err| {err.max():.3e} > {2e-2 * m:.3e}"
-        assert err.mean() <= 2e-3 * m, f"{what}: mean |err| {err.mean():.3e} > {2e-3 * m:.3e}"
-    else:
-        assert err.max() <= 1e-4 * m, f"{what}: max |err| {err.max():.3e} > {1e-4 * m:.3e}"
 
 
 def _dout(shape, dt, seed):

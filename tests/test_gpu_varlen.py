@@ -1,14 +1,17 @@
 """GPU parity: packed variable-length sequences -- unpad / pad and the packing
 index bit-exact against oracle.varlen, per-sequence DFlash block masks
-bit-exact, and packed attention against the fp64 oracle (bf16: max|err| <=
-2e-2, mean|err| <= 2e-3; f32: max|err| <= 1e-4; -inf LSE exactly)."""
+bit-exact, packed attention against the fp64 oracle (bf16: max|err| <=
+2e-2, mean|err| <= 2e-3; f32: max|err| <= 1e-4; -inf LSE exactly), and its
+gradients against the fp64 oracle (the same bars scaled by max(1, max|ref|))."""
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_bm_equal, assert_close, bsm, np_bm, say, synth
-from oracle.varlen import attention_varlen, block_mask_varlen, dflash_varlen_geoms, pad, unpad
+from gpu_helpers import assert_bm_equal, assert_close, assert_grad_close, bsm, np_bm, say, synth
+from oracle.attention_bwd import group_grads
+from oracle.varlen import (attention_varlen, attention_varlen_bwd, block_mask_varlen,
+                           dflash_varlen_geoms, pad, unpad)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +135,80 @@ def test_varlen_training_shape_sampled():
                                     synth.as_f64(v[None, k0:k1]), 0, h, rows, mask=geoms[b])
             assert_close(o_np[q0 + rows, h], wo, "bf16", f"O seq={b} h={h}")
             assert_close(lse_np[h, q0 + rows], wl, "bf16", f"LSE seq={b} h={h}")
+
+
+def _bwd(seqs, H, KVH, D, dt, layer, bs=16, use_bm=True, seed=0, what=""):
+    """GPU forward + backward of packed sequences; returns the inputs, dO and
+    the gradients (dq, dk, dv) on the host."""
+    q, k, v, cu_q, cu_k = _pack(seqs, H, KVH, D, dt, seed)
+    do = synth.normal_tensor(tuple(q.shape), seed, synth.TID_DOUT, dt)
+    vl = bsm.Varlen(torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(), H, KVH, D)
+    pred = None if layer is None else bsm.varlen_dflash(bs, **layer)
+    bm = bsm.build_block_mask_varlen(vl, pred) if (pred is not None and use_bm) else None
+    say("varlen backward", what, seqs if len(seqs) < 8 else len(seqs), H, KVH, D, dt, layer)
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o, lse = bsm.masked_attn_varlen_fwd(qc, kc, vc, vl, pred=pred, block_mask=bm,
+                                        return_lse=True)
+    dq, dk, dv = bsm.masked_attn_varlen_bwd(qc, kc, vc, o, do.cuda(), lse, vl, pred=pred,
+                                            block_mask=bm)
+    torch.cuda.synchronize()
+    return (q, k, v, do, cu_q, cu_k), tuple(x.float().cpu().numpy() for x in (dq, dk, dv))
+
+
+def _check_bwd(seqs, H, KVH, D, dt, layer, bs=16, use_bm=True, seed=0, what=""):
+    (q, k, v, do, cu_q, cu_k), (dq, dk, dv) = _bwd(seqs, H, KVH, D, dt, layer, bs, use_bm,
+                                                   seed, what)
+    geoms = None if layer is None else dflash_varlen_geoms(cu_q, cu_k, bs, **layer)
+    rq, rk, rv = attention_varlen_bwd(synth.as_f64(q), synth.as_f64(k), synth.as_f64(v),
+                                      synth.as_f64(do), cu_q, cu_k, geoms=geoms)
+    for b in range(len(seqs)):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        assert_grad_close(dq[q0:q1], rq[q0:q1], dt, f"{what} seq {b} dq")
+        assert_grad_close(dk[k0:k1], rk[k0:k1], dt, f"{what} seq {b} dk")
+        assert_grad_close(dv[k0:k1], rv[k0:k1], dt, f"{what} seq {b} dv")
+        if q1 == q0:          # keys that no query sees: exactly zero
+            assert not dk[k0:k1].any() and not dv[k0:k1].any(), f"{what} seq {b}"
+
+
+@pytest.mark.parametrize("layer", LAYERS, ids=[_id(c) for c in LAYERS])
+@pytest.mark.parametrize("H,KVH,D,dt", [(8, 2, 128, "bf16"), (4, 2, 64, "bf16"),
+                                        (3, 3, 128, "bf16"), (4, 2, 64, "f32")])
+def test_varlen_dflash_backward(layer, H, KVH, D, dt):
+    """Matrix-core backward (bf16), its one-head form (G = 1) and the float
+    kernels; sequences with no queries (with and without keys), no context,
+    ragged tiles."""
+    seqs = _dflash_seqs(16, [(100, 2), (0, 0), (300, 10), (50, 0), (0, 3), (700, 1)])
+    _check_bwd(seqs, H, KVH, D, dt, layer, what="dflash")
+
+
+def test_varlen_backward_without_block_mask_and_without_mask():
+    seqs = _dflash_seqs(16, [(135, 9), (257, 1), (0, 2)])
+    _check_bwd(seqs, 8, 2, 128, "bf16", dict(layer_type="sliding", sliding_window=64),
+               use_bm=False, what="no bm")
+    _check_bwd([(200, 333), (1, 7), (0, 5), (129, 129)], 8, 2, 128, "bf16", None,
+               what="no mask")
+    _check_bwd([(200, 333), (1, 7), (129, 129)], 4, 4, 64, "f32", None, what="no mask f32")
+
+
+def test_varlen_backward_training_shape_sampled():
+    """The packed training-size batch of the forward test: every gradient of
+    two KV groups of two sequences against the oracle."""
+    bs = 16
+    seqs = _dflash_seqs(bs, [(4096, 256), (2048, 128), (1024, 64), (3008, 47)])
+    H, KVH, D = 32, 8, 128
+    layer = dict(layer_type="sliding", sliding_window=2048)
+    (q, k, v, do, cu_q, cu_k), (dq, dk, dv) = _bwd(seqs, H, KVH, D, "bf16", layer, seed=3,
+                                                   what="training size")
+    geoms = dflash_varlen_geoms(cu_q, cu_k, bs, **layer)
+    G = H // KVH
+    for b in (1, 3):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        for kvh in (0, 5):
+            say("oracle seq", b, "group", kvh)
+            rq, rk, rv = group_grads(synth.as_f64(q[None, q0:q1]), synth.as_f64(k[None, k0:k1]),
+                                     synth.as_f64(v[None, k0:k1]), synth.as_f64(do[None, q0:q1]),
+                                     0, kvh, mask=geoms[b])
+            w = f"seq {b} group {kvh}"
+            assert_grad_close(dq[q0:q1, kvh * G:(kvh + 1) * G], rq, "bf16", f"{w} dq")
+            assert_grad_close(dk[k0:k1, kvh], rk, "bf16", f"{w} dk")
+            assert_grad_close(dv[k0:k1, kvh], rv, "bf16", f"{w} dv")
