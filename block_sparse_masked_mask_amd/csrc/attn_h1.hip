@@ -1,5 +1,6 @@
-// Masked attention forward, bf16, one head per workgroup (gfx950): the
-// mask-free / DFlash-predicate path with 64-key sub-tiles.
+// Masked attention forward, bf16, one head per workgroup (gfx950), with
+// 64-key sub-tiles: no mask, the DFlash predicate, or a dense bool mask and /
+// or an additive bias read row by row.
 //
 // Same arithmetic as k_attn_bf16_v2 (S^T = K Q^T and O^T += V^T P^T on
 // v_mfma_f32_32x32x16_bf16, float online softmax with the running max raised
@@ -76,12 +77,15 @@ struct H1Row {
   f32x16 oacc[D / 32];
   float m_run, l_run;
   RowIv32 iv;
+  const uint8_t* mrow;   // mask row or null
+  const uint16_t* brow;  // bias row or null
   bool qvalid;
 };
 
 // One 64-key sub-tile (keys k0 ..) in buffer SLOT: S^T of its two 32-key
 // chunks, one max (and at most one rescale) per row, the probabilities, PV.
-template <int D, int SLOT>
+// MODE 1: the row's dense mask bytes and / or bias values enter the scores.
+template <int D, int MODE, int SLOT>
 __device__ __attribute__((always_inline)) inline void sub_tile(const char* lds,
                                                                const AttnParams& p, int k0,
                                                                bool is_full, H1Row<D>& R,
@@ -133,7 +137,7 @@ __device__ __attribute__((always_inline)) inline void sub_tile(const char* lds,
 #pragma unroll
   for (int j = 0; j < PV; ++j) va[j] = vop(j);
 
-  const bool plain = !check_k && !check_mask && R.qvalid;
+  const bool plain = !check_k && !check_mask && R.qvalid && (MODE == 0 || R.brow == nullptr);
   float mloc = -INFINITY;
   if (plain) {
 #pragma unroll
@@ -147,14 +151,29 @@ __device__ __attribute__((always_inline)) inline void sub_tile(const char* lds,
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int kb = k0 + c * 32 + 16 * sb + 8 * hh;  // 8 consecutive keys
+        float bv[8];
+        if (MODE == 1 && R.brow) {
+          bias8_log2(R.brow + kb, bv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+        }
         uint32_t mbits = 0xFFu;
-        if (check_mask) mbits = range_bits(R.iv.lo1, R.iv.hi1, kb) | range_bits(R.iv.lo2, R.iv.hi2, kb);
+        if (check_mask) {
+          if (MODE == 1 && p.mask_kind == 2) {
+            uint2 mb = make_uint2(0, 0);
+            if (R.mrow) mb = *reinterpret_cast<const uint2*>(R.mrow + kb);
+            mbits = byte_bits8(mb);
+          } else {
+            mbits = range_bits(R.iv.lo1, R.iv.hi1, kb) | range_bits(R.iv.lo2, R.iv.hi2, kb);
+          }
+        }
         if (!R.qvalid) mbits = 0;
         if (check_k) mbits &= range_bits(0, Sk, kb);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
-          float sv = sacc[c][u] * p.scale_log2;
+          float sv = sacc[c][u] * p.scale_log2 + bv[e];
           sv = ((mbits >> e) & 1u) ? sv : -INFINITY;
           sacc[c][u] = sv;
           mloc = fmaxf(mloc, sv);
@@ -214,7 +233,7 @@ __device__ __attribute__((always_inline)) inline void sub_tile(const char* lds,
   }
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork) {
   constexpr int NS = D / 16;
   constexpr int NDC = D / 32;
@@ -267,6 +286,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork
     for (int s = 0; s < NS; ++s)
       R.qf[s] = R.qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh) : bf16x8{};
   }
+  R.mrow = (MODE == 1 && p.mask_kind == 2 && R.qvalid) ? aux_row(p.mask, 1, b, h, p.G, q)
+                                                        : nullptr;
+  R.brow = (MODE == 1 && p.has_bias && R.qvalid)
+               ? reinterpret_cast<const uint16_t*>(aux_row(p.bias, 2, b, h, p.G, q))
+               : nullptr;
   R.iv = RowIv32{0, 0, 0, 0};
   if (p.mask_kind == 1) {
     const RowIv v = dflash_row(seq.rule, p.pred_row0 ? 0 : q);
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork
       }
       ld.issue(kslot(SLOT ^ 1), vslot(SLOT ^ 1), 2 * kt_nxt + ((j + 1) & 1), wu);
     }
-    sub_tile<D, SLOT>(s_kv, p, kt_cur * kTile + (j & 1) * kSub, full_cur, R, off, lane, seq.Sk);
+    sub_tile<D, MODE, SLOT>(s_kv, p, kt_cur * kTile + (j & 1) * kSub, full_cur, R, off, lane, seq.Sk);
     kt_cur = kt_nxt;
     full_cur = full_nxt;
   };
@@ -349,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork
 
 bool attn_h1_applies(const AttnParams& p, int D) {
   if (D != 64 && D != 128) return false;
-  if (p.varlen || p.mask_kind == 2 || p.has_bias || p.staged) return false;
+  if (p.varlen || p.staged) return false;
   // 32-bit buffer offsets within one (b, kv head)
   if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
   if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;
@@ -359,10 +383,18 @@ bool attn_h1_applies(const AttnParams& p, int D) {
 hipError_t launch_attn_bf16_h1(const AttnParams& p, int D, hipStream_t s) {
   const int nWork = p.B * p.H * p.nQ;
   if (nWork == 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL((k_attn_bf16_h1<128>), dim3(nWork), dim3(256), 0, s, p, nWork);
-  else
-    hipLaunchKernelGGL((k_attn_bf16_h1<64>), dim3(nWork), dim3(256), 0, s, p, nWork);
+  const bool aux = p.mask_kind == 2 || p.has_bias;
+  if (D == 128) {
+    if (aux)
+      hipLaunchKernelGGL((k_attn_bf16_h1<128, 1>), dim3(nWork), dim3(256), 0, s, p, nWork);
+    else
+      hipLaunchKernelGGL((k_attn_bf16_h1<128, 0>), dim3(nWork), dim3(256), 0, s, p, nWork);
+  } else {
+    if (aux)
+      hipLaunchKernelGGL((k_attn_bf16_h1<64, 1>), dim3(nWork), dim3(256), 0, s, p, nWork);
+    else
+      hipLaunchKernelGGL((k_attn_bf16_h1<64, 0>), dim3(nWork), dim3(256), 0, s, p, nWork);
+  }
   return hipGetLastError();
 }
 

@@ -381,3 +381,54 @@ def test_odd_group_sizes(H, KVH, D, case, Sq, Sk, with_bm):
     q, k, v = cuda(*synth.qkv(2, Sq, Sk, H, KVH, D, "bf16", seed=60 + H + D))
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d) if with_bm else None
     _run_and_check(q, k, v, "bf16", pred=d, bm=bm, what=f"G={H // KVH} D={D} {case}")
+
+
+ONE_HEAD_AUX = [
+    # (H, KVH, D, mask shape, bias shape): heads that no two-head workgroup can
+    # pair (odd G), or per-head block masks, with dense masks and / or biases
+    (3, 3, 128, (2, 3, 300, 640), None),                  # MHA, per-head mask
+    (3, 3, 128, (1, 1, 1, 640), (2, 3, 1, 640)),          # broadcast mask, per-head bias
+    (6, 2, 64, (2, 2, 300, 640), (1, 6, 300, 640)),       # G = 3, KV-head mask
+    (6, 2, 128, None, (2, 1, 1, 640)),                    # bias only
+    (3, 1, 128, (1, 3, 300, 640), (2, 1, 300, 640)),      # G = 3, one KV head
+    (4, 2, 128, (2, 4, 300, 640), (2, 2, 300, 640)),      # G = 2, per-head block mask
+]
+
+
+@pytest.mark.parametrize("H,KVH,D,mshape,bshape", ONE_HEAD_AUX)
+def test_one_head_mask_and_bias(H, KVH, D, mshape, bshape):
+    """One head per workgroup with a dense mask and / or a bias: every row of
+    every head, with the mask's own (per-head when it has H heads) block mask
+    and without one; ragged query and key tiles (Sq = 300, Sk = 600)."""
+    B, Sq, Sk = 2, 300, 600
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=70 + H + D))
+    mask = bias = None
+    if mshape is not None:
+        m = synth.random_bool(mshape, 0.3, 71, synth.TID_MASK)
+        m[..., 5] = True
+        mask = torch.from_numpy(m).cuda()
+    if bshape is not None:
+        bias = synth.normal_tensor(bshape, 71, synth.TID_BIAS, "bf16").cuda()
+    what = f"one-head H={H} KVH={KVH} D={D} m={mshape} b={bshape}"
+    if mask is not None:
+        bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+        _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, scale=0.07, what=what)
+    _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, scale=0.07, what=what + " no bm")
+
+
+def test_one_head_fully_masked_rows_and_single_keys():
+    B, Sq, Sk, H, KVH, D = 1, 200, 300, 3, 3, 128
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=72))
+    m = np.zeros((1, 1, Sq, 384), bool)
+    m[0, 0, ::3, 7] = True          # single kept key
+    m[0, 0, 1::3, :] = True         # everything kept (and the tail, ignored)
+    # rows 2::3 keep nothing
+    mask = torch.from_numpy(m).cuda()
+    bias = synth.normal_tensor((1, H, 1, 384), 72, synth.TID_BIAS, "bf16").cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    o, lse = _run_and_check(q, k, v, "bf16", mask=mask, bias=bias, bm=bm,
+                            what="one-head masked rows")
+    assert (o[0, 2::3].float() == 0).all()
+    assert torch.isneginf(lse[0, :, 2::3]).all()
+    torch.testing.assert_close(o[0, ::3, 1].float(), v[0, 7:8, 1].float().expand(67, D),
+                               rtol=0, atol=0)
