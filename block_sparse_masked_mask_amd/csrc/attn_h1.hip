@@ -268,6 +268,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork
   const int b = grp / p.KVH;
   const int h = kvh * p.G + hg;
   const SeqView seq = seq_view(p, b);
+  if (qt >= seq.nQ) return;  // past a packed sequence's end (uniform)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h1(AttnParams p, int nWork
 
 bool attn_h1_applies(const AttnParams& p, int D) {
   if (D != 64 && D != 128) return false;
-  if (p.varlen || p.staged) return false;
+  if (p.staged) return false;
   // 32-bit buffer offsets within one (b, kv head)
   if ((int64_t)p.Sk * p.k_sk * 2 >= (int64_t)1 << 31) return false;
   if ((int64_t)p.Sk * p.v_sk * 2 >= (int64_t)1 << 31) return false;

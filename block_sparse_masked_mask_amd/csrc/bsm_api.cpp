@@ -1186,6 +1186,8 @@ int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* a, hipStre
       WorkOrder ord;
       varlen_order(vl, vi, a->pred ? &p.rule : nullptr, ord);
       he = launch_attn_bf16_v2(p, (int)g.D, stream, &ord);
+    } else if (attn_h1_applies(p, (int)g.D)) {
+      he = launch_attn_bf16_h1(p, (int)g.D, stream);
     } else {
       he = launch_attn_bf16(p, (int)g.D, stream);
     }
