@@ -98,20 +98,47 @@ __device__ inline float bias_at(const AttnParams& f, int b, int h, int q, int64_
                        : ld_elem(reinterpret_cast<const float*>(row), j));
 }
 
+// Products of the 16 bytes a lane holds of O and dO (8 bf16 or 4 floats), summed.
+template <typename T>
+__device__ inline float dot16(uint4 a, uint4 b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (sizeof(T) == 2) {
+      s = fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), s);
+      s = fmaf(__uint_as_float(x[i] & 0xFFFF0000u), __uint_as_float(y[i] & 0xFFFF0000u), s);
+    } else {
+      s = fmaf(__uint_as_float(x[i]), __uint_as_float(y[i]), s);
+    }
+  }
+  return s;
+}
+
+// Delta = rowsum(dO * O), one row per D * sizeof(T) / 16 lanes (16-byte loads).
 template <typename T, int D>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void k_bwd_delta(AttnBwdParams p) {
+__global__ __launch_bounds__(256) void k_bwd_delta(AttnBwdParams p) {
+  constexpr int LPR = D * (int)sizeof(T) / 16;  // lanes per row
+  constexpr int EPL = 16 / (int)sizeof(T);      // elements per lane
   const AttnParams& f = p.f;
-  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= (int64_t)f.B * f.H * f.Sq) return;
-  const int q = (int)(row % f.Sq);
-  const int64_t bh = row / f.Sq;
-  const int h = (int)(bh % f.H);
-  const int b = (int)(bh / f.H);
-  const T* o = reinterpret_cast<const T*>(f.o) + b * f.o_sb + q * f.o_sq + h * f.o_sh;
-  const T* dO = reinterpret_cast<const T*>(p.dout) + b * p.do_sb + q * p.do_sq + h * p.do_sh;
-  const float s = dot(load_vec<T, D>(o, lane), load_vec<T, D>(dO, lane));
-  if (lane == 0) p.delta[row] = s;
+  const int64_t nrows = (int64_t)f.B * f.H * f.Sq;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < nrows) {
+    const int q = (int)(row % f.Sq);
+    const int64_t bh = row / f.Sq;
+    const int h = (int)(bh % f.H);
+    const int b = (int)(bh / f.H);
+    const T* o = reinterpret_cast<const T*>(f.o) + b * f.o_sb + q * f.o_sq + h * f.o_sh;
+    const T* dO = reinterpret_cast<const T*>(p.dout) + b * p.do_sb + q * p.do_sq + h * p.do_sh;
+    s = dot16<T>(*reinterpret_cast<const uint4*>(o + c * EPL),
+                 *reinterpret_cast<const uint4*>(dO + c * EPL));
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (row < nrows && c == 0) p.delta[row] = s;
 }
 
 template <typename T, int D>
@@ -261,8 +288,9 @@ hipError_t launch_typed(const AttnBwdParams& p, hipStream_t s) {
                          blk, 0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
-                     blk, 0, s, p);
+  constexpr int kDeltaRows = 256 / (D * (int)sizeof(T) / 16);  // rows per delta block
+  hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((rows + kDeltaRows - 1) / kDeltaRows), dim3(256),
+                     0, s, p);
   if (sizeof(T) == 2 && attn_bwd_mfma_applies(p, D)) return launch_attn_bwd_mfma(p, s);
   hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock), blk,
                      0, s, p);
