@@ -115,6 +115,21 @@ def test_fully_masked_rows():
     _check_full(q, k, v, "bf16", mask=mask, bm=bm, seed=3, what="masked rows")
 
 
+@pytest.mark.parametrize("D,dt", [(128, "bf16"), (64, "f32")])
+def test_no_queries_zero_key_grads(D, dt):
+    """Sq = 0: no query attends to any key, so dK = dV = 0 (written, not left
+    as the allocator's memory)."""
+    B, Sk, H, KVH = 2, 50, 4, 2
+    q, k, v = cuda(*synth.qkv(B, 0, Sk, H, KVH, D, dt, seed=4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 0), dtype=torch.float32, device=q.device)
+    say("backward without queries", D, dt)
+    dq, dk, dv, _ = bsm.masked_attn_bwd(q, k, v, o, torch.empty_like(q), lse)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0
+    assert (dk == 0).all() and (dv == 0).all()
+
+
 @pytest.mark.parametrize("with_mask", [True, False])
 def test_decode_swap(with_mask):
     """Sq == 1 with H > KVH: the head-group swap, with a per-head bias."""
