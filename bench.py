@@ -305,8 +305,8 @@ VARLEN_LAYOUT = [(4096, 256), (2048, 128), (1024, 64), (3008, 47)]  # (context, 
 def measure_varlen():
     """Four DFlash sequences of different lengths packed together (H=32, KVH=8,
     D=128, blocks of 16), both layer types of the training shape: per-sequence
-    block mask and packed attention, TFLOP/s counted on each sequence's kept
-    tiles."""
+    block mask and packed attention forward and backward, TFLOP/s counted on
+    each sequence's kept tiles."""
     out = {}
     cfg = synth.CONFIGS["dflash_train_bf16"]
     H, KVH, D, bs = cfg["H"], cfg["KVH"], cfg["D"], cfg["block_size"]
@@ -333,6 +333,15 @@ def measure_varlen():
                                                          out=o), reps=5)
         out[f"attn_varlen/dflash_4seq_bf16/{lay['name']}_ms"] = ms
         out[f"attn_varlen/dflash_4seq_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
+        # backward, one sequence after another (2.5x the forward's counted flops)
+        o, lse = bsm.masked_attn_varlen_fwd(q, k, v, vl, pred=pred, block_mask=bm,
+                                            return_lse=True)
+        do = synth.normal_tensor(tuple(q.shape), 1, synth.TID_DOUT, "bf16").cuda()
+        ms = _time_ms(lambda: bsm.masked_attn_varlen_bwd(q, k, v, o, do, lse, vl, pred=pred,
+                                                         block_mask=bm), reps=5)
+        out[f"attn_varlen_bwd/dflash_4seq_bf16/{lay['name']}_ms"] = ms
+        out[f"attn_varlen_bwd/dflash_4seq_bf16/{lay['name']}_TFLOP/s"] = \
+            2.5 * fl / (ms * 1e-3) / 1e12
     return out
 
 

@@ -308,6 +308,25 @@ hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream
   return D == 128 ? launch_typed<float, 128>(p, s) : launch_typed<float, 64>(p, s);
 }
 
+hipError_t launch_attn_bwd_delta(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s) {
+  const int64_t rows = (int64_t)p.f.B * p.f.H * p.f.Sq;
+  if (rows == 0) return hipSuccess;
+  const int epr = D * (is_bf16 ? 2 : 4) / 16;  // lanes per row
+  const dim3 grid((unsigned)((rows + 256 / epr - 1) / (256 / epr)));
+  if (is_bf16) {
+    if (D == 128)
+      hipLaunchKernelGGL((k_bwd_delta<uint16_t, 128>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_bwd_delta<uint16_t, 64>), grid, dim3(256), 0, s, p);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((k_bwd_delta<float, 128>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_bwd_delta<float, 64>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_zero, dim3((n + 255) / 256), dim3(256), 0, s, x, n);

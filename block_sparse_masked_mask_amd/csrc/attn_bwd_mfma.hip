@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
       qvalid ? f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
                    kLog2e
              : -INFINITY;
-  const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
+  const float delta = qvalid ? P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + q] : 0.f;
   const bool live = lse2 != -INFINITY;  // rows with no kept key have zero gradients
   const uint8_t* mrow = (AUX && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
   const uint16_t* brow = (AUX && f.has_bias && qvalid)
@@ -291,7 +291,8 @@ struct DqOffs {
 };
 
 template <bool AUX>
-__global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWork) {
+__global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWork,
+                                                        const WorkOrder order) {
   const AttnParams& f = P.f;
   __shared__ __align__(1024) Tiles<kD> buf0;
   __shared__ __align__(1024) Tiles<kD> buf1;
@@ -302,7 +303,19 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   const int pairs = f.G / 2;
   const int ngrp = nWork / f.nQ;
   int qt, grp;
-  if (ngrp % kXcds == 0) {
+  if (f.varlen && order.n > 0) {
+    // packed sequences, items (b, query tile) in the host's order (heaviest
+    // first), KVH * pairs workgroups per item
+    const int per = f.KVH * pairs;
+    const int it = order.item[L / per];
+    qt = it & 1023;
+    grp = (it >> 10) * per + L % per;
+  } else if (f.varlen) {
+    // every group's heaviest (last) query tiles first, groups spread over the
+    // XCDs; tiles past a sequence's end exit at once
+    grp = L % ngrp;
+    qt = f.nQ - 1 - L / ngrp;
+  } else if (ngrp % kXcds == 0) {
     const int gx = ngrp / kXcds;
     const int li = L / kXcds;
     qt = f.nQ - 1 - li / gx;
@@ -318,6 +331,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   grp /= pairs;
   const int kvh = grp % f.KVH;
   const int b = grp / f.KVH;
+  // a packed sequence's rows, keys and DFlash geometry (the batch itself otherwise)
+  const SeqView seq = seq_view(f, b);
+  if (qt >= seq.nQ) return;  // past a packed sequence's end (uniform)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -326,15 +342,16 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   const int hh = lane >> 5;
   const int h0 = kvh * f.G + 2 * hp;
   const int h = h0 + (w >> 2);
-  const int q = qt * kTile + 32 * (w & 3) + n;
-  const bool qvalid = q < f.Sq;
+  const int q = qt * kTile + 32 * (w & 3) + n;  // row within the sequence
+  const bool qvalid = q < seq.Sq;
+  const int64_t qg = seq.q0 + q;                 // row of the (packed) tensors
 
   bf16x8 qf[kNS], df[kNS];
   {
     const __bf16* qr = reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb +
-                       (int64_t)q * f.q_sq + (int64_t)h * f.q_sh;
+                       qg * f.q_sq + (int64_t)h * f.q_sh;
     const __bf16* dr = reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb +
-                       (int64_t)q * P.do_sq + (int64_t)h * P.do_sh;
+                       qg * P.do_sq + (int64_t)h * P.do_sh;
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
       qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hh) : bf16x8{};
@@ -342,17 +359,18 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
     }
   }
   const float lse2 =
-      qvalid ? f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] *
+      qvalid ? f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + qg * f.lse_sq] *
                    kLog2e
              : -INFINITY;
-  const float delta = qvalid ? P.delta[((int64_t)b * f.H + h) * f.Sq + q] : 0.f;
+  const float delta =
+      qvalid ? P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + qg] : 0.f;
   const bool live = lse2 != -INFINITY;
   const uint8_t* mrow = (AUX && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
   const uint16_t* brow = (AUX && f.has_bias && qvalid)
       ? reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, q)) : nullptr;
   RowIv32 iv{0, 0, 0, 0};
   if (f.mask_kind == 1) {
-    const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+    const RowIv v = dflash_row(seq.rule, f.pred_row0 ? 0 : q);
     iv = RowIv32{(int)v.lo1, (int)v.hi1, (int)v.lo2, (int)v.hi2};
   }
   f32x16 dq[kNDC];
@@ -362,11 +380,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   DqOffs off;
   off.init(lane);
   Loader<kD, 1> ld;
-  ld.init(reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb + (int64_t)kvh * f.k_sh,
-          reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb + (int64_t)kvh * f.v_sh,
-          f.k_sk, f.v_sk, f.Sk, w, lane);
+  ld.init(reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb + seq.k0 * f.k_sk +
+              (int64_t)kvh * f.k_sh,
+          reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb + seq.k0 * f.v_sk +
+              (int64_t)kvh * f.v_sh,
+          f.k_sk, f.v_sk, seq.Sk, w, lane);
   TileList tl;
-  tl.init(f, b, h0, qt);  // identical for both heads of the pair
+  tl.init(f, b, h0, qt, seq.nK);  // identical for both heads of the pair
   const int ntiles = tl.count();
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
     if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
 
     const int k0 = kt_cur * kTile;
-    const bool test = !full_cur || k0 + kTile > f.Sk || !qvalid;
+    const bool test = !full_cur || k0 + kTile > seq.Sk || !qvalid;
     const char* kb = reinterpret_cast<const char*>(cur.k);
     const char* vb = reinterpret_cast<const char*>(cur.v);
 #pragma unroll
@@ -421,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
             bits = range_bits(iv.lo1, iv.hi1, kbk) | range_bits(iv.lo2, iv.hi2, kbk);
           if (AUX && !full_cur && f.mask_kind == 2)
             bits = mrow ? byte_bits8(*reinterpret_cast<const uint2*>(mrow + kbk)) : 0u;
-          bits &= range_bits(0, f.Sk, kbk);
+          bits &= range_bits(0, seq.Sk, kbk);
           if (!qvalid) bits = 0;
         }
         float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -464,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
     full_cur = full_nxt;
   }
   if (qvalid) {
-    __bf16* out = reinterpret_cast<__bf16*>(P.dq) + (int64_t)b * P.dq_sb + (int64_t)q * P.dq_sq +
+    __bf16* out = reinterpret_cast<__bf16*>(P.dq) + (int64_t)b * P.dq_sb + qg * P.dq_sq +
                   (int64_t)h * P.dq_sh;
 #pragma unroll
     for (int dc = 0; dc < kNDC; ++dc) {
@@ -536,7 +556,8 @@ struct DkdvOffs {
 };
 
 template <bool AUX>
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) {
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
+                                                               const WorkOrder order) {
   const AttnParams& f = P.f;
   // two slots: Q tile (.k) and dO tile (.v) of a visited (head, query tile), with
   // its rows' LSE (log2 units), Delta and the key test's keep bits; the loads of
@@ -547,11 +568,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   __shared__ uint64_t s_keep[2][kTile][2];  // keep bits: row, 64-key half
   __shared__ float s_bias[2][kTile];        // a query-broadcast bias row (log2 units)
   // key tile major, lowest key tile first: under causal-like masks the low key
-  // tiles are seen by the most query tiles, so the longest work items start first
-  const int kt = blockIdx.x / (f.B * f.KVH);
-  const int bk = blockIdx.x % (f.B * f.KVH);
-  const int kvh = bk % f.KVH;
-  const int b = bk / f.KVH;
+  // tiles are seen by the most query tiles, so the longest work items start
+  // first; packed sequences take the host's order of (b, key tile) items
+  // (heaviest first), KVH workgroups per item
+  int kt, kvh, b;
+  if (f.varlen && order.n > 0) {
+    const int it = order.item[blockIdx.x / f.KVH];
+    kt = it & 1023;
+    b = it >> 10;
+    kvh = blockIdx.x % f.KVH;
+  } else {
+    kt = blockIdx.x / (f.B * f.KVH);
+    const int bk = blockIdx.x % (f.B * f.KVH);
+    kvh = bk % f.KVH;
+    b = bk / f.KVH;
+  }
+  // a packed sequence's rows, keys and DFlash geometry (the batch itself otherwise)
+  const SeqView seq = seq_view(f, b);
+  if (kt >= seq.nK) return;  // past a packed sequence's end (uniform)
   const int k0 = kt * kTile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -559,16 +593,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int key = k0 + 32 * w + n;  // this lane's key (column of S, dP, P, dS)
-  const bool kvalid = key < f.Sk;
-  const bool test_k = k0 + kTile > f.Sk;
+  const int64_t kg = seq.k0 + key;   // its row of the (packed) K, V, dK, dV
+  const bool kvalid = key < seq.Sk;
+  const bool test_k = k0 + kTile > seq.Sk;
 
   // the lane's K and V rows: B operands of S = Q K^T and dP = dO V^T
   bf16x8 kf[kNS], vf[kNS];
   {
     const __bf16* kr = reinterpret_cast<const __bf16*>(f.k) + (int64_t)b * f.k_sb +
-                       (int64_t)key * f.k_sk + (int64_t)kvh * f.k_sh;
+                       kg * f.k_sk + (int64_t)kvh * f.k_sh;
     const __bf16* vr = reinterpret_cast<const __bf16*>(f.v) + (int64_t)b * f.v_sb +
-                       (int64_t)key * f.v_sk + (int64_t)kvh * f.v_sh;
+                       kg * f.v_sk + (int64_t)kvh * f.v_sh;
 #pragma unroll
     for (int s = 0; s < kNS; ++s) {
       kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(kr + 16 * s + 8 * hh) : bf16x8{};
@@ -593,7 +628,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   if (listed) {
     for (int base = 0; base < end; base += kThreads) {
       const int ps = base + tid;
-      const int c = ps < end ? tile_class_of(f, b, kvh * f.G + ps / f.nQ, ps % f.nQ, kt) : 0;
+      const int c = (ps < end && ps % f.nQ < seq.nQ)
+                        ? tile_class_of(f, b, kvh * f.G + ps / f.nQ, ps % f.nQ, kt) : 0;
       int tot;
       const int o = block_excl_sum<kThreads / 64>(c != 0 ? 1 : 0, s_scan, tot);
       if (c != 0) s_vis[nvis + o] = (uint16_t)((ps << 2) | c);
@@ -608,6 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   };
   auto next_visit = [&](int pos, int& cls) {
     for (; pos < end; ++pos) {
+      if (pos % f.nQ >= seq.nQ) continue;
       cls = __builtin_amdgcn_readfirstlane(
           tile_class_of(f, b, kvh * f.G + pos / f.nQ, pos % f.nQ, kt));
       if (cls != 0) return pos;
@@ -622,9 +659,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
     if (tid < kTile) {
       const int q = q0 + tid;
       float l2 = -INFINITY, dl = 0.f;
-      if (q < f.Sq) {
-        l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + (int64_t)q * f.lse_sq] * kLog2e;
-        dl = P.delta[((int64_t)b * f.H + h) * f.Sq + q];
+      if (q < seq.Sq) {
+        const int64_t qg = seq.q0 + q;
+        l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + qg * f.lse_sq] * kLog2e;
+        dl = P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + qg];
       }
       s_lse2[sl][tid] = l2;
       s_delta[sl][tid] = dl;
@@ -638,14 +676,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
       const int r = tid >> 1, half = tid & 1;
       const int q = q0 + r;
       uint64_t bits = 0;
-      if (q < f.Sq) {
+      if (q < seq.Sq) {
         const uint8_t* mr = aux_row(f.mask, 1, b, h, f.G, q) + k0 + 64 * half;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t kb = k0 + 64 * half + 8 * j;
           const uint32_t mb = cls == 1 ? byte_bits8(*reinterpret_cast<const uint2*>(mr + 8 * j))
                                        : 0xFFu;
-          bits |= (uint64_t)(mb & range_bits(0, f.Sk, kb)) << (8 * j);
+          bits |= (uint64_t)(mb & range_bits(0, seq.Sk, kb)) << (8 * j);
         }
       }
       s_keep[sl][r][half] = bits;
@@ -653,17 +691,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
       const int r = tid >> 1, half = tid & 1;
       const int q = q0 + r;
       uint64_t bits = 0;
-      if (q < f.Sq) {
-        int lo1 = 0, hi1 = f.Sk, lo2 = 0, hi2 = 0;
+      if (q < seq.Sq) {
+        int lo1 = 0, hi1 = seq.Sk, lo2 = 0, hi2 = 0;
         if (cls == 1 && f.mask_kind == 1) {
-          const RowIv v = dflash_row(f.rule, f.pred_row0 ? 0 : q);
+          const RowIv v = dflash_row(seq.rule, f.pred_row0 ? 0 : q);
           lo1 = (int)v.lo1;
           hi1 = (int)v.hi1;
           lo2 = (int)v.lo2;
           hi2 = (int)v.hi2;
         }
-        hi1 = hi1 < f.Sk ? hi1 : f.Sk;
-        hi2 = hi2 < f.Sk ? hi2 : f.Sk;
+        hi1 = hi1 < seq.Sk ? hi1 : seq.Sk;
+        hi2 = hi2 < seq.Sk ? hi2 : seq.Sk;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int kb = k0 + 64 * half + 8 * j;
@@ -673,9 +711,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
       s_keep[sl][r][half] = bits;
     }
     Loader<kD, 2> ld;
-    ld.init(reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb + (int64_t)h * f.q_sh,
-            reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb + (int64_t)h * P.do_sh,
-            f.q_sq, P.do_sq, f.Sq, w, lane);
+    ld.init(reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb + seq.q0 * f.q_sq +
+                (int64_t)h * f.q_sh,
+            reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb + seq.q0 * P.do_sq +
+                (int64_t)h * P.do_sh,
+            f.q_sq, P.do_sq, seq.Sq, w, lane);
     ld.issue(buf[sl], pos % f.nQ, w);
   };
 
@@ -793,7 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int q = vq0 + r0 + e;
-              if (q < f.Sq)
+              if (q < seq.Sq)
                 bv[e] = bias_log2(bf16_to_f32(reinterpret_cast<const uint16_t*>(
                     aux_row(f.bias, 2, b, vh, f.G, q))[key]));
             }
@@ -815,7 +855,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int q = vq0 + r0 + e;
-              if (q < f.Sq && dsv[8 * st + e] != 0.f)
+              if (q < seq.Sq && dsv[8 * st + e] != 0.f)
                 atomicAdd(reinterpret_cast<float*>(const_cast<uint8_t*>(
                               aux_row(P.dbias, 4, b, vh, f.G, q))) + key,
                           dsv[8 * st + e]);
@@ -846,9 +886,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P) 
   if (AUX && P.dbias_acc && f.bias.q_bcast) db_flush();
   // dK^T / dV^T accumulators: lane holds d = 32 dc + 8 (r / 4) + 4 hh + r % 4 of its key
   if (kvalid) {
-    __bf16* ko = reinterpret_cast<__bf16*>(P.dk) + (int64_t)b * P.dk_sb + (int64_t)key * P.dk_sk +
+    __bf16* ko = reinterpret_cast<__bf16*>(P.dk) + (int64_t)b * P.dk_sb + kg * P.dk_sk +
                  (int64_t)kvh * P.dk_sh;
-    __bf16* vo = reinterpret_cast<__bf16*>(P.dv) + (int64_t)b * P.dv_sb + (int64_t)key * P.dv_sk +
+    __bf16* vo = reinterpret_cast<__bf16*>(P.dv) + (int64_t)b * P.dv_sb + kg * P.dv_sk +
                  (int64_t)kvh * P.dv_sh;
 #pragma unroll
     for (int dc = 0; dc < kNDC; ++dc) {
@@ -876,22 +916,30 @@ bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D) {
          (int64_t)p.f.Sq * p.do_sq * 2 < ((int64_t)1 << 31);
 }
 
-hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
+hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s, const WorkOrder* dq_order,
+                                const WorkOrder* dkdv_order) {
+  static const WorkOrder kNoOrder{};  // n = 0
   const AttnParams& f = p.f;
+  const WorkOrder& oq = (dq_order && f.varlen) ? *dq_order : kNoOrder;
+  const WorkOrder& ok = (dkdv_order && f.varlen) ? *dkdv_order : kNoOrder;
   const int64_t nq = (int64_t)f.B * f.H * f.nQ;
-  const int64_t nk = (int64_t)f.B * f.KVH * f.nK;
+  const int64_t nk = ok.n > 0 ? (int64_t)ok.n * f.KVH : (int64_t)f.B * f.KVH * f.nK;
   // the two-head pipelined dQ kernel needs head pairs that share their block
   // mask row and K / V offsets within 32 bits
-  const bool pair = f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1) && !f.varlen &&
+  const bool pair = f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1) &&
                     (int64_t)f.Sk * f.k_sk * 2 < ((int64_t)1 << 31) &&
                     (int64_t)f.Sk * f.v_sk * 2 < ((int64_t)1 << 31);
   const bool aux = f.has_bias || f.mask_kind == 2;
+  // packed sequences: only the two-head dQ kernel and the dK / dV kernel read
+  // a sequence's rows and keys, and neither takes a mask tensor or bias there
+  if (f.varlen && (!pair || aux)) return hipErrorInvalidValue;
   if (nq > 0) {
-    const int nWork = (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
+    const int nWork = oq.n > 0 ? oq.n * f.KVH * (f.G / 2)
+                               : (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
     if (pair && aux)
-      hipLaunchKernelGGL(k_bwd_dq_pair<true>, dim3(nWork), dim3(512), 0, s, p, nWork);
+      hipLaunchKernelGGL(k_bwd_dq_pair<true>, dim3(nWork), dim3(512), 0, s, p, nWork, oq);
     else if (pair)
-      hipLaunchKernelGGL(k_bwd_dq_pair<false>, dim3(nWork), dim3(512), 0, s, p, nWork);
+      hipLaunchKernelGGL(k_bwd_dq_pair<false>, dim3(nWork), dim3(512), 0, s, p, nWork, oq);
     else if (aux)
       hipLaunchKernelGGL(k_bwd_dq_mfma<true>, dim3(nq), dim3(kThreads), 0, s, p);
     else
@@ -899,9 +947,9 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s) {
   }
   if (nk > 0) {
     if (aux)
-      hipLaunchKernelGGL(k_bwd_dkdv_mfma<true>, dim3(nk), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(k_bwd_dkdv_mfma<true>, dim3(nk), dim3(kThreads), 0, s, p, ok);
     else
-      hipLaunchKernelGGL(k_bwd_dkdv_mfma<false>, dim3(nk), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(k_bwd_dkdv_mfma<false>, dim3(nk), dim3(kThreads), 0, s, p, ok);
   }
   return hipGetLastError();
 }

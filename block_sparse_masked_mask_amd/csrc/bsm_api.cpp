@@ -879,6 +879,8 @@ int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_
   p.dv_sh = a->dv.stride[2];
   char* ws = static_cast<char*>(a->workspace);
   p.delta = reinterpret_cast<float*>(ws);
+  p.delta_sb = (int64_t)p.f.H * p.f.Sq;
+  p.delta_sh = p.f.Sq;
   DbiasOut dout{};
   hipError_t he = hipSuccess;
   if (a->dbias) {
@@ -1102,6 +1104,47 @@ void varlen_order(const bsm_varlen* vl, const VarlenInfo& vi, const DFlashRule* 
   ord.n = (int32_t)items.size();
 }
 
+// (sequence, key tile) items of the dK / dV kernel over packed sequences,
+// heaviest first: a key tile's cost is the number of the sequence's query
+// tiles whose rows keep any of its keys (every one without a DFlash rule).
+void varlen_key_order(const bsm_varlen* vl, const VarlenInfo& vi, const DFlashRule* rule,
+                      WorkOrder& ord) {
+  ord.n = 0;
+  if (vi.B > 64 || vi.nK > 1024) return;
+  std::vector<std::pair<int64_t, int>> items;  // (-cost, b << 10 | kt)
+  for (int64_t b = 0; b < vi.B; ++b) {
+    const int64_t Sq = vl->cu_seqlens_q_host[b + 1] - vl->cu_seqlens_q_host[b];
+    const int64_t Sk = vl->cu_seqlens_k_host[b + 1] - vl->cu_seqlens_k_host[b];
+    const int64_t nQ = (Sq + kTile - 1) / kTile;
+    const int64_t nK = (Sk + kTile - 1) / kTile;
+    std::vector<int64_t> cost(nK, rule ? 0 : nQ);
+    if (rule) {
+      DFlashRule r = *rule;  // the sequence's own geometry, as the kernels complete it
+      r.C = Sk - Sq;
+      const int64_t nb = Sq / r.bs;
+      if (r.S == 0) r.S = nb > 0 ? r.C / nb : 0;
+      auto add = [&](int64_t lo, int64_t hi) {
+        hi = std::min(hi, Sk);
+        for (int64_t kt = lo / kTile; hi > lo && kt <= (hi - 1) / kTile; ++kt) ++cost[kt];
+      };
+      for (int64_t qt = 0; qt < nQ; ++qt) {
+        const RowIv a = dflash_row(r, qt * kTile);
+        const RowIv z = dflash_row(r, std::min(Sq, (qt + 1) * kTile) - 1);
+        add(a.lo1, std::max(a.hi1, z.hi1));
+        add(a.lo2, z.hi2);
+      }
+    }
+    for (int64_t kt = 0; kt < nK; ++kt) items.emplace_back(-cost[kt], (int)((b << 10) | kt));
+  }
+  if ((int64_t)items.size() > kMaxOrder) return;
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) {
+                     return x.first < y.first;
+                   });
+  for (size_t i = 0; i < items.size(); ++i) ord.item[i] = (uint16_t)items[i].second;
+  ord.n = (int32_t)items.size();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1255,8 +1298,8 @@ int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
   if ((e = check_tensor_qkv(&a->dv, "dv", 1, tk, vl->KVH, vl->D, dt))) return e;
   if (!a->lse && vl->H * tq > 0) return fail(BSM_E_ARG, "lse is NULL");
   if (std::isnan(a->softmax_scale)) return fail(BSM_E_ARG, "softmax_scale is NaN");
-  DFlashRule unused{};
-  if (a->pred && (e = check_dflash_varlen(a->pred, vl, unused))) return e;
+  DFlashRule vrule{};
+  if (a->pred && (e = check_dflash_varlen(a->pred, vl, vrule))) return e;
   const bsm_block_mask* bm = a->bm;
   if (bm) {
     if (!a->pred) return fail(BSM_E_ARG, "a block mask needs pred");
@@ -1274,9 +1317,87 @@ int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
   if (need > 0 && (!a->workspace || (uintptr_t)a->workspace % 256))
     return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
 
-  // Each sequence is a padded batch of one: its rows of the packed tensors,
-  // its DFlash geometry (C_b = Sk_b - Sq_b context tokens, NB_b = Sq_b / bs
-  // blocks), its row of the block mask, and its LSE columns.
+  const int64_t G = vl->H / vl->KVH;
+  // bf16, D = 128, head pairs: one launch of each matrix-core kernel over every
+  // sequence (sequence mode, as the packed forward), after Delta over the packed
+  // rows (H x total_q floats, within the per-sequence workspace's size).
+  if (dt == BSM_BF16 && vl->D == 128 && G % 2 == 0 && vi.B > 0 && tq > 0 &&
+      tk * a->k.stride[1] * 2 < ((int64_t)1 << 31) && tk * a->v.stride[1] * 2 < ((int64_t)1 << 31) &&
+      vi.maxSq * a->q.stride[1] * 2 < ((int64_t)1 << 31) &&
+      vi.maxSq * a->dout.stride[1] * 2 < ((int64_t)1 << 31)) {
+    AttnInputs in;
+    in.rule = vrule;
+    if (bm) {
+      in.bmv.kv_num = bm->kv_num_blocks;
+      in.bmv.kv_idx = bm->kv_indices;
+      in.bmv.full_num = bm->full_kv_num_blocks;
+      in.bmv.full_idx = bm->full_kv_indices;
+      in.bmv.Bm = bm->Bm;
+      in.bmv.Hm = 1;
+      in.bmv.nQm = bm->nQm;
+      in.bmv.nK = bm->nK;
+      in.bmv.h_mode = 0;
+    }
+    Geo g{};
+    g.B = vi.B;
+    g.H = vl->H;
+    g.KVH = vl->KVH;
+    g.Sq = tq;
+    g.Sk = tk;
+    g.D = vl->D;
+    g.G = G;
+    g.swap = false;
+    AttnBwdParams p{};
+    fill_params(g, a->q, a->k, a->v, const_cast<void*>(a->o.data), a->o.stride,
+                const_cast<float*>(a->lse), a->softmax_scale, a->pred != nullptr, false, false,
+                bm != nullptr, in, p.f);
+    p.f.q_sb = p.f.k_sb = p.f.v_sb = p.f.o_sb = 0;
+    p.f.lse_sb = 0;
+    p.f.lse_sh = tq;
+    p.f.lse_sq = 1;
+    p.f.Sq = (int32_t)vi.maxSq;
+    p.f.nQ = (int32_t)vi.nQ;
+    p.f.Sk = (int32_t)tk;  // bounds the 32-bit offset checks
+    p.f.nK = (int32_t)vi.nK;
+    p.f.varlen = 1;
+    p.f.cu_q = vl->cu_seqlens_q;
+    p.f.cu_k = vl->cu_seqlens_k;
+    p.scale = p.f.scale_log2 / 1.4426950408889634f;
+    p.dout = a->dout.data;
+    p.do_sb = 0;
+    p.do_sq = a->dout.stride[1];
+    p.do_sh = a->dout.stride[2];
+    p.dq = const_cast<void*>(a->dq.data);
+    p.dq_sb = 0;
+    p.dq_sq = a->dq.stride[1];
+    p.dq_sh = a->dq.stride[2];
+    p.dk = const_cast<void*>(a->dk.data);
+    p.dk_sb = 0;
+    p.dk_sk = a->dk.stride[1];
+    p.dk_sh = a->dk.stride[2];
+    p.dv = const_cast<void*>(a->dv.data);
+    p.dv_sb = 0;
+    p.dv_sk = a->dv.stride[1];
+    p.dv_sh = a->dv.stride[2];
+    p.delta = static_cast<float*>(a->workspace);
+    p.delta_sb = 0;
+    p.delta_sh = tq;
+    // Delta: the packed rows as one batch of total_q rows, (H, total_q)
+    AttnBwdParams pd = p;
+    pd.f.B = 1;
+    pd.f.Sq = (int32_t)tq;
+    pd.f.varlen = 0;
+    WorkOrder qord, kord;
+    varlen_order(vl, vi, a->pred ? &p.f.rule : nullptr, qord);
+    varlen_key_order(vl, vi, a->pred ? &p.f.rule : nullptr, kord);
+    hipError_t he = launch_attn_bwd_delta(pd, 128, 1, stream);
+    if (he == hipSuccess) he = launch_attn_bwd_mfma(p, stream, &qord, &kord);
+    return hip_status(he, "masked_attn_varlen_bwd");
+  }
+
+  // Otherwise each sequence is a padded batch of one: its rows of the packed
+  // tensors, its DFlash geometry (C_b = Sk_b - Sq_b context tokens, NB_b =
+  // Sq_b / bs blocks), its row of the block mask, and its LSE columns.
   char* ws = static_cast<char*>(a->workspace);
   const int32_t* cq = vl->cu_seqlens_q_host;
   const int32_t* ck = vl->cu_seqlens_k_host;
@@ -1338,6 +1459,8 @@ int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
     p.dv_sk = dv.stride[1];
     p.dv_sh = dv.stride[2];
     p.delta = reinterpret_cast<float*>(delta);
+    p.delta_sb = (int64_t)p.f.H * p.f.Sq;
+    p.delta_sh = p.f.Sq;
     const hipError_t he = launch_attn_bwd(p, (int)g.D, dt == BSM_BF16, stream);
     if (he != hipSuccess) return hip_status(he, "masked_attn_varlen_bwd");
   }

@@ -109,11 +109,12 @@ struct AttnBwdParams {
   int64_t dk_sb, dk_sk, dk_sh;
   void* dv;
   int64_t dv_sb, dv_sk, dv_sh;
-  float* delta;             // (B, H, Sq) rowsum(dO * O), contiguous
+  float* delta;             // rowsum(dO * O): row q of (b, h) at b * delta_sb + h * delta_sh + q
   float* dbias_acc;         // float accumulator of dbias, or null
   AuxView dbias;            // dbias_acc addressed like the bias
   float scale;              // softmax scale (natural units)
   int32_t pad;
+  int64_t delta_sb, delta_sh;  // (B, H, Sq) contiguous: H * Sq, Sq; packed: 0, total_q
 };
 
 // Float dbias accumulator -> dbias (bias dtype, caller strides), original
@@ -214,7 +215,9 @@ int64_t staged_aux_bytes(const AttnParams& p);
 hipError_t launch_aux_combine(AttnParams& p, void* ws, hipStream_t s);
 // Order in which a packed (varlen) launch of the pipelined kernel takes its
 // (sequence, query tile) items: item[i] = b << 10 | qt, heaviest first; each
-// item spans KVH * G / 2 workgroups. n = 0: the kernel's own order.
+// item spans KVH * G / 2 workgroups (the backward's dK / dV kernel: (sequence,
+// key tile) items b << 10 | kt, KVH workgroups each). n = 0: the kernel's own
+// order.
 constexpr int kMaxOrder = 1024;
 struct WorkOrder {
   int32_t n;
@@ -228,10 +231,16 @@ bool attn_h1_applies(const AttnParams& p, int D);
 hipError_t launch_attn_bf16_h1(const AttnParams& p, int D, hipStream_t s);
 // backward: rowsum(dO * O), then dQ and dK / dV (+ dbias accumulation)
 hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
+// rowsum(dO * O) alone, row (b, h, q) at delta[(b * H + h) * Sq + q]
+hipError_t launch_attn_bwd_delta(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
-// bf16 matrix-core dQ and dK / dV (D = 128, no bias, no dense mask)
+// bf16 matrix-core dQ and dK / dV (D = 128); for packed sequences (f.varlen)
+// only head pairs without a mask tensor or bias
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D);
-hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s);
+// (packed: optional host orders of (b, query tile) and (b, key tile) items)
+hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s,
+                                const WorkOrder* dq_order = nullptr,
+                                const WorkOrder* dkdv_order = nullptr);
 hipError_t launch_dbias_out(const DbiasOut& d, hipStream_t s);
 // bf16 short query blocks (at most 32 query rows per (b, h)): the packed /
 // split kernel (p.pack, p.splits set; the merge of the splits' partial states
