@@ -58,8 +58,8 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # differs, traffic is reported as null.
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "d64aa088618d925a",
-                "fetch_kib": 86600.1, "write_kib": 65536.0,
+                "sha256_16": "ddedffa66e3cc79b",
+                "fetch_kib": 86603.2, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
