@@ -58,7 +58,7 @@ int check_geom(const bsm_geom* g, Geo& o) {
     return fail(BSM_E_SHAPE, "H=%lld is not a multiple of KVH=%lld", (long long)g->H,
                 (long long)g->KVH);
   if (g->Sq > INT32_MAX / 2 || g->Sk > INT32_MAX / 2 || g->B > 65535 || g->H > 65535)
-    return fail(BSM_E_UNSUPPORTED, "geometry beyond this build's limits");
+    return fail(BSM_E_UNSUPPORTED, "geometry beyond the library's size limits");
   o.B = g->B;
   o.H = g->H;
   o.KVH = g->KVH;
@@ -937,7 +937,7 @@ int check_varlen(const bsm_varlen* vl, VarlenInfo& vi) {
                 (long long)vl->KVH);
   if (vl->num_seqs > 65535 || vl->H > 65535 || vl->total_q > INT32_MAX / 2 ||
       vl->total_k > INT32_MAX / 2)
-    return fail(BSM_E_UNSUPPORTED, "varlen sizes beyond this build's limits");
+    return fail(BSM_E_UNSUPPORTED, "varlen sizes beyond the library's size limits");
   const int64_t B = vl->num_seqs;
   if (!vl->cu_seqlens_q_host || !vl->cu_seqlens_k_host || !vl->cu_seqlens_q ||
       !vl->cu_seqlens_k)

@@ -66,7 +66,7 @@ typedef enum {
   BSM_E_SHAPE = -2,       /* sizes violate the 4D / GQA / DFlash contract */
   BSM_E_STRIDE = -3,      /* non-contiguous last dim, illegal 0 stride, misalignment */
   BSM_E_DTYPE = -4,       /* dtype not allowed for this argument */
-  BSM_E_UNSUPPORTED = -5, /* valid request outside what this build implements */
+  BSM_E_UNSUPPORTED = -5, /* valid request outside what the library implements */
   BSM_E_HIP = -6          /* HIP launch error */
 } bsm_status;
 
