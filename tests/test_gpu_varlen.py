@@ -212,3 +212,22 @@ def test_varlen_backward_training_shape_sampled():
             assert_grad_close(dq[q0:q1, kvh * G:(kvh + 1) * G], rq, "bf16", f"{w} dq")
             assert_grad_close(dk[k0:k1, kvh], rk, "bf16", f"{w} dk")
             assert_grad_close(dv[k0:k1, kvh], rv, "bf16", f"{w} dv")
+
+
+def test_varlen_backward_many_sequences():
+    """70 short sequences (more than the host work orders take): the kernels'
+    own mapping of (sequence, tile) items; with and without a DFlash mask."""
+    rng = np.random.default_rng(9)
+    layout = [(int(c), int(nb)) for c, nb in zip(rng.integers(0, 90, 70), rng.integers(0, 4, 70))]
+    layout = [(c - c % nb if nb else c, nb) for c, nb in layout]   # context a multiple of blocks
+    seqs = _dflash_seqs(16, layout)
+    _check_bwd(seqs, 8, 2, 128, "bf16", dict(is_causal=True), what="70 seqs dflash")
+    _check_bwd([(int(a), int(b)) for a, b in zip(rng.integers(0, 40, 70), rng.integers(0, 60, 70))],
+               8, 2, 128, "bf16", None, what="70 seqs no mask")
+
+
+def test_varlen_backward_queries_without_keys():
+    """No mask: a sequence with queries and no keys has zero dQ (its rows keep
+    nothing), beside ordinary ones."""
+    _check_bwd([(40, 0), (130, 77), (0, 9), (17, 200)], 8, 2, 128, "bf16", None,
+               what="queries without keys")
