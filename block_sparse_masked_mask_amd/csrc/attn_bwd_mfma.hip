@@ -365,9 +365,14 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   const float delta =
       qvalid ? P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + qg] : 0.f;
   const bool live = lse2 != -INFINITY;
-  const uint8_t* mrow = (AUX && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
-  const uint16_t* brow = (AUX && f.has_bias && qvalid)
+  const bool staged = AUX && f.staged;  // mask and bias folded into one float row
+  const uint8_t* mrow =
+      (AUX && !staged && f.mask_kind == 2 && qvalid) ? aux_row(f.mask, 1, b, h, f.G, q) : nullptr;
+  const uint16_t* brow = (AUX && !staged && f.has_bias && qvalid)
       ? reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, q)) : nullptr;
+  const float* cbrow = staged ? f.cb + (int64_t)b * f.cb_sb +
+                                    (f.cb_hmode == 1 ? h : (f.cb_hmode == 2 ? h / f.G : 0)) * f.cb_sh
+                              : nullptr;
   RowIv32 iv{0, 0, 0, 0};
   if (f.mask_kind == 1) {
     const RowIv v = dflash_row(seq.rule, f.pred_row0 ? 0 : q);
@@ -439,13 +444,21 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
         if (test) {
           if (!full_cur && f.mask_kind == 1)
             bits = range_bits(iv.lo1, iv.hi1, kbk) | range_bits(iv.lo2, iv.hi2, kbk);
-          if (AUX && !full_cur && f.mask_kind == 2)
+          if (AUX && !staged && !full_cur && f.mask_kind == 2)
             bits = mrow ? byte_bits8(*reinterpret_cast<const uint2*>(mrow + kbk)) : 0u;
           bits &= range_bits(0, seq.Sk, kbk);
           if (!qvalid) bits = 0;
         }
         float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (AUX && brow) bias8_log2(brow + kbk, bv);
+        if (staged) {
+          // the folded row: bias in log2 units, -inf where the mask drops a key
+          const float4 c0 = *reinterpret_cast<const float4*>(cbrow + kbk);
+          const float4 c1 = *reinterpret_cast<const float4*>(cbrow + kbk + 4);
+          bv[0] = c0.x, bv[1] = c0.y, bv[2] = c0.z, bv[3] = c0.w;
+          bv[4] = c1.x, bv[5] = c1.y, bv[6] = c1.z, bv[7] = c1.w;
+        } else if (AUX && brow) {
+          bias8_log2(brow + kbk, bv);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * sb + e;
@@ -667,11 +680,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
       s_lse2[sl][tid] = l2;
       s_delta[sl][tid] = dl;
     }
-    if (AUX && f.has_bias && f.bias.q_bcast && tid < kTile) {
+    if (AUX && f.staged) {
+      // mask and bias folded into one float row: the tile's 128-key slice
+      if (tid < kTile) {
+        const int64_t hc = f.cb_hmode == 1 ? h : (f.cb_hmode == 2 ? h / f.G : 0);
+        s_bias[sl][tid] = f.cb[(int64_t)b * f.cb_sb + hc * f.cb_sh + k0 + tid];
+      }
+    } else if (AUX && f.has_bias && f.bias.q_bcast && tid < kTile) {
       const uint16_t* br = reinterpret_cast<const uint16_t*>(aux_row(f.bias, 2, b, h, f.G, 0));
       s_bias[sl][tid] = bias_log2(bf16_to_f32(br[k0 + tid]));
     }
-    if (AUX && f.mask_kind == 2 && (cls == 1 || test_k)) {
+    if (AUX && f.staged) {
+      // no keep bits: the folded row drops masked keys and keys >= Sk
+    } else if (AUX && f.mask_kind == 2 && (cls == 1 || test_k)) {
       // keep bits from the mask bytes of row tid / 2, keys of half tid % 2
       const int r = tid >> 1, half = tid & 1;
       const int q = q0 + r;
@@ -746,7 +767,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
     int ncls = 0;
     const int npos = following(it, pos, ncls);
     if (npos < end) prepare(sl ^ 1, npos, ncls);
-    const bool test = cls == 1 || test_k;
+    const bool test = !(AUX && f.staged) && (cls == 1 || test_k);
     const int vh = kvh * f.G + pos / f.nQ;  // this visit's head and first row
     const int vq0 = (pos % f.nQ) * kTile;
     if (AUX && P.dbias_acc && f.bias.q_bcast) {
@@ -824,8 +845,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
         }
         // the bias of (row, this lane's key) in log2 units
         float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (AUX && f.has_bias) {
-          if (f.bias.q_bcast) {
+        if (AUX && (f.staged || f.has_bias)) {
+          if (f.staged || f.bias.q_bcast) {
             const float bk = s_bias[sl][32 * w + n];
 #pragma unroll
             for (int e = 0; e < 8; ++e) bv[e] = bk;

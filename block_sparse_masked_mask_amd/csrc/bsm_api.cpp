@@ -811,12 +811,66 @@ int masked_attn_fwd(const bsm_geom* geom, const bsm_attn_args* a, hipStream_t st
   return hip_status(he, "masked_attn_fwd");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Kernel parameters of a padded backward call (workspace pointers aside).
+void bwd_params(const Geo& g, const bsm_attn_bwd_args* a, const AttnInputs& in,
+                AttnBwdParams& p) {
+  p = AttnBwdParams{};
+  fill_params(g, a->q, a->k, a->v, const_cast<void*>(a->o.data), a->o.stride,
+              const_cast<float*>(a->lse),
+              a->softmax_scale, a->pred, a->mask, a->bias, a->bm, in, p.f);
+  p.scale = p.f.scale_log2 / 1.4426950408889634f;
+  p.dout = a->dout.data;
+  qlike_strides(g, a->dout.stride, p.do_sb, p.do_sq, p.do_sh);
+  p.dq = const_cast<void*>(a->dq.data);
+  qlike_strides(g, a->dq.stride, p.dq_sb, p.dq_sq, p.dq_sh);
+  p.dk = const_cast<void*>(a->dk.data);
+  p.dk_sb = a->dk.stride[0];
+  p.dk_sk = a->dk.stride[1];
+  p.dk_sh = a->dk.stride[2];
+  p.dv = const_cast<void*>(a->dv.data);
+  p.dv_sb = a->dv.stride[0];
+  p.dv_sk = a->dv.stride[1];
+  p.dv_sh = a->dv.stride[2];
+}
+
+// Bytes of the folded mask / bias rows the matrix-core backward reads when
+// both broadcast over queries (the forward's staged rows), or 0: bf16, D =
+// 128, and the two-head dQ kernel (even G, a head-shared block-mask row).
+int64_t bwd_staged_bytes(const AttnBwdParams& p, int64_t D, int32_t dt) {
+  const AttnParams& f = p.f;
+  if (dt != BSM_BF16 || D != 128 || !attn_bwd_mfma_applies(p, 128) || !staged_aux_applies(f))
+    return 0;
+  if (f.G % 2 || (f.has_bm && f.bm.h_mode == 1)) return 0;
+  if ((int64_t)f.Sk * f.k_sk * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)f.Sk * f.v_sk * 2 >= ((int64_t)1 << 31))
+    return 0;
+  return staged_aux_bytes(f);
+}
+
+}  // namespace
+
+extern "C" {
+
 int attn_bwd_workspace_size(const bsm_geom* geom, const bsm_attn_bwd_args* a, int64_t* bytes) {
   Geo g;
   int e = check_geom(geom, g);
   if (e) return e;
   if (!a || !bytes) return fail(BSM_E_ARG, "args or bytes is NULL");
-  *bytes = bwd_workspace_bytes(g, a->bias, a->dbias);
+  int64_t n = bwd_workspace_bytes(g, a->bias, a->dbias);
+  if ((a->mask || a->bias) && g.B > 0) {
+    AttnInputs in;
+    if ((e = check_attn_aux(g, a->q.dtype, a->pred, a->mask, a->bias, a->bm, a->softmax_scale,
+                            in)))
+      return e;
+    AttnBwdParams p;
+    bwd_params(g, a, in, p);
+    n += bwd_staged_bytes(p, g.D, a->q.dtype);
+  }
+  *bytes = n;
   return BSM_OK;
 }
 
@@ -852,7 +906,10 @@ int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_
     if ((e = check_strides(d, "dbias", elem_size(dt)))) return e;
     if (!d->data && numel(d) > 0) return fail(BSM_E_ARG, "dbias: data is NULL");
   }
-  const int64_t need = bwd_workspace_bytes(g, a->bias, a->dbias);
+  AttnBwdParams p;
+  bwd_params(g, a, in, p);
+  const int64_t staged = g.B > 0 ? bwd_staged_bytes(p, g.D, dt) : 0;
+  const int64_t need = bwd_workspace_bytes(g, a->bias, a->dbias) + staged;
   if (a->workspace_bytes < need)
     return fail(BSM_E_ARG, "workspace of %lld bytes, %lld needed", (long long)a->workspace_bytes,
                 (long long)need);
@@ -860,23 +917,6 @@ int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_
     return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
   if (g.B == 0) return BSM_OK;
 
-  AttnBwdParams p{};
-  fill_params(g, a->q, a->k, a->v, const_cast<void*>(a->o.data), a->o.stride,
-              const_cast<float*>(a->lse),
-              a->softmax_scale, a->pred, a->mask, a->bias, a->bm, in, p.f);
-  p.scale = p.f.scale_log2 / 1.4426950408889634f;
-  p.dout = a->dout.data;
-  qlike_strides(g, a->dout.stride, p.do_sb, p.do_sq, p.do_sh);
-  p.dq = const_cast<void*>(a->dq.data);
-  qlike_strides(g, a->dq.stride, p.dq_sb, p.dq_sq, p.dq_sh);
-  p.dk = const_cast<void*>(a->dk.data);
-  p.dk_sb = a->dk.stride[0];
-  p.dk_sk = a->dk.stride[1];
-  p.dk_sh = a->dk.stride[2];
-  p.dv = const_cast<void*>(a->dv.data);
-  p.dv_sb = a->dv.stride[0];
-  p.dv_sk = a->dv.stride[1];
-  p.dv_sh = a->dv.stride[2];
   char* ws = static_cast<char*>(a->workspace);
   p.delta = reinterpret_cast<float*>(ws);
   p.delta_sb = (int64_t)p.f.H * p.f.Sq;
@@ -911,6 +951,11 @@ int masked_attn_bwd(const bsm_geom* geom, const bsm_attn_bwd_args* a, hipStream_
     dout.s1 = a->dbias->size[1] == 1 ? 0 : a->dbias->stride[1];
     dout.s2 = a->dbias->size[2] == 1 ? 0 : a->dbias->stride[2];
     dout.is_bf16 = dt == BSM_BF16;
+  }
+  if (staged > 0) {
+    // the folded rows go after Delta and the dbias accumulator
+    he = launch_aux_combine(p.f, ws + bwd_workspace_bytes(g, a->bias, a->dbias), stream);
+    if (he != hipSuccess) return hip_status(he, "masked_attn_bwd");
   }
   he = launch_attn_bwd(p, (int)g.D, dt == BSM_BF16, stream);
   if (he == hipSuccess && a->dbias) he = launch_dbias_out(dout, stream);

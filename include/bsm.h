@@ -317,10 +317,14 @@ typedef struct {
   int64_t workspace_bytes;   /*   as reported by attn_bwd_workspace_size */
 } bsm_attn_bwd_args;
 
-/* Bytes of device workspace masked_attn_bwd needs for these arguments (only
- * geometry, bias and dbias are read): float Delta = rowsum(dO * O) for every
- * (b, h, q), plus a float accumulator of the bias's size when dbias is
- * requested. */
+/* Bytes of device workspace masked_attn_bwd needs for these arguments
+ * (geometry, dtype and the mask / bias / block-mask descriptors are read, no
+ * device data): float Delta = rowsum(dO * O) for every (b, h, q), plus a float
+ * accumulator of the bias's size when dbias is requested, plus, for bf16 at
+ * D = 128 with a mask and / or bias that broadcast over queries, one float row
+ * per (b, head of the broadcast) and key: the bias in log2 units, -inf where
+ * the mask drops a key ([FSA-190] Design: broadcast over the query dim).
+ * Errors as masked_attn_bwd's checks of those descriptors. */
 int attn_bwd_workspace_size(const bsm_geom* geom, const bsm_attn_bwd_args* args,
                             int64_t* bytes);
 

@@ -316,8 +316,16 @@ def test_attention_bwd_validation(L):
     g = bsm.Geom(*geom)
     need = ctypes.c_int64(0)
     assert L.attn_bwd_workspace_size(ctypes.byref(g), ctypes.byref(a), ctypes.byref(need)) == 0
-    # Delta (2*16*64 floats) + the bias accumulator (2*4*384 floats), 256-byte parts
-    assert need.value == 2 * 16 * 64 * 4 + 2 * 4 * 384 * 4
+    # Delta (2*16*64 floats) + the bias accumulator (2*4*384 floats) + the bias
+    # folded into one float row per (b, KV head) for the matrix-core kernels
+    # (it broadcasts over queries), 256-byte parts
+    assert need.value == 2 * 16 * 64 * 4 + 2 * 4 * 384 * 4 + 2 * 4 * 384 * 4
+    f32 = _bwd_args(geom, bsm.BSM_F32)                   # f32: the generic kernels, no rows
+    fb, fdb = _t4((2, 4, 1, 384), bsm.BSM_F32), _t4((2, 4, 1, 384), bsm.BSM_F32)
+    f32.bias, f32.dbias = ctypes.pointer(fb), ctypes.pointer(fdb)
+    n32 = ctypes.c_int64(0)
+    assert L.attn_bwd_workspace_size(ctypes.byref(g), ctypes.byref(f32), ctypes.byref(n32)) == 0
+    assert n32.value == 2 * 16 * 64 * 4 + 2 * 4 * 384 * 4
     a.workspace, a.workspace_bytes = 1 << 24, need.value - 4
     assert L.masked_attn_bwd(ctypes.byref(g), ctypes.byref(a), None) == bsm.BSM_E_ARG
     assert b"workspace" in L.bsm_last_error()
