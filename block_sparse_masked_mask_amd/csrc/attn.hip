@@ -297,6 +297,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // float path: vector-ALU products, 64 queries x (4 threads per query)
+
+// x of another lane of the same quad (DPP quad_perm CTRL), one VALU op
+template <int CTRL>
+__device__ inline float quad_xor(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 64;
 
@@ -365,16 +371,18 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         *reinterpret_cast<float4*>(&sv[r * P + c4 * 4]) = vv4;
       }
       __syncthreads();
+      // fully unrolled key loops: s[] stays in registers
       float s[kF32Keys];
       float mloc = -INFINITY;
-#pragma unroll 8
+#pragma unroll
       for (int j = 0; j < kF32Keys; ++j) {
         const float* kr = &sk[j * P + part * DS];
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < DS; ++i) acc = fmaf(qv[i], kr[i], acc);
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
+        // the 4 threads of a query are a DPP quad: xor 1, then xor 2
+        acc += quad_xor<0xB1>(acc);  // quad_perm [1, 0, 3, 2]
+        acc += quad_xor<0x4E>(acc);  // quad_perm [2, 3, 0, 1]
         const int64_t key = k0 + j;
         float sc = acc * p.scale_log2;
         if (brow && key < seq.Sk) sc += bias_log2(brow[key]);
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DS; ++i) o[i] *= alpha;
-#pragma unroll 8
+#pragma unroll
       for (int j = 0; j < kF32Keys; ++j) {
         const float e = exp2f(s[j] - m_use);
         l_run += e;
