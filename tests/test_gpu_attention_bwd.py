@@ -104,6 +104,23 @@ def test_dense_mask_and_bias(dt, mshape, bshape, D):
                 need_dbias=bias is not None, seed=2, what=f"dense m={mshape} b={bshape}")
 
 
+@pytest.mark.parametrize("H,KVH,per_head_bm", [(3, 3, False), (3, 1, False), (4, 2, True)])
+def test_broadcast_mask_bias_single_head_kernels(H, KVH, per_head_bm):
+    """Query-broadcast mask and bias where the one-head dQ kernel runs (odd G,
+    or a per-head block mask): the rows are not folded there, the kernels read
+    the mask bytes and bias values, with dbias."""
+    B, Sq, Sk, D = 2, 150, 200, 128
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=8))
+    mh = H if per_head_bm else 1
+    m = synth.random_bool((B, mh, 1, 256), 0.4, 8, synth.TID_MASK)
+    m[..., 3] = True
+    mask = torch.from_numpy(m).cuda()
+    bias = synth.normal_tensor((B, KVH, 1, 256), 8, synth.TID_BIAS, "bf16").cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    _check_full(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, scale=0.09, need_dbias=True,
+                seed=8, what=f"broadcast H={H} KVH={KVH} per-head bm={per_head_bm}")
+
+
 def test_fully_masked_rows():
     B, Sq, Sk, H, KVH, D = 1, 130, 200, 2, 1, 64
     q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=3))
