@@ -296,31 +296,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// float path: vector-ALU products, 64 queries x (4 threads per query)
+// float path: vector-ALU products, 16 queries x (16 threads per query), so
+// that short query blocks still spread over many workgroups
 
-// x of another lane of the same quad (DPP quad_perm CTRL), one VALU op
+// x of another lane of the same 16-lane row (DPP control CTRL), one VALU op
 template <int CTRL>
-__device__ inline float quad_xor(float x) {
+__device__ inline float dpp_swap(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-constexpr int kF32Rows = 64;
+// sum over the 16 lanes of a row: quad xor 1 and xor 2 (quad_perm [1,0,3,2],
+// [2,3,0,1]), then the two quads of each half row (row_half_mirror) and the
+// two halves (row_mirror)
+__device__ inline float row16_sum(float x) {
+  x += dpp_swap<0xB1>(x);
+  x += dpp_swap<0x4E>(x);
+  x += dpp_swap<0x141>(x);
+  x += dpp_swap<0x140>(x);
+  return x;
+}
+constexpr int kF32Tpq = 16;                 // threads per query
+constexpr int kF32Rows = 256 / kF32Tpq;    // queries per workgroup
 constexpr int kF32Keys = 64;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
-  constexpr int DS = D / 4;   // dims per thread
+  constexpr int DS = D / kF32Tpq;  // dims per thread
   constexpr int P = D + 4;    // LDS pitch in floats
   __shared__ __align__(16) float sk[kF32Keys * P];
   __shared__ __align__(16) float sv[kF32Keys * P];
 
-  const int rt = blockIdx.x;  // 64-row tile
+  const int rt = blockIdx.x;  // block of kF32Rows rows
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int part = tid & 3;
+  const int part = tid & (kF32Tpq - 1);
   const SeqView seq = seq_view(p, b);
   if (rt * kF32Rows >= seq.Sq) return;  // past a packed sequence's end (uniform)
-  const int q = rt * kF32Rows + (tid >> 2);
+  const int q = rt * kF32Rows + tid / kF32Tpq;
   const bool qvalid = q < seq.Sq;
   const int kvh = h / p.G;
   const int qt = (rt * kF32Rows) / kTile;
@@ -380,9 +392,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnParams p) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < DS; ++i) acc = fmaf(qv[i], kr[i], acc);
-        // the 4 threads of a query are a DPP quad: xor 1, then xor 2
-        acc += quad_xor<0xB1>(acc);  // quad_perm [1, 0, 3, 2]
-        acc += quad_xor<0x4E>(acc);  // quad_perm [2, 3, 0, 1]
+        acc = row16_sum(acc);  // the query's 16 threads are one DPP row
         const int64_t key = k0 + j;
         float sc = acc * p.scale_log2;
         if (brow && key < seq.Sk) sc += bias_log2(brow[key]);
