@@ -28,6 +28,14 @@
 //    per target row (float atomics only across workgroups: batches or KV
 //    groups sharing a bias row); a bias per query takes one atomic add per
 //    (query, key) and head.
+//  * A mask and / or bias that broadcast over queries can come folded into one
+//    float row per (b, head of the broadcast) (f.staged: the bias in log2
+//    units, -inf where the mask drops a key or past Sk; [FSA-190] Design),
+//    which both kernels read in place of keep bits and bias values.
+//  * Packed sequences (f.varlen, the two-head dQ kernel and dK / dV): a work
+//    item reads its sequence's rows, keys and DFlash geometry through
+//    seq_view, items come in the host's order (heaviest first) when given, and
+//    those past a sequence's tiles exit at once ([FSA-197] Changes: varlen).
 #include <math.h>
 
 #include "attn_common.h"
