@@ -22,9 +22,9 @@
 //   * online softmax in float with exp2 (scale * log2 e folded in); the row
 //     rescale is a per-lane scalar because each lane owns one query row;
 //   * O^T += V^T P^T on the same MFMA, V^T read as 16-byte rows from LDS.
-// f32 kernel (k_attn_f32): true float products on the vector ALU, 64 queries per
-// workgroup, 4 threads per query each owning D/4 dims; K and V tiles of 64 keys
-// staged in LDS.
+// f32 kernel (k_attn_f32): true float products on the vector ALU, 16 queries per
+// workgroup, 16 threads per query each owning D/16 dims (dot products summed
+// across the 16 lanes by DPP); K and V tiles of 64 keys staged in LDS.
 #include <math.h>
 
 #include "attn_common.h"
