@@ -19,7 +19,10 @@ value = counted flops of the step / step time, where counted flops are
   configs      -- the other workloads at full size: long-context DFlash (TFLOP/s,
                   fraction of peak, device memory), dynamic top-k (TFLOP/s,
                   fraction of peak), decode (GB/s of the tile and the gather
-                  path against HBM peak), tiny fp32 (launch time);
+                  path against HBM peak), tiny fp32 (launch time); the
+                  backward of the training shape and of the dynamic-mask
+                  workload with dbias, and the packed 4-sequence pack forward
+                  and backward (ms, TFLOP/s counted);
   cpu_baseline -- the CPU oracle on a pool of one-thread host processes, one
                   per usable core (at most 16), on a bounded random sample of
                   every workload: wall seconds, oracle seconds, extrapolated
@@ -589,7 +592,11 @@ def measure_configs():
     return {"tiny_dflash_fp32": measure_tiny(),
             "long_dflash_bf16": measure_long_context(),
             "dynamic_topk_bf16": measure_dynamic_topk(),
-            "decode_swap_bf16": measure_decode_swap()}
+            "decode_swap_bf16": measure_decode_swap(),
+            # the backward (training shape; dynamic-mask workload with dbias) and
+            # packed sequences (forward and backward)
+            "backward": measure_backward(),
+            "varlen_dflash_4seq_bf16": measure_varlen()}
 
 
 # ---------------------------------------------------------------------------
