@@ -261,13 +261,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq_mfma(AttnBwdParams P) {
   }
 }
 
-// ------------------------------------------------- dQ, two heads per workgroup
+// ------------------------------------------------- dQ, pipelined
 //
-// The layout of the pipelined forward (attn_v2.hip): 512 threads, waves 0-3
-// take 128 query rows of head h and waves 4-7 the same rows of head h + 1 of
-// the same KV group (their block-mask row is shared), K and V tiles reach LDS
-// by LDS-DMA, double buffered, V with its transposed-read swizzle. Per 32-key
-// chunk: S^T = K Q^T, dP^T = V dO^T, dS, then dQ^T += K^T dS^T.
+// The layout of the pipelined forward (attn_v2.hip): 512 threads, K and V
+// tiles reach LDS by LDS-DMA, double buffered, V with its transposed-read
+// swizzle. Per 32-key chunk: S^T = K Q^T, dP^T = V dO^T, dS, then
+// dQ^T += K^T dS^T. HP = 2: waves 0-3 take 128 query rows of head h and waves
+// 4-7 the same rows of head h + 1 of the same KV group (their block-mask row is
+// shared), each wave all 128 keys of a tile. HP = 1 (odd G, per-head block
+// masks): one head, waves 0-3 take keys 0-63 of every tile and waves 4-7 keys
+// 64-127 for the same 128 rows, and the two partial dQ^T are summed through
+// LDS at the end.
 
 // Per-lane LDS byte offsets of the operand reads, computed once. A 32-key chunk
 // adds 32 rows, a 16-key step 16 rows: neither changes a swizzle.
@@ -298,17 +302,19 @@ struct DqOffs {
   }
 };
 
-template <bool AUX>
+template <bool AUX, int HP>
 __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWork,
                                                         const WorkOrder order) {
+  static_assert(HP == 1 || HP == 2, "one or two heads per workgroup");
+  constexpr int NC = HP == 2 ? kTile / 32 : kTile / 64;  // 32-key chunks per wave and tile
   const AttnParams& f = P.f;
   __shared__ __align__(1024) Tiles<kD> buf0;
   __shared__ __align__(1024) Tiles<kD> buf1;
 
-  // work items (b, KV-group head pair, query tile) as in the pipelined forward
+  // work items (b, KV-group head pair or head, query tile) as in the pipelined forward
   const int L = blockIdx.x;
   const int xcd = L % kXcds;
-  const int pairs = f.G / 2;
+  const int pairs = f.G / HP;
   const int ngrp = nWork / f.nQ;
   int qt, grp;
   if (f.varlen && order.n > 0) {
@@ -348,8 +354,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
   const int w = tid >> 6;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int h0 = kvh * f.G + 2 * hp;
-  const int h = h0 + (w >> 2);
+  const int h0 = kvh * f.G + HP * hp;
+  const int h = HP == 2 ? h0 + (w >> 2) : h0;
+  // the key half of every tile (one head); wave-uniform, kept in a scalar register
+  const int kh = HP == 2 ? 0 : __builtin_amdgcn_readfirstlane(w >> 2);
   const int q = qt * kTile + 32 * (w & 3) + n;  // row within the sequence
   const bool qvalid = q < seq.Sq;
   const int64_t qg = seq.q0 + q;                 // row of the (packed) tensors
@@ -399,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
               (int64_t)kvh * f.v_sh,
           f.k_sk, f.v_sk, seq.Sk, w, lane);
   TileList tl;
-  tl.init(f, b, h0, qt, seq.nK);  // identical for both heads of the pair
+  tl.init(f, b, h0, qt, seq.nK);  // identical for both heads of a pair
   const int ntiles = tl.count();
   bool full_cur = false;
   int kt_cur = ntiles > 0 ? tl.tile(0, full_cur) : 0;
@@ -416,12 +424,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
     barrier();
     if (it + 1 < ntiles) ld.issue(nxt, kt_nxt, w);
 
-    const int k0 = kt_cur * kTile;
-    const bool test = !full_cur || k0 + kTile > seq.Sk || !qvalid;
-    const char* kb = reinterpret_cast<const char*>(cur.k);
-    const char* vb = reinterpret_cast<const char*>(cur.v);
+    const int k0 = kt_cur * kTile + 32 * NC * kh;
+    const bool test = !full_cur || k0 + 32 * NC > seq.Sk || !qvalid;
+    const char* kb = reinterpret_cast<const char*>(cur.k) + 32 * NC * kh * kRowB;
+    const char* vb = reinterpret_cast<const char*>(cur.v) + 32 * NC * kh * kRowB;
 #pragma unroll
-    for (int c = 0; c < kTile / 32; ++c) {
+    for (int c = 0; c < NC; ++c) {
       f32x16 st = f32x16{}, dpt = f32x16{};
       // row operands kAhead d-steps ahead
       bf16x8 ka[kAhead], va[kAhead];
@@ -503,6 +511,31 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq_pair(AttnBwdParams P, int nWo
     }
     kt_cur = kt_nxt;
     full_cur = full_nxt;
+  }
+  if (HP == 1) {
+    // waves 4-7 hand their partial dQ^T to waves 0-3 through the (now idle)
+    // first K / V buffer: 4 waves x 64 lanes x 64 floats = its 64 KiB
+    static_assert(sizeof(Tiles<kD>) == 4 * 64 * 4 * kNDC * 16, "reduction buffer size");
+    float4* red = reinterpret_cast<float4*>(&buf0);
+    __syncthreads();  // every wave is done with the tiles
+    if (kh == 1) {
+#pragma unroll
+      for (int dc = 0; dc < kNDC; ++dc)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          red[(((w & 3) * kNDC + dc) * 4 + g) * 64 + lane] =
+              make_float4(dq[dc][4 * g], dq[dc][4 * g + 1], dq[dc][4 * g + 2], dq[dc][4 * g + 3]);
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int dc = 0; dc < kNDC; ++dc)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 o = red[(((w & 3) * kNDC + dc) * 4 + g) * 64 + lane];
+        dq[dc][4 * g] += o.x, dq[dc][4 * g + 1] += o.y;
+        dq[dc][4 * g + 2] += o.z, dq[dc][4 * g + 3] += o.w;
+      }
   }
   if (qvalid) {
     __bf16* out = reinterpret_cast<__bf16*>(P.dq) + (int64_t)b * P.dq_sb + qg * P.dq_sq +
@@ -953,22 +986,26 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s, const Wor
   const WorkOrder& ok = (dkdv_order && f.varlen) ? *dkdv_order : kNoOrder;
   const int64_t nq = (int64_t)f.B * f.H * f.nQ;
   const int64_t nk = ok.n > 0 ? (int64_t)ok.n * f.KVH : (int64_t)f.B * f.KVH * f.nK;
-  // the two-head pipelined dQ kernel needs head pairs that share their block
-  // mask row and K / V offsets within 32 bits
-  const bool pair = f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1) &&
-                    (int64_t)f.Sk * f.k_sk * 2 < ((int64_t)1 << 31) &&
-                    (int64_t)f.Sk * f.v_sk * 2 < ((int64_t)1 << 31);
+  // the pipelined dQ kernel needs K / V offsets within 32 bits; it takes head
+  // pairs when G is even and the pair shares its block-mask row, else one head
+  const bool piped = (int64_t)f.Sk * f.k_sk * 2 < ((int64_t)1 << 31) &&
+                     (int64_t)f.Sk * f.v_sk * 2 < ((int64_t)1 << 31);
+  const int hp = (f.G % 2 == 0 && !(f.has_bm && f.bm.h_mode == 1)) ? 2 : 1;
   const bool aux = f.has_bias || f.mask_kind == 2;
-  // packed sequences: only the two-head dQ kernel and the dK / dV kernel read
+  // packed sequences: only the pipelined dQ kernel and the dK / dV kernel read
   // a sequence's rows and keys, and neither takes a mask tensor or bias there
-  if (f.varlen && (!pair || aux)) return hipErrorInvalidValue;
+  if (f.varlen && (!piped || aux)) return hipErrorInvalidValue;
   if (nq > 0) {
-    const int nWork = oq.n > 0 ? oq.n * f.KVH * (f.G / 2)
-                               : (int)((int64_t)f.B * f.KVH * (f.G / 2) * f.nQ);
-    if (pair && aux)
-      hipLaunchKernelGGL(k_bwd_dq_pair<true>, dim3(nWork), dim3(512), 0, s, p, nWork, oq);
-    else if (pair)
-      hipLaunchKernelGGL(k_bwd_dq_pair<false>, dim3(nWork), dim3(512), 0, s, p, nWork, oq);
+    const int nWork = oq.n > 0 ? oq.n * f.KVH * (f.G / hp)
+                               : (int)((int64_t)f.B * f.KVH * (f.G / hp) * f.nQ);
+    if (piped && hp == 2 && aux)
+      hipLaunchKernelGGL((k_bwd_dq_pair<true, 2>), dim3(nWork), dim3(512), 0, s, p, nWork, oq);
+    else if (piped && hp == 2)
+      hipLaunchKernelGGL((k_bwd_dq_pair<false, 2>), dim3(nWork), dim3(512), 0, s, p, nWork, oq);
+    else if (piped && aux)
+      hipLaunchKernelGGL((k_bwd_dq_pair<true, 1>), dim3(nWork), dim3(512), 0, s, p, nWork, oq);
+    else if (piped)
+      hipLaunchKernelGGL((k_bwd_dq_pair<false, 1>), dim3(nWork), dim3(512), 0, s, p, nWork, oq);
     else if (aux)
       hipLaunchKernelGGL(k_bwd_dq_mfma<true>, dim3(nq), dim3(kThreads), 0, s, p);
     else

@@ -839,12 +839,11 @@ void bwd_params(const Geo& g, const bsm_attn_bwd_args* a, const AttnInputs& in,
 
 // Bytes of the folded mask / bias rows the matrix-core backward reads when
 // both broadcast over queries (the forward's staged rows), or 0: bf16, D =
-// 128, and the two-head dQ kernel (even G, a head-shared block-mask row).
+// 128, and the pipelined dQ kernel (K / V offsets within 32 bits).
 int64_t bwd_staged_bytes(const AttnBwdParams& p, int64_t D, int32_t dt) {
   const AttnParams& f = p.f;
   if (dt != BSM_BF16 || D != 128 || !attn_bwd_mfma_applies(p, 128) || !staged_aux_applies(f))
     return 0;
-  if (f.G % 2 || (f.has_bm && f.bm.h_mode == 1)) return 0;
   if ((int64_t)f.Sk * f.k_sk * 2 >= ((int64_t)1 << 31) ||
       (int64_t)f.Sk * f.v_sk * 2 >= ((int64_t)1 << 31))
     return 0;
@@ -1362,11 +1361,10 @@ int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
   if (need > 0 && (!a->workspace || (uintptr_t)a->workspace % 256))
     return fail(BSM_E_ARG, "workspace is NULL or not 256-byte aligned");
 
-  const int64_t G = vl->H / vl->KVH;
-  // bf16, D = 128, head pairs: one launch of each matrix-core kernel over every
-  // sequence (sequence mode, as the packed forward), after Delta over the packed
-  // rows (H x total_q floats, within the per-sequence workspace's size).
-  if (dt == BSM_BF16 && vl->D == 128 && G % 2 == 0 && vi.B > 0 && tq > 0 &&
+  // bf16, D = 128: one launch of each matrix-core kernel over every sequence
+  // (sequence mode, as the packed forward), after Delta over the packed rows
+  // (H x total_q floats, within the per-sequence workspace's size).
+  if (dt == BSM_BF16 && vl->D == 128 && vi.B > 0 && tq > 0 &&
       tk * a->k.stride[1] * 2 < ((int64_t)1 << 31) && tk * a->v.stride[1] * 2 < ((int64_t)1 << 31) &&
       vi.maxSq * a->q.stride[1] * 2 < ((int64_t)1 << 31) &&
       vi.maxSq * a->dout.stride[1] * 2 < ((int64_t)1 << 31)) {
@@ -1390,7 +1388,7 @@ int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* a,
     g.Sq = tq;
     g.Sk = tk;
     g.D = vl->D;
-    g.G = G;
+    g.G = vl->H / vl->KVH;
     g.swap = false;
     AttnBwdParams p{};
     fill_params(g, a->q, a->k, a->v, const_cast<void*>(a->o.data), a->o.stride,

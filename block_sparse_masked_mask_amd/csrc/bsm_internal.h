@@ -235,7 +235,7 @@ hipError_t launch_attn_bwd(const AttnBwdParams& p, int D, int is_bf16, hipStream
 hipError_t launch_attn_bwd_delta(const AttnBwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
 // bf16 matrix-core dQ and dK / dV (D = 128); for packed sequences (f.varlen)
-// only head pairs without a mask tensor or bias
+// only without a mask tensor or bias, K / V offsets within 32 bits
 bool attn_bwd_mfma_applies(const AttnBwdParams& p, int D);
 // (packed: optional host orders of (b, query tile) and (b, key tile) items)
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, hipStream_t s,

@@ -397,9 +397,8 @@ int masked_attn_varlen_fwd(const bsm_varlen* vl, const bsm_attn_args* args, hipS
  * NULL (BSM_E_UNSUPPORTED). A sequence with keys and no queries gets zero dK,
  * dV. args.workspace: at least masked_attn_varlen_bwd_workspace_size bytes of
  * device memory, 256-byte aligned, owned by the caller (Delta = rowsum(dO * O)
- * of every row). bf16 with D = 128 and an even H / KVH runs every sequence in
- * one launch of each kernel; other calls run the sequences one after another
- * on stream. */
+ * of every row). bf16 with D = 128 runs every sequence in one launch of each
+ * kernel; other calls run the sequences one after another on stream. */
 int masked_attn_varlen_bwd_workspace_size(const bsm_varlen* vl, int64_t* bytes);
 int masked_attn_varlen_bwd(const bsm_varlen* vl, const bsm_attn_bwd_args* args,
                            hipStream_t stream);

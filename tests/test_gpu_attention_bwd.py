@@ -106,9 +106,9 @@ def test_dense_mask_and_bias(dt, mshape, bshape, D):
 
 @pytest.mark.parametrize("H,KVH,per_head_bm", [(3, 3, False), (3, 1, False), (4, 2, True)])
 def test_broadcast_mask_bias_single_head_kernels(H, KVH, per_head_bm):
-    """Query-broadcast mask and bias where the one-head dQ kernel runs (odd G,
-    or a per-head block mask): the rows are not folded there, the kernels read
-    the mask bytes and bias values, with dbias."""
+    """Query-broadcast mask and bias where the dQ kernel takes one head per
+    workgroup (odd G, or a per-head block mask), reading the folded mask /
+    bias rows, with dbias."""
     B, Sq, Sk, D = 2, 150, 200, 128
     q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=8))
     mh = H if per_head_bm else 1
@@ -119,6 +119,38 @@ def test_broadcast_mask_bias_single_head_kernels(H, KVH, per_head_bm):
     bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
     _check_full(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, scale=0.09, need_dbias=True,
                 seed=8, what=f"broadcast H={H} KVH={KVH} per-head bm={per_head_bm}")
+
+
+@pytest.mark.parametrize("H,KVH", [(2, 2), (3, 1)])
+def test_one_head_dq_dense_and_dflash(H, KVH):
+    """Odd G: the pipelined dQ kernel with one head per workgroup, its waves
+    splitting each key tile in halves whose partial dQ are summed at the end.
+    A per-query mask and bias with dbias (mask bytes and bias values read per
+    tile), a DFlash predicate with its block mask, and no mask; ragged query and
+    key tails, so one half of the last key tile lies past Sk."""
+    B, Sq, Sk, D = 2, 300, 333, 128
+    q, k, v = cuda(*synth.qkv(B, Sq, Sk, H, KVH, D, "bf16", seed=11))
+    m = synth.random_bool((B, H, Sq, 384), 0.3, 11, synth.TID_MASK)
+    m[..., 5] = True
+    mask = torch.from_numpy(m).cuda()
+    bias = synth.normal_tensor((B, H, Sq, 384), 11, synth.TID_BIAS, "bf16").cuda()
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), mask=mask)
+    _check_full(q, k, v, "bf16", mask=mask, bias=bias, bm=bm, scale=0.08, need_dbias=True,
+                seed=11, what=f"one-head dq dense H={H} KVH={KVH}")
+    _check_full(q, k, v, "bf16", seed=11, what=f"one-head dq no mask H={H} KVH={KVH}")
+    d = bsm.DFlash(**SMALL_DFLASH[1])
+    q, k, v = cuda(*synth.qkv(B, d.Sq, d.Sk, H, KVH, D, "bf16", seed=12))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    _check_full(q, k, v, "bf16", pred=d, bm=bm, seed=12, what=f"one-head dq dflash H={H} KVH={KVH}")
+
+
+def test_one_head_dq_mid_size():
+    """H = KVH at a size spanning 8 query and 24 key tiles: every gradient
+    against the oracle, DFlash causal layer with its block mask."""
+    d = bsm.DFlash(2048, 64, 16, is_causal=True)
+    q, k, v = cuda(*synth.qkv(1, d.Sq, d.Sk, 2, 2, 128, "bf16", seed=13))
+    bm = bsm.build_block_mask(bsm.geometry_of(q, k), pred=d)
+    _check_full(q, k, v, "bf16", pred=d, bm=bm, seed=13, what="one-head dq mid size")
 
 
 def test_fully_masked_rows():

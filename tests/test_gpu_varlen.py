@@ -172,11 +172,13 @@ def _check_bwd(seqs, H, KVH, D, dt, layer, bs=16, use_bm=True, seed=0, what=""):
 
 @pytest.mark.parametrize("layer", LAYERS, ids=[_id(c) for c in LAYERS])
 @pytest.mark.parametrize("H,KVH,D,dt", [(8, 2, 128, "bf16"), (4, 2, 64, "bf16"),
-                                        (3, 3, 128, "bf16"), (4, 2, 64, "f32")])
+                                        (3, 3, 128, "bf16"), (6, 2, 128, "bf16"),
+                                        (4, 2, 64, "f32")])
 def test_varlen_dflash_backward(layer, H, KVH, D, dt):
-    """Matrix-core backward (bf16), its one-head form (G = 1) and the float
-    kernels; sequences with no queries (with and without keys), no context,
-    ragged tiles."""
+    """Matrix-core backward (bf16) in one launch per kernel, with head pairs
+    (even G) and one head per dQ workgroup (G = 1, 3), and the float kernels;
+    sequences with no queries (with and without keys), no context, ragged
+    tiles."""
     seqs = _dflash_seqs(16, [(100, 2), (0, 0), (300, 10), (50, 0), (0, 3), (700, 1)])
     _check_bwd(seqs, H, KVH, D, dt, layer, what="dflash")
 
@@ -222,6 +224,7 @@ def test_varlen_backward_many_sequences():
     layout = [(c - c % nb if nb else c, nb) for c, nb in layout]   # context a multiple of blocks
     seqs = _dflash_seqs(16, layout)
     _check_bwd(seqs, 8, 2, 128, "bf16", dict(is_causal=True), what="70 seqs dflash")
+    _check_bwd(seqs, 3, 1, 128, "bf16", dict(is_causal=True), what="70 seqs dflash G=3")
     _check_bwd([(int(a), int(b)) for a, b in zip(rng.integers(0, 40, 70), rng.integers(0, 60, 70))],
                8, 2, 128, "bf16", None, what="70 seqs no mask")
 
