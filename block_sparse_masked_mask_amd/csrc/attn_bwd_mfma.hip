@@ -705,21 +705,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
     }
     return end;
   };
-  // row data of visit pos into slot sl, then its tile loads (after the row
-  // data's own loads, so no later wait for them also waits for the tiles)
-  auto prepare = [&](int sl, int pos, int cls) {
+  // Row data of a visit: its rows' LSE (log2 units) and Delta are loaded into
+  // registers (thread tid < 128: row q0 + tid) before the visit's tiles go out
+  // and the current visit is computed, and reach LDS slot sl, with the key
+  // test's keep bits and a query-broadcast bias row, after it, so that no wait
+  // for them holds up the matrix work.
+  struct RowPre {
+    float lse, dl;  // natural-log LSE, converted when stored
+  };
+  // every thread loads row q0 + tid % 128, clamped into the sequence (a visit
+  // has at least one row): no branch, so nothing waits for the values until
+  // they are stored
+  auto load_rows = [&](int pos) {
+    const int h = kvh * f.G + pos / f.nQ;
+    const int q = min((pos % f.nQ) * kTile + (tid & (kTile - 1)), seq.Sq - 1);
+    const int64_t qg = seq.q0 + q;
+    return RowPre{f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + qg * f.lse_sq],
+                  P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + qg]};
+  };
+  auto store_rows = [&](int sl, int pos, int cls, const RowPre& r) {
     const int h = kvh * f.G + pos / f.nQ;
     const int q0 = (pos % f.nQ) * kTile;
     if (tid < kTile) {
-      const int q = q0 + tid;
-      float l2 = -INFINITY, dl = 0.f;
-      if (q < seq.Sq) {
-        const int64_t qg = seq.q0 + q;
-        l2 = f.lse[(int64_t)b * f.lse_sb + (int64_t)h * f.lse_sh + qg * f.lse_sq] * kLog2e;
-        dl = P.delta[(int64_t)b * P.delta_sb + (int64_t)h * P.delta_sh + qg];
-      }
-      s_lse2[sl][tid] = l2;
-      s_delta[sl][tid] = dl;
+      // rows past Sq or without a kept key get +inf: their probabilities
+      // exp2(x - inf) come out 0 with no test per element
+      const bool ok = q0 + tid < seq.Sq;
+      const float l2 = r.lse * kLog2e;
+      s_lse2[sl][tid] = (ok && l2 != -INFINITY) ? l2 : INFINITY;
+      s_delta[sl][tid] = ok ? r.dl : 0.f;
     }
     if (AUX && f.staged) {
       // mask and bias folded into one float row: the tile's 128-key slice
@@ -772,13 +785,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
       }
       s_keep[sl][r][half] = bits;
     }
+  };
+  // the Q and dO tiles of visit pos into LDS tiles tq, tdo (LDS-DMA)
+  auto issue_tiles = [&](__bf16* tq, __bf16* tdo, int pos) {
+    const int h = kvh * f.G + pos / f.nQ;
     Loader<kD, 2> ld;
     ld.init(reinterpret_cast<const __bf16*>(f.q) + (int64_t)b * f.q_sb + seq.q0 * f.q_sq +
                 (int64_t)h * f.q_sh,
             reinterpret_cast<const __bf16*>(P.dout) + (int64_t)b * P.do_sb + seq.q0 * P.do_sq +
                 (int64_t)h * P.do_sh,
             f.q_sq, P.do_sq, seq.Sq, w, lane);
-    ld.issue(buf[sl], pos % f.nQ, w);
+    ld.issue(tq, tdo, pos % f.nQ, w);
   };
 
   // the visit after visit `it` (at position pos), or end
@@ -800,14 +817,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
   const bool db_rows = AUX && P.dbias_acc != nullptr && !f.bias.q_bcast;
   int cls = 0;
   int pos = listed ? (nvis > 0 ? listed_visit(0, cls) : end) : next_visit(0, cls);
-  if (pos < end) prepare(0, pos, cls);
+  if (pos < end) {
+    store_rows(0, pos, cls, load_rows(pos));
+    issue_tiles(buf[0].k, buf[0].v, pos);
+  }
   for (int it = 0; pos < end; ++it) {
     const int sl = it & 1;
-    wait_vmcnt<0>();   // this visit's tiles (this thread's share)
-    __syncthreads();   // everyone's share, and the row data; slot sl ^ 1 is free
+    wait_vmcnt<0>();   // this visit's tiles and row data (this thread's share)
+    __syncthreads();   // everyone's share; slot sl ^ 1 is free
     int ncls = 0;
     const int npos = following(it, pos, ncls);
-    if (npos < end) prepare(sl ^ 1, npos, ncls);
+    const RowPre pre = load_rows(npos < end ? npos : pos);
+    // One visit: the next visit's tiles go out into slot sl ^ 1 (fq, fdo) while
+    // this one's (tq, tdo) are computed. As restrict parameters the slots tell
+    // the compiler that the LDS reads do not touch the tiles in flight, so it
+    // does not wait for those loads before them.
+    auto visit = [&](const char* __restrict__ tq, const char* __restrict__ tdo,
+                     __bf16* __restrict__ fq, __bf16* __restrict__ fdo)
+                     __attribute__((always_inline)) {
+    if (npos < end) issue_tiles(fq, fdo, npos);
     const bool test = !(AUX && f.staged) && (cls == 1 || test_k);
     const int vh = kvh * f.G + pos / f.nQ;  // this visit's head and first row
     const int vq0 = (pos % f.nQ) * kTile;
@@ -816,8 +844,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
         db_flush();
       db_h = vh;
     }
-    const char* tq = reinterpret_cast<const char*>(buf[sl].k);
-    const char* tdo = reinterpret_cast<const char*>(buf[sl].v);
     auto ld8 = [](const char* a) { return *reinterpret_cast<const bf16x8*>(a); };
     auto tr8 = [](const char* a0, const char* a1) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
@@ -904,8 +930,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int u = 8 * st + e;
-          const float ex = __builtin_amdgcn_exp2f(fmaf(s[u], f.scale_log2, bv[e] - l2[e]));
-          const float pr = (((bits >> e) & 1u) && l2[e] != -INFINITY) ? ex : 0.f;
+          const float ex = __builtin_amdgcn_exp2f(
+              fmaf(s[u], f.scale_log2, AUX ? bv[e] - l2[e] : -l2[e]));
+          const float pr = (test && !((bits >> e) & 1u)) ? 0.f : ex;
           pv[u] = pr;
           dsv[u] = pr * (dp[u] - dl[e]);
         }
@@ -942,6 +969,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv_mfma(AttnBwdParams P,
       }
       pin_reads_ahead<NT, kTrAhead, 4, 2>();
     }
+    };
+    visit(reinterpret_cast<const char*>(buf[sl].k), reinterpret_cast<const char*>(buf[sl].v),
+          buf[sl ^ 1].k, buf[sl ^ 1].v);
+    if (npos < end) store_rows(sl ^ 1, npos, ncls, pre);
     pos = npos;
     cls = ncls;
   }
