@@ -221,7 +221,7 @@ def measure_backward():
         o, lse = bsm.masked_attn_fwd(q, k, v, pred=d, block_mask=bm, return_lse=True)
         do = synth.normal_tensor(tuple(q.shape), 0, synth.TID_DOUT, "bf16").cuda()
         ms = _time_ms(lambda: bsm.masked_attn_bwd(q, k, v, o, do, lse, pred=d, block_mask=bm),
-                      reps=3)
+                      reps=10)
         fl = 2.5 * counted_flops(bm, geom)
         out[f"attn_bwd/dflash_train_bf16/{lay['name']}_ms"] = ms
         out[f"attn_bwd/dflash_train_bf16/{lay['name']}_TFLOP/s"] = fl / (ms * 1e-3) / 1e12
@@ -238,7 +238,7 @@ def measure_backward():
     o, lse = bsm.masked_attn_fwd(q, k, v, mask=mask, bias=bias, block_mask=bm, return_lse=True)
     do = synth.normal_tensor(tuple(q.shape), 0, synth.TID_DOUT, "bf16").cuda()
     ms = _time_ms(lambda: bsm.masked_attn_bwd(q, k, v, o, do, lse, mask=mask, bias=bias,
-                                              block_mask=bm, need_dbias=True), reps=3)
+                                              block_mask=bm, need_dbias=True), reps=10)
     fl = 2.5 * counted_flops(bm, geom)
     out["attn_bwd/dynamic_topk_bf16_dbias_ms"] = ms
     out["attn_bwd/dynamic_topk_bf16_dbias_TFLOP/s"] = fl / (ms * 1e-3) / 1e12

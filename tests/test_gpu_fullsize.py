@@ -2,8 +2,9 @@
 pool of host processes (tests/oracle_pool.py):
 
   * DFlash training shape, both layers: every row of every (b, h);
-  * long-context DFlash: rows in every (b, h, query tile) -- two per tile,
-    placed differently per head -- plus rows 0, 127, 128 and the last; and the
+  * long-context DFlash: rows in every (b, h, query tile) -- one in each of
+    its four 32-row blocks, placed differently per head and tile -- plus rows
+    0, 127, 128 and the last; and the
     head-shared block mask on all 256 query tiles, bit-exact;
   * dynamic top-k: every row of every (b, h);
   * decode with the head-group swap: every (b, h), through the block mask and
@@ -60,11 +61,13 @@ def test_dflash_train_every_row(li):
 
 
 def _tile_rows(Sq, h):
-    """Two rows in every 128-row query tile, at head-dependent places, and the
-    first / last rows and the 127 / 128 boundary."""
+    """One row in each 32-row block of every 128-row query tile (the rows one
+    wave of the attention kernel owns), at head- and tile-dependent places, and
+    the first / last rows and the 127 / 128 boundary."""
     rows = {0, 127, 128, Sq - 1}
     for qt in range((Sq + 127) // 128):
-        for r in ((h * 41 + qt * 7) % 128, (h * 13 + 64 + qt * 3) % 128):
+        for blk in range(4):
+            r = 32 * blk + (h * 11 + qt * 7 + blk * 5) % 32
             if qt * 128 + r < Sq:
                 rows.add(qt * 128 + r)
     return sorted(rows)
